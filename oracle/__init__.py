@@ -1,0 +1,28 @@
+"""CPU fp64 oracle for tile-window 3D attention, pooled global attention and
+the gated merge.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package. The product path
+(``video_dit_sparse_amd``) never imports it, and it never imports the product
+path: the two share no code.
+"""
+from .ref import (  # noqa: F401
+    token_coords,
+    tile_index,
+    tile_counts,
+    tile_extent,
+    window_radius,
+    sta_mask_row,
+    sta_ref,
+    dense_ref,
+    attention_weights_ref,
+    pool_ref,
+    pooled_grid,
+    global_ref,
+    merge_ref,
+    sta_pair_count_ref,
+    sta_flops_ref,
+    global_flops_ref,
+    dense_flops_ref,
+    to_f64,
+)

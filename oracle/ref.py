@@ -1,0 +1,300 @@
+"""Plain fp64 NumPy definitions of what the attention path computes.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py``; never by the product path, and it
+imports nothing from it.
+
+Sources (all read as the definition of a masked softmax, nothing blocked,
+fused or reordered beyond what the definition states):
+
+* UltraGen: High-Resolution Video Generation with Hierarchical Attention
+  (arXiv 2510.18775), summary page, §3 "Preliminaries": a video latent of
+  T x H x W positions becomes N = T*H*W tokens; full self-attention forms an
+  N x N map.  Token order here is raster, n = (t*H + h)*W + w.
+* Fast Video Generation with Sliding Tile Attention (arXiv 2502.04507),
+  abstract: attention proceeds tile by tile, each query tile attending the key
+  tiles of a local 3D window around it, in contrast to token-wise sliding
+  windows.
+* UltraGen summary, §4.3 "Cross-window Hierarchical Local Attention": window
+  partitions alternate between layers, the second one shifted so that K
+  windows per side become K+1.  Read here as a non-cyclic offset ``shift`` of
+  the tile lattice (tile index = floor((x + s) / b)), so edge tiles are partial.
+* UltraGen summary, §4.2 "Spatially-Compressed Global Attention": frame-wise
+  compression with stride k before global attention.  Read here as k_h x k_w
+  average pooling within each frame (a stride-k depthwise convolution whose
+  weights all equal 1/(k_h k_w)); cells that run past the frame edge average
+  only their real tokens.
+* AtlasVid (arXiv 2605.16649), abstract: "asymmetric" global-local attention.
+  Read here as full-resolution queries against pooled keys and values.
+* UltraGen summary, §4.1 "Time-Aware Global-Local Attention": a fusion factor
+  combines the local and the global latent.  Read here as a per-head gate:
+  O = w_loc[h] * O_loc + w_glob[h] * O_glob.
+* UltraGen summary, App. B "Efficiency Analysis": attention cost counted as
+  proportional to (attended query-key pairs) x D; here 4*D FLOP per pair
+  (2*D for q.k, 2*D for p*v).
+
+Every array argument is a single head, ``[N, D]``, unless stated otherwise.
+Inputs are converted to fp64 from exactly the values the caller holds
+(bf16 bit patterns widen exactly to fp32 and then to fp64).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "to_f64", "token_coords", "tile_index", "tile_counts", "tile_extent",
+    "window_radius", "sta_mask_row", "sta_ref", "dense_ref",
+    "attention_weights_ref", "pooled_grid", "pool_ref", "global_ref",
+    "merge_ref", "sta_pair_count_ref", "sta_flops_ref", "global_flops_ref",
+    "dense_flops_ref",
+]
+
+
+# --------------------------------------------------------------------------
+# inputs
+# --------------------------------------------------------------------------
+def to_f64(x) -> np.ndarray:
+    """Widen to fp64 without changing any value.
+
+    Accepts NumPy arrays (a ``uint16`` array is taken as raw bf16 bit
+    patterns) or any object with ``detach()/cpu()/float()/numpy()`` (a torch
+    tensor; bf16 -> fp32 is exact).
+    """
+    if hasattr(x, "detach"):
+        return x.detach().cpu().float().numpy().astype(np.float64)
+    a = np.asarray(x)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# token grid and tile lattice
+# --------------------------------------------------------------------------
+def token_coords(grid) -> np.ndarray:
+    """(t, h, w) of every token in raster order n = (t*H + h)*W + w.
+
+    UltraGen §3: the T x H x W latent is flattened to N = T*H*W tokens.
+    Returns int64 ``[N, 3]``.
+    """
+    T, H, W = (int(g) for g in grid)
+    n = np.arange(T * H * W, dtype=np.int64)
+    return np.stack([n // (H * W), (n // W) % H, n % W], axis=1)
+
+
+def tile_index(coords, tile, shift=(0, 0, 0)) -> np.ndarray:
+    """Tile coordinate of each token: i_d = floor((x_d + s_d) / b_d).
+
+    The shifted lattice is the second window partition of UltraGen §4.3.
+    """
+    b = np.asarray(tile, dtype=np.int64)
+    s = np.asarray(shift, dtype=np.int64)
+    return (np.asarray(coords, dtype=np.int64) + s) // b
+
+
+def tile_counts(grid, tile, shift=(0, 0, 0)) -> tuple:
+    """Number of tiles per dim: ceil((L_d + s_d) / b_d)."""
+    return tuple(-(-(int(L) + int(s)) // int(b)) for L, b, s in zip(grid, tile, shift))
+
+
+def tile_extent(i, L, b, s) -> tuple:
+    """Token range [lo, hi) of tile ``i`` along one dim of length ``L``."""
+    return max(0, i * b - s), min(L, (i + 1) * b - s)
+
+
+def window_radius(window) -> tuple:
+    """Window of w tiles centred on the query tile has radius (w - 1) / 2.
+
+    Only odd windows are centred; even ones are rejected.
+    """
+    for w in window:
+        if int(w) < 1 or int(w) % 2 == 0:
+            raise ValueError(f"window must be odd and >= 1, got {tuple(window)}")
+    return tuple((int(w) - 1) // 2 for w in window)
+
+
+def sta_mask_row(tiles_of_keys: np.ndarray, query_tile, radius) -> np.ndarray:
+    """Boolean mask over all keys for one query: key m is attended iff its
+    tile is within ``radius`` tiles of the query's tile in every dim.
+
+    Sliding Tile Attention, abstract: the window is a 3D neighbourhood of
+    tiles; windows are clipped at the grid edge (never moved inward).
+    """
+    d = np.abs(tiles_of_keys - np.asarray(query_tile, dtype=np.int64)[None, :])
+    return np.all(d <= np.asarray(radius, dtype=np.int64)[None, :], axis=1)
+
+
+# --------------------------------------------------------------------------
+# attention
+# --------------------------------------------------------------------------
+def _softmax_attend(qb, kb, vb, scale):
+    """softmax(scale * q k^T) v over the given keys, plus LSE (natural log)."""
+    s = scale * (qb @ kb.T)
+    mx = s.max(axis=1, keepdims=True)
+    p = np.exp(s - mx)
+    l = p.sum(axis=1, keepdims=True)
+    o = (p @ vb) / l
+    return o, mx[:, 0] + np.log(l[:, 0])
+
+
+def sta_ref(q, k, v, grid, tile, window, shift=(0, 0, 0), scale=None, rows=None):
+    """Sliding-tile attention for one head.
+
+    For query token n: O_n = sum_m softmax_m(scale * q_n . k_m) v_m with m over
+    the keys whose tile lies in the window around n's tile (``sta_mask_row``).
+
+    The explicit boolean mask is built row by row over all N keys; rows of one
+    query tile are checked to be identical and non-empty (the query's own tile
+    is always in its window), then that tile's rows are evaluated on exactly
+    the selected keys, which equals masking every other key to -inf.
+
+    ``rows``: optional query token indices to evaluate (rows are independent).
+    Returns (O [len(rows), D], LSE [len(rows)]).
+    """
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    N, D = q.shape
+    T, H, W = grid
+    assert N == T * H * W and k.shape[0] == N and v.shape[0] == N
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    radius = window_radius(window)
+    ti = tile_index(token_coords(grid), tile, shift)
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.empty((len(rows), v.shape[1]))
+    lse = np.empty(len(rows))
+    uniq, inv = np.unique(ti[rows], axis=0, return_inverse=True)
+    inv = np.asarray(inv).reshape(-1)
+    for g in range(len(uniq)):
+        pos = np.nonzero(inv == g)[0]
+        block = np.empty((len(pos), N), dtype=bool)
+        for j, n in enumerate(rows[pos]):
+            block[j] = sta_mask_row(ti, ti[n], radius)
+        assert block[0].any(), "a query row with no key"
+        assert (block == block[0][None, :]).all(), "rows of one query tile differ"
+        keys = np.nonzero(block[0])[0]
+        o[pos], lse[pos] = _softmax_attend(q[rows[pos]], k[keys], v[keys], scale)
+    return o, lse
+
+
+def dense_ref(q, k, v, scale=None, rows=None):
+    """Full softmax attention over all keys (UltraGen §3's N x N map)."""
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[1])
+    qr = q if rows is None else q[np.asarray(rows, dtype=np.int64)]
+    return _softmax_attend(qr, k, v, scale)
+
+
+def attention_weights_ref(q, k, grid, tile, window, shift=(0, 0, 0), scale=None):
+    """Full N x N attention weights of sliding-tile attention (tiny inputs).
+
+    Entry [n, m] is softmax weight of key m for query n, exactly 0 where the
+    tile window excludes m.
+    """
+    q, k = to_f64(q), to_f64(k)
+    N, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    radius = window_radius(window)
+    ti = tile_index(token_coords(grid), tile, shift)
+    P = np.zeros((N, N))
+    for n in range(N):
+        keys = np.nonzero(sta_mask_row(ti, ti[n], radius))[0]
+        s = scale * (k[keys] @ q[n])
+        e = np.exp(s - s.max())
+        P[n, keys] = e / e.sum()
+    return P
+
+
+# --------------------------------------------------------------------------
+# compressed global branch
+# --------------------------------------------------------------------------
+def pooled_grid(grid, pool_hw) -> tuple:
+    """Grid of pooled tokens: T x ceil(H / k_h) x ceil(W / k_w).
+
+    Frames are not pooled (the compression of UltraGen §4.2 is frame-wise).
+    """
+    T, H, W = grid
+    kh, kw = pool_hw
+    return (int(T), -(-int(H) // int(kh)), -(-int(W) // int(kw)))
+
+
+def pool_ref(x, grid, pool_hw) -> np.ndarray:
+    """k_h x k_w spatial average pooling of one head's tokens, frame by frame.
+
+    Output row (t, i, j) in raster order is the mean of x over
+    {(t, h, w): i*k_h <= h < min(H, (i+1)*k_h), j*k_w <= w < min(W, (j+1)*k_w)}.
+    """
+    x = to_f64(x)
+    T, H, W = grid
+    kh, kw = pool_hw
+    _, Hp, Wp = pooled_grid(grid, pool_hw)
+    X = x.reshape(T, H, W, -1)
+    out = np.empty((T, Hp, Wp, X.shape[-1]))
+    for t in range(T):
+        for i in range(Hp):
+            for j in range(Wp):
+                cell = X[t, i * kh:min(H, (i + 1) * kh), j * kw:min(W, (j + 1) * kw)]
+                out[t, i, j] = cell.mean(axis=(0, 1))
+    return out.reshape(T * Hp * Wp, -1)
+
+
+def global_ref(q, k_pooled, v_pooled, scale=None, rows=None):
+    """Every full-resolution query attends all pooled keys, no mask.
+
+    AtlasVid's asymmetric global-local attention: queries are not compressed.
+    """
+    return dense_ref(q, k_pooled, v_pooled, scale=scale, rows=rows)
+
+
+def merge_ref(o_local, o_global, w_local, w_global) -> np.ndarray:
+    """O = w_loc[h] * O_loc + w_glob[h] * O_glob, per head.
+
+    ``o_local``/``o_global``: ``[heads, ..., D]``; ``w_local`` may be None
+    (all ones).  UltraGen §4.1's fusion factor, taken as a per-head gate.
+    """
+    ol, og = to_f64(o_local), to_f64(o_global)
+    heads = ol.shape[0]
+    wl = np.ones(heads) if w_local is None else to_f64(w_local).reshape(heads)
+    wg = to_f64(w_global).reshape(heads)
+    shape = (heads,) + (1,) * (ol.ndim - 1)
+    return wl.reshape(shape) * ol + wg.reshape(shape) * og
+
+
+# --------------------------------------------------------------------------
+# effective work
+# --------------------------------------------------------------------------
+def sta_pair_count_ref(grid, tile, window, shift=(0, 0, 0)) -> int:
+    """Attended (query, key) token pairs of one head: sum over tile pairs
+    (a, c) inside each other's window of tokens(a) * tokens(c).
+
+    Built from the explicit tile-level mask, so partial tiles count only
+    their real tokens.
+    """
+    radius = np.asarray(window_radius(window), dtype=np.int64)
+    counts = tile_counts(grid, tile, shift)
+    sizes = [np.array([tile_extent(i, int(L), int(b), int(s))[1] - tile_extent(i, int(L), int(b), int(s))[0]
+                       for i in range(n)], dtype=np.int64)
+             for L, b, s, n in zip(grid, tile, shift, counts)]
+    idx = np.stack(np.meshgrid(*[np.arange(n) for n in counts], indexing="ij"), axis=-1).reshape(-1, 3)
+    tok = sizes[0][idx[:, 0]] * sizes[1][idx[:, 1]] * sizes[2][idx[:, 2]]
+    A = np.all(np.abs(idx[:, None, :] - idx[None, :, :]) <= radius[None, None, :], axis=2)
+    return int(tok @ A.astype(np.int64) @ tok)
+
+
+def sta_flops_ref(grid, tile, window, shift=(0, 0, 0), head_dim=128, heads=1, batch=1) -> float:
+    """4 * D FLOP per attended pair (2D for q.k, 2D for the p*v update)."""
+    return 4.0 * head_dim * heads * batch * sta_pair_count_ref(grid, tile, window, shift)
+
+
+def global_flops_ref(grid, pool_hw, head_dim=128, heads=1, batch=1) -> float:
+    T, H, W = grid
+    M = int(np.prod(pooled_grid(grid, pool_hw)))
+    return 4.0 * head_dim * heads * batch * (T * H * W) * M
+
+
+def dense_flops_ref(grid, head_dim=128, heads=1, batch=1) -> float:
+    N = int(np.prod(grid))
+    return 4.0 * head_dim * heads * batch * N * N

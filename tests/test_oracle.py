@@ -1,0 +1,349 @@
+"""Pins for the CPU oracle: each test checks the oracle against something other
+than itself (a library routine, a closed form, an invariant, a brute force
+built differently, or a fact the pages state).  CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as R
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+def randn(seed, *shape):
+    return rng(seed).standard_normal(shape)
+
+
+def coords_lib(grid):
+    """Token coordinates via numpy's own index decomposition (not the oracle's)."""
+    T, H, W = grid
+    t, h, w = np.unravel_index(np.arange(T * H * W), (T, H, W))
+    return np.stack([t, h, w], axis=1)
+
+
+# ---------------------------------------------------------------- softmax core
+def test_dense_matches_torch_sdpa_fp64():
+    q, k, v = randn(1, 40, 32), randn(2, 55, 32), randn(3, 55, 24)
+    for scale in (None, 0.3):
+        o, lse = R.dense_ref(q, k, v, scale=scale)
+        s = scale if scale is not None else 1 / math.sqrt(32)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None], scale=s)[0]
+        np.testing.assert_allclose(o, ref.numpy(), rtol=0, atol=1e-12)
+        lse_lib = torch.logsumexp(s * torch.from_numpy(q) @ torch.from_numpy(k).T, dim=1).numpy()
+        np.testing.assert_allclose(lse, lse_lib, rtol=0, atol=1e-12)
+
+
+def test_two_key_closed_form():
+    # logits 0 and ln 3 -> weights 1/4, 3/4 exactly
+    q = np.array([[1.0, 0.0]])
+    k = np.array([[0.0, 5.0], [math.log(3.0), -2.0]])
+    v = np.array([[4.0, -8.0], [8.0, 4.0]])
+    o, lse = R.dense_ref(q, k, v, scale=1.0)
+    np.testing.assert_allclose(o[0], [0.25 * 4 + 0.75 * 8, 0.25 * -8 + 0.75 * 4], atol=1e-14)
+    np.testing.assert_allclose(lse[0], math.log(1 + 3), atol=1e-14)
+
+
+def test_single_key_returns_value():
+    q, k, v = randn(4, 3, 8), randn(5, 1, 8), randn(6, 1, 8)
+    o, lse = R.dense_ref(q, k, v)
+    np.testing.assert_allclose(o, np.repeat(v, 3, axis=0), atol=1e-15)
+    np.testing.assert_allclose(lse, (q @ k.T)[:, 0] / math.sqrt(8), atol=1e-14)
+
+
+def test_bf16_bits_widen_exactly():
+    x = torch.randn(64, dtype=torch.float32).to(torch.bfloat16)
+    bits = x.view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(R.to_f64(bits), x.float().numpy().astype(np.float64))
+    np.testing.assert_array_equal(R.to_f64(x), x.float().numpy().astype(np.float64))
+
+
+# ---------------------------------------------------------------- token grid
+@pytest.mark.parametrize("grid", [(4, 8, 8), (3, 5, 7), (1, 1, 9), (21, 90, 160)])
+def test_token_coords_raster(grid):
+    np.testing.assert_array_equal(R.token_coords(grid), coords_lib(grid))
+
+
+def test_tile_partition_sizes_closed_form():
+    # 2K workload: T=21 tile 4 shift 2 -> [2,4,4,4,4,3]; H=90 tile 8 shift 4 ->
+    # [4, 8 x 10, 6]; W=160 tile 8 shift 4 -> [4, 8 x 19, 4]; unshifted H -> [8 x 11, 2].
+    def sizes(L, b, s):
+        n = R.tile_counts((L, 1, 1), (b, 1, 1), (s, 0, 0))[0]
+        return [R.tile_extent(i, L, b, s)[1] - R.tile_extent(i, L, b, s)[0] for i in range(n)]
+    assert sizes(21, 4, 2) == [2, 4, 4, 4, 4, 3]
+    assert sizes(90, 8, 4) == [4] + [8] * 10 + [6]
+    assert sizes(160, 8, 4) == [4] + [8] * 19 + [4]
+    assert sizes(90, 8, 0) == [8] * 11 + [2]
+    assert sizes(21, 4, 0) == [4] * 5 + [1]
+    # extents agree with the tile index of every coordinate
+    for L, b, s in [(21, 4, 2), (13, 4, 3), (7, 3, 1), (10, 5, 0)]:
+        x = np.arange(L)
+        ti = R.tile_index(np.stack([x, 0 * x, 0 * x], 1), (b, 1, 1), (s, 0, 0))[:, 0]
+        n = R.tile_counts((L, 1, 1), (b, 1, 1), (s, 0, 0))[0]
+        assert ti.max() == n - 1 and ti.min() == 0
+        for i in range(n):
+            lo, hi = R.tile_extent(i, L, b, s)
+            np.testing.assert_array_equal(np.nonzero(ti == i)[0], np.arange(lo, hi))
+
+
+def test_shifted_partition_page_fact():
+    facts = json.load(open(os.path.join(GOLDEN, "page_facts.json")))["shifted_partition"]
+    for K, expect in zip(facts["K"], facts["shifted_windows_per_side"]):
+        b = 8
+        L = K * b
+        assert R.tile_counts((L, L, L), (b, b, b), (0, 0, 0)) == (K, K, K)
+        assert R.tile_counts((L, L, L), (b, b, b), (0, b // 2, b // 2)) == (K, expect, expect)
+        # the two edge windows of the shifted partition are half windows
+        assert R.tile_extent(0, L, b, b // 2) == (0, b // 2)
+        assert R.tile_extent(expect - 1, L, b, b // 2) == (L - b // 2, L)
+
+
+def test_window_rejects_even():
+    with pytest.raises(ValueError):
+        R.window_radius((3, 2, 3))
+    with pytest.raises(ValueError):
+        R.window_radius((0, 1, 1))
+
+
+# ---------------------------------------------------------------- STA pins
+FULL_WINDOW_CASES = [
+    # grid, tile, window, shift
+    ((4, 8, 8), (2, 4, 4), (3, 3, 3), (0, 0, 0)),        # the tiny fp32 workload: dense
+    ((3, 5, 7), (2, 2, 3), (3, 5, 5), (1, 1, 2)),        # partial tiles + shift, full window
+    ((2, 6, 6), (1, 1, 1), (3, 11, 11), (0, 0, 0)),
+]
+
+
+@pytest.mark.parametrize("grid,tile,window,shift", FULL_WINDOW_CASES)
+def test_full_window_is_dense(grid, tile, window, shift):
+    N = int(np.prod(grid))
+    q, k, v = randn(10, N, 16), randn(11, N, 16), randn(12, N, 16)
+    o, lse = R.sta_ref(q, k, v, grid, tile, window, shift, scale=0.25)
+    od, lsed = R.dense_ref(q, k, v, scale=0.25)
+    np.testing.assert_allclose(o, od, atol=1e-12)
+    np.testing.assert_allclose(lse, lsed, atol=1e-12)
+
+
+SPARSE_CASES = [
+    ((8, 16, 16), (2, 4, 4), (3, 3, 3), (0, 0, 0)),
+    ((7, 13, 21), (3, 4, 8), (3, 3, 1), (1, 2, 4)),
+    ((5, 9, 11), (2, 3, 3), (1, 3, 5), (1, 0, 2)),
+    ((4, 8, 12), (2, 4, 4), (1, 3, 3), (1, 2, 0)),
+]
+
+
+@pytest.mark.parametrize("grid,tile,window,shift", [c for c in SPARSE_CASES if np.prod(c[0]) <= 1200])
+def test_weights_row_stochastic_and_zero_outside(grid, tile, window, shift):
+    N = int(np.prod(grid))
+    q, k = randn(20, N, 8), randn(21, N, 8)
+    P = R.attention_weights_ref(q, k, grid, tile, window, shift)
+    assert (P >= 0).all()
+    np.testing.assert_allclose(P.sum(axis=1), 1.0, atol=1e-12)
+    # independent zero pattern: per-dim 1-D tile ids from integer division of raw coordinates
+    c = coords_lib(grid)
+    tid = (c + np.array(shift)) // np.array(tile)
+    r = (np.array(window) - 1) // 2
+    allowed = np.ones((N, N), bool)
+    for d in range(3):
+        allowed &= np.abs(tid[:, d][:, None] - tid[:, d][None, :]) <= r[d]
+    assert (P[~allowed] == 0).all()
+    assert (P[allowed] > 0).all()
+
+
+@pytest.mark.parametrize("window", [(1, 1, 1), (3, 3, 3), (1, 3, 5), (3, 5, 1)])
+def test_unit_tiles_equal_token_sliding_window(window):
+    grid = (4, 7, 9)
+    N = int(np.prod(grid))
+    q, k, v = randn(30, N, 12), randn(31, N, 12), randn(32, N, 12)
+    o, lse = R.sta_ref(q, k, v, grid, (1, 1, 1), window, (0, 0, 0), scale=0.4)
+    c = coords_lib(grid)
+    r = (np.array(window) - 1) // 2
+    for n in range(N):
+        keys = np.nonzero(np.all(np.abs(c - c[n]) <= r, axis=1))[0]
+        on, ln = R.dense_ref(q[n:n + 1], k[keys], v[keys], scale=0.4)
+        np.testing.assert_allclose(o[n], on[0], atol=1e-12)
+        np.testing.assert_allclose(lse[n], ln[0], atol=1e-12)
+
+
+def _box_1d(L, b, s, r, x):
+    """Interval of coordinates whose 1-D tile is within r of x's tile (scan)."""
+    tiles = [(xx + s) // b for xx in range(L)]
+    sel = [xx for xx in range(L) if abs(tiles[xx] - tiles[x]) <= r]
+    assert sel == list(range(sel[0], sel[-1] + 1))
+    return sel[0], sel[-1] + 1
+
+
+@pytest.mark.parametrize("grid,tile,window,shift", SPARSE_CASES + [((4, 8, 8), (2, 4, 4), (3, 3, 3), (0, 0, 0))])
+def test_zero_keys_give_window_box_mean(grid, tile, window, shift):
+    """K = 0 makes all logits 0: O is the plain mean of V over the window's
+    tokens, here via a 3-D summed-area table; LSE is log(count)."""
+    T, H, W = grid
+    N = T * H * W
+    D = 6
+    v = randn(40, N, D)
+    q = randn(41, N, D)
+    k = np.zeros((N, D))
+    rows = np.arange(N) if N <= 800 else rng(42).choice(N, 400, replace=False)
+    o, lse = R.sta_ref(q, k, v, grid, tile, window, shift, rows=rows)
+    S = np.zeros((T + 1, H + 1, W + 1, D))
+    S[1:, 1:, 1:] = v.reshape(T, H, W, D).cumsum(0).cumsum(1).cumsum(2)
+    r = [(w - 1) // 2 for w in window]
+    c = coords_lib(grid)
+    for i, n in enumerate(rows):
+        (t0, t1), (h0, h1), (w0, w1) = [
+            _box_1d(L, b, s, rr, x) for L, b, s, rr, x in zip(grid, tile, shift, r, c[n])]
+        tot = (S[t1, h1, w1] - S[t0, h1, w1] - S[t1, h0, w1] - S[t1, h1, w0]
+               + S[t0, h0, w1] + S[t0, h1, w0] + S[t1, h0, w0] - S[t0, h0, w0])
+        cnt = (t1 - t0) * (h1 - h0) * (w1 - w0)
+        np.testing.assert_allclose(o[i], tot / cnt, atol=1e-12)
+        np.testing.assert_allclose(lse[i], math.log(cnt), atol=1e-12)
+
+
+def test_constant_values_pass_through():
+    grid, tile, window, shift = (5, 9, 11), (2, 3, 3), (1, 3, 5), (1, 0, 2)
+    N = int(np.prod(grid))
+    q, k = randn(50, N, 8) * 3, randn(51, N, 8) * 3
+    c = randn(52, 1, 5)
+    v = np.repeat(c, N, axis=0)
+    o, _ = R.sta_ref(q, k, v, grid, tile, window, shift)
+    np.testing.assert_allclose(o, v, atol=1e-13)
+
+
+def test_translation_by_whole_tiles():
+    """Rolling the grid by one tile in w moves interior outputs by one tile."""
+    grid, tile, window = (4, 8, 24), (2, 4, 4), (3, 3, 3)
+    T, H, W = grid
+    N = T * H * W
+    q, k, v = randn(60, N, 8), randn(61, N, 8), randn(62, N, 8)
+    roll = lambda x: np.roll(x.reshape(T, H, W, -1), 4, axis=2).reshape(N, -1)
+    o, _ = R.sta_ref(q, k, v, grid, tile, window)
+    o2, _ = R.sta_ref(roll(q), roll(k), roll(v), grid, tile, window)
+    o = o.reshape(T, H, W, -1)
+    o2 = o2.reshape(T, H, W, -1)
+    # w tiles 1..3 (window stays clear of both edges before and after the roll)
+    np.testing.assert_allclose(o2[:, :, 8:20], o[:, :, 4:16], atol=1e-12)
+
+
+def test_row_subset_equals_full():
+    grid, tile, window, shift = (7, 13, 21), (3, 4, 8), (3, 3, 1), (1, 2, 4)
+    N = int(np.prod(grid))
+    q, k, v = randn(70, N, 8), randn(71, N, 8), randn(72, N, 8)
+    rows = rng(73).choice(N, 97, replace=False)
+    o_all, l_all = R.sta_ref(q, k, v, grid, tile, window, shift)
+    o_s, l_s = R.sta_ref(q, k, v, grid, tile, window, shift, rows=rows)
+    # same values up to the summation order of a different-sized BLAS call
+    np.testing.assert_allclose(o_s, o_all[rows], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l_s, l_all[rows], rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------- pooling / global / merge
+@pytest.mark.parametrize("grid,pool", [((3, 8, 12), (4, 4)), ((2, 9, 10), (4, 3)), ((2, 5, 7), (8, 8)), ((1, 6, 6), (1, 1))])
+def test_pool_ramp_closed_form(grid, pool):
+    T, H, W = grid
+    kh, kw = pool
+    c = coords_lib(grid).astype(np.float64)
+    x = np.stack([c[:, 1] * W + c[:, 2], c[:, 0] * 1000.0 + c[:, 2], np.full(len(c), 7.5)], axis=1)
+    p = R.pool_ref(x, grid, pool)
+    Tp, Hp, Wp = R.pooled_grid(grid, pool)
+    assert (Tp, Hp, Wp) == (T, -(-H // kh), -(-W // kw))
+    for t in range(T):
+        for i in range(Hp):
+            for j in range(Wp):
+                h0, h1 = i * kh, min(H, (i + 1) * kh)
+                w0, w1 = j * kw, min(W, (j + 1) * kw)
+                mh, mw = (h0 + h1 - 1) / 2, (w0 + w1 - 1) / 2      # mean of an integer range
+                row = p[(t * Hp + i) * Wp + j]
+                np.testing.assert_allclose(row, [mh * W + mw, t * 1000.0 + mw, 7.5], atol=1e-12)
+
+
+def test_pool_identity_and_global_dense():
+    grid = (2, 6, 5)
+    N = 60
+    x = randn(80, N, 4)
+    np.testing.assert_array_equal(R.pool_ref(x, grid, (1, 1)), x)
+    q, k, v = randn(81, N, 4), randn(82, N, 4), randn(83, N, 4)
+    og, lg = R.global_ref(q, R.pool_ref(k, grid, (1, 1)), R.pool_ref(v, grid, (1, 1)))
+    od, ld = R.dense_ref(q, k, v)
+    np.testing.assert_array_equal(og, od)
+    np.testing.assert_array_equal(lg, ld)
+
+
+def test_pool_matches_torch_avg_pool_when_divisible():
+    grid, pool = (3, 8, 12), (4, 3)
+    T, H, W = grid
+    x = randn(84, T * H * W, 5)
+    ref = torch.nn.functional.avg_pool2d(
+        torch.from_numpy(x.reshape(T, H, W, 5)).permute(0, 3, 1, 2), pool, stride=pool)
+    ref = ref.permute(0, 2, 3, 1).reshape(-1, 5).numpy()
+    np.testing.assert_allclose(R.pool_ref(x, grid, pool), ref, atol=1e-13)
+
+
+def test_merge_special_cases_and_linearity():
+    ol, og = randn(90, 3, 10, 4), randn(91, 3, 10, 4)
+    g = rng(92).uniform(size=3)
+    np.testing.assert_array_equal(R.merge_ref(ol, og, None, np.zeros(3)), ol)
+    np.testing.assert_array_equal(R.merge_ref(ol, og, np.zeros(3), np.ones(3)), og)
+    m = R.merge_ref(ol, og, None, g)
+    for h in range(3):
+        np.testing.assert_allclose(m[h], ol[h] + g[h] * og[h], atol=1e-15)
+    # heads are independent: permuting heads permutes outputs
+    perm = [2, 0, 1]
+    np.testing.assert_array_equal(R.merge_ref(ol[perm], og[perm], None, g[perm]), m[perm])
+
+
+# ---------------------------------------------------------------- effective work
+@pytest.mark.parametrize("grid,tile,window,shift", SPARSE_CASES[1:] + FULL_WINDOW_CASES)
+def test_pair_count_brute_force(grid, tile, window, shift):
+    N = int(np.prod(grid))
+    c = coords_lib(grid)
+    tid = (c + np.array(shift)) // np.array(tile)
+    r = (np.array(window) - 1) // 2
+    count = 0
+    for n in range(N):
+        count += int(np.all(np.abs(tid - tid[n]) <= r, axis=1).sum())
+    assert R.sta_pair_count_ref(grid, tile, window, shift) == count
+
+
+def test_pair_count_720p_by_hand():
+    # tile lattice 5 x 6 x 10; clipped window tile counts per dim (radius 1, 1, 2):
+    # T: 2+3+3+3+2 = 13, H: 2+3+3+3+3+2 = 16, W: 3+4+5*6+4+3 = 44; 384 tokens per tile
+    assert R.sta_pair_count_ref((30, 48, 80), (6, 8, 8), (3, 3, 5)) == 13 * 16 * 44 * 384 * 384
+    assert R.sta_flops_ref((30, 48, 80), (6, 8, 8), (3, 3, 5), head_dim=128, heads=24) == 4 * 128 * 24 * 9152 * 384 ** 2
+
+
+def test_full_attention_growth_page_fact():
+    f = json.load(open(os.path.join(GOLDEN, "page_facts.json")))["full_attention_growth"]
+    g1, g2 = (5, 12, 20), (5, 12 * f["hw_factor"], 20 * f["hw_factor"])
+    assert np.prod(g2) == f["token_factor"] * np.prod(g1)
+    assert R.dense_flops_ref(g2) == f["map_factor"] * R.dense_flops_ref(g1)
+
+
+def test_cost_estimate_page_fact():
+    """Local K x K windows give 1/K^2 of dense; queries against 2x2-pooled keys
+    in those windows give 1/(4K^2); Q, K, V all compressed by K per side give
+    1/K^4.  The sum reproduces the page's about-12-fold estimate at K = 4."""
+    f = json.load(open(os.path.join(GOLDEN, "page_facts.json")))["cost_estimate"]
+    K = f["K"]
+    grid = (3, 8 * K, 8 * K)
+    T, H, W = grid
+    dense = R.dense_flops_ref(grid)
+    local = R.sta_flops_ref(grid, (T, H // K, W // K), (1, 1, 1))
+    assert local * K ** 2 == dense
+    # hierarchical term (reading): each window's queries vs its keys pooled 2x2
+    hier = local / 4
+    glob_c = R.dense_flops_ref(R.pooled_grid(grid, (K, K)))
+    assert glob_c * K ** f["formula_global_power"] == dense
+    speedup = dense / (local + hier + glob_c)
+    formula = 1 / (f["formula_local_coeff"] / K ** 2 + f["formula_hier_coeff"] / K ** 2 + 1 / K ** 4)
+    assert abs(speedup - formula) < 1e-12
+    assert round(speedup) == f["approx_speedup"]
+    # asymmetric global (full-resolution Q against K x K pooled K/V) is 1/K^2
+    assert R.global_flops_ref(grid, (K, K)) * K ** 2 == dense
