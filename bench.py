@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Benchmark of the sliding-tile attention hot path on one MI355X.
+
+A step is one pass of the workload's hot path over one batch of synthetic
+inputs already resident in HBM.  The default workload is the 720P sliding-tile
+attention latent (T=30, H=48, W=80; tile 6x8x8; window 3x3x5 tiles; 24 heads;
+head_dim 128; bf16), where a step is one ``sta_attn_fwd`` call.  The value is
+effective TFLOP/s: 4*head_dim FLOP per attended (query, key) token pair, only
+pairs inside the tile windows counted.
+
+Prints one JSON line (rank 0).  Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective attention TFLOP/s + ms/call (720P-shape STA, bf16); % MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "sta_bf16_720p_counters.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "video_dit_sparse_amd", "csrc", f) for f in ("attn_bf16.hip", "internal.h")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the sliding-tile kernel from the committed
+    rocprofv3 counter summary, or None if absent or taken on other source."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    text = open(COUNTERS_FILE).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_hash and m_bytes) or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(w, q, k, v, budget_s: float):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    whole query tiles of head 0, in a seeded random order, until the time
+    budget is spent.  Returns the JSON object."""
+    import numpy as np
+    import oracle as R
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    qh, kh, vh = (R.to_f64(x[0, 0]) for x in (q, k, v))
+    shift = w.shifts[0]
+    counts = R.tile_counts(w.grid, w.tile, shift)
+    coords = R.token_coords(w.grid)
+    ti = R.tile_index(coords, w.tile, shift)
+    radius = R.window_radius(w.window)
+    rng = np.random.default_rng(0)
+    order = rng.permutation(int(np.prod(counts)))
+    done_flops, tiles, rows_done = 0.0, 0, 0
+    t0 = time.perf_counter()
+    for flat in order:
+        a = np.unravel_index(flat, counts)
+        rows = np.nonzero(np.all(ti == np.array(a)[None, :], axis=1))[0]
+        nkeys = int(R.sta_mask_row(ti, a, radius).sum())
+        R.sta_ref(qh, kh, vh, w.grid, w.tile, w.window, shift, scale=w.softmax_scale, rows=rows)
+        done_flops += 4.0 * w.head_dim * len(rows) * nkeys
+        tiles += 1
+        rows_done += len(rows)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": done_flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{tiles} whole query tiles ({rows_done} query rows) of head 0 of {w.name}, "
+                      f"fp64 NumPy, {el:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="sta_720p")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget (0 = skip)")
+    ap.add_argument("--dense-steps", type=int, default=3, help="full-window comparison calls (0 = skip)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the sliding-tile path has no multi-GPU mode)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import video_dit_sparse_amd as V
+    from video_dit_sparse_amd import pipeline as P
+    from video_dit_sparse_amd import workloads as WL
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    V.lib()  # fail loudly without the HIP library
+    dev = "cuda:0"
+    w = WL.WORKLOADS[args.workload]
+    log(f"[bench] workload {w.name}: {w.description}")
+    q, k, v = WL.make_qkv(w, dev)
+    gate = WL.make_gate(w, dev)
+    buf = P.Buffers(w, q)
+    fl = P.flops(w)
+    step_flops = sum(fl.values())
+
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        P.run(w, q, k, v, gate, buf)
+    torch.cuda.synchronize()
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        P.run(w, q, k, v, gate, buf)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ev_ms = ev0.elapsed_time(ev1)
+    ms_per_step = wall_ms / args.steps
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (events {ev_ms / args.steps:.3f}), "
+        f"{value:.1f} effective TFLOP/s")
+
+    # dominant kernel: the sliding-tile attention launch(es) alone, timed with
+    # events on the stream it is launched on
+    n_local = len(w.shifts)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        for i, s in enumerate(w.shifts):
+            V.sta_attn_fwd(q, k, v, w.grid, w.tile, w.window, s, scale=w.softmax_scale, out=buf.local[i])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    launch_ms = e0.elapsed_time(e1) / (args.steps * n_local)
+    launch_flops = fl["local"] / n_local
+    achieved = launch_flops / (launch_ms * 1e-3) / 1e12
+    traffic = measured_traffic() if w.name == "sta_720p" else None
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "kernel": "box_attn_bf16_kernel<128>", "launch_ms": round(launch_ms, 4),
+                "flop_per_launch": launch_flops}
+
+    extra = {}
+    if args.dense_steps > 0 and w.pool_hw is None:
+        # the same kernel with a window covering the whole tile lattice = dense attention
+        n_tiles = [-(-(L + s) // b) for L, b, s in zip(w.grid, w.tile, w.shifts[0])]
+        full = tuple(2 * n - 1 for n in n_tiles)
+        V.sta_attn_fwd(q, k, v, w.grid, w.tile, full, scale=w.softmax_scale, out=buf.local[0])
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        for _ in range(args.dense_steps):
+            V.sta_attn_fwd(q, k, v, w.grid, w.tile, full, scale=w.softmax_scale, out=buf.local[0])
+        d1.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = d0.elapsed_time(d1) / args.dense_steps
+        dense_flops = V.sta_flops(w.batch, w.heads, w.head_dim, w.grid, w.tile, full)
+        extra["dense_same_kernel"] = {"window": list(full), "ms_per_call": round(dense_ms, 3),
+                                      "tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 1),
+                                      "speedup_vs_dense": round(dense_ms / launch_ms, 2)}
+        log(f"[bench] dense (window {full}): {dense_ms:.2f} ms, speed-up {dense_ms / launch_ms:.2f}x")
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        log(f"[bench] CPU oracle sample ({args.cpu_seconds:.0f} s budget)")
+        cpu = cpu_baseline(w, q, k, v, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "grid": list(w.grid), "tile": list(w.tile), "window": list(w.window),
+                   "shifts": [list(s) for s in w.shifts], "pool_hw": w.pool_hw, "batch": w.batch,
+                   "heads": w.heads, "head_dim": w.head_dim, "tokens": w.n_tokens,
+                   "effective_flop_per_step": step_flops},
+        "pct_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        **extra,
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

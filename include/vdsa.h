@@ -1,0 +1,189 @@
+/*
+ * vdsa.h - tile-window sparse attention for video latents on MI355X (gfx950).
+ *
+ * C ABI of libvdsa.so.  Plain pointers, sizes and small descriptor structs; no
+ * C++ or framework types cross it.
+ *
+ * The problem these calls solve:
+ *   A video latent of T x H x W positions is a sequence of N = T*H*W tokens in
+ *   raster order n = (t*H + h)*W + w (UltraGen, arXiv 2510.18775, summary
+ *   section 3 "Preliminaries").  Each of Q, K, V, O is logically
+ *   [batch, heads, N, head_dim] with head_dim contiguous; the batch, head and
+ *   token strides are free (BHND and BNHD storage both work).
+ *
+ * Conventions shared by every call:
+ *   - Memory is caller-owned device memory.  No call allocates, frees or
+ *     keeps a pointer after it returns.
+ *   - Every argument check runs on the host before anything is enqueued.  On
+ *     error nothing is launched, outputs are untouched, a status is returned
+ *     and vdsa_last_error() describes it.  Nothing aborts; no exception
+ *     crosses the ABI.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream).  A fault during a kernel surfaces at the caller's next
+ *     synchronisation, as with any HIP launch.
+ *   - Calls are thread-safe (no global mutable state except a thread-local
+ *     error string).
+ *   - dtype VDSA_BF16: bf16 inputs and outputs (upper 16 bits of IEEE fp32),
+ *     fp32 accumulation and fp32 softmax.  VDSA_F32: fp32 throughout.
+ *   - Alignment: every tensor pointer 16-byte aligned; every batch, head and
+ *     token stride times the element size a multiple of 16 bytes.
+ *   - Size limit: within one (batch, head), the largest element offset
+ *     ((N-1)*stride_n + head_dim) must be below 2^32.
+ */
+#ifndef VDSA_H
+#define VDSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VDSA_ABI_VERSION 1
+
+typedef enum {
+  VDSA_OK = 0,
+  VDSA_ERR_NULL = 1,        /* a required pointer is NULL */
+  VDSA_ERR_SHAPE = 2,       /* a dimension <= 0, or an offset beyond the size limit */
+  VDSA_ERR_WINDOW = 3,      /* tile < 1, window even or < 1, shift outside [0, tile), pool < 1 */
+  VDSA_ERR_UNSUPPORTED = 4, /* head_dim not in {64, 128}, unknown dtype, non-finite scale */
+  VDSA_ERR_ALIGN = 5,       /* pointer or stride breaks the 16-byte rule */
+  VDSA_ERR_ALIAS = 6,       /* an output overlaps an input it must not overlap */
+  VDSA_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than the reported size */
+  VDSA_ERR_HIP = 8          /* the HIP runtime rejected a launch */
+} vdsa_status;
+
+typedef enum { VDSA_F32 = 0, VDSA_BF16 = 1 } vdsa_dtype;
+
+/* Element strides of a [batch, heads, N, head_dim] view; head_dim stride is 1. */
+typedef struct {
+  int64_t b, h, n;
+} vdsa_strides;
+
+typedef struct {
+  int32_t batch, heads, head_dim;   /* head_dim in {64, 128} */
+  int32_t grid_t, grid_h, grid_w;   /* N = grid_t * grid_h * grid_w */
+  vdsa_dtype dtype;
+  float scale;                      /* logits = scale * (q . k) */
+} vdsa_problem;
+
+/*
+ * Sliding-tile configuration, all in tokens except `window` (in tiles).
+ *   tile[d]   >= 1: tile extent per dim (t, h, w).
+ *   window[d] odd >= 1: a query tile attends the key tiles whose tile index
+ *             differs from its own by at most (window[d]-1)/2 in every dim,
+ *             clipped at the grid edge (Sliding Tile Attention, arXiv
+ *             2502.04507, abstract: tile-by-tile attention over a local 3D
+ *             window of tiles).  window[d] >= 2*tiles[d]-1 in every dim is
+ *             full attention.
+ *   shift[d]  in [0, tile[d]): tile index of coordinate x is
+ *             floor((x + shift) / tile), a non-cyclic offset of the tile
+ *             lattice that makes edge tiles partial (the shifted partition of
+ *             UltraGen section 4.3, "Cross-window Hierarchical Local
+ *             Attention").  Partial tiles hold only real tokens.
+ */
+typedef struct {
+  int32_t tile[3];
+  int32_t window[3];
+  int32_t shift[3];
+} vdsa_sta_cfg;
+
+/*
+ * sta_attn_fwd - sliding-tile 3D attention (local branch).
+ *
+ * For every (b, h, query token n):
+ *   O[n] = sum_m softmax_m(scale * Q[n].K[m]) V[m]
+ * over the keys m whose tile is inside the window of n's tile.  The window
+ * map is computed in-kernel; no mask is materialised.
+ *
+ *   q, k, v : device, [batch, heads, N, head_dim] with the given strides.
+ *   o       : device output, same shape; must not overlap q, k, v or lse.
+ *   lse     : optional device output (NULL to skip), fp32 [batch, heads, N]
+ *             contiguous: natural-log sum of exp(scale * q.k) over the window.
+ * Errors: VDSA_ERR_NULL, _SHAPE, _WINDOW, _UNSUPPORTED, _ALIGN, _ALIAS, _HIP.
+ */
+vdsa_status sta_attn_fwd(const vdsa_problem* prob, const vdsa_sta_cfg* cfg,
+                         const void* q, const vdsa_strides* q_strides,
+                         const void* k, const vdsa_strides* k_strides,
+                         const void* v, const vdsa_strides* v_strides,
+                         void* o, const vdsa_strides* o_strides,
+                         float* lse, void* stream);
+
+/*
+ * global_pooled_attn_workspace_size - bytes of device workspace that
+ * global_pooled_attn_fwd needs for `prob` and `pool_hw` (pooled K and V).
+ */
+vdsa_status global_pooled_attn_workspace_size(const vdsa_problem* prob, const int32_t pool_hw[2],
+                                              size_t* bytes);
+
+/*
+ * global_pooled_attn_fwd - compressed global branch.
+ *
+ * K and V are average-pooled pool_hw[0] x pool_hw[1] within each frame
+ * (frames are not pooled; a cell past the frame edge averages its real
+ * tokens only), giving M = T * ceil(H/ph) * ceil(W/pw) pooled tokens in raster
+ * order; then every full-resolution query attends all M pooled keys, unmasked:
+ *   O[n] = sum_m softmax_m(scale * Q[n].Kp[m]) Vp[m].
+ * (UltraGen section 4.2 "Spatially-Compressed Global Attention": frame-wise
+ * stride-k compression before attention, here with uniform 1/(ph*pw)
+ * weights; AtlasVid, arXiv 2605.16649, abstract: asymmetric global-local
+ * attention, i.e. queries stay at full resolution.)  Pooled K/V are stored in
+ * the I/O dtype in `workspace`.
+ *
+ *   workspace : device, at least global_pooled_attn_workspace_size() bytes,
+ *               16-byte aligned, not overlapping any tensor argument.  Its
+ *               contents after the call are the pooled K then pooled V,
+ *               each [batch, heads, M, head_dim] contiguous.
+ * Errors: as sta_attn_fwd, plus VDSA_ERR_WORKSPACE.
+ */
+vdsa_status global_pooled_attn_fwd(const vdsa_problem* prob, const int32_t pool_hw[2],
+                                   const void* q, const vdsa_strides* q_strides,
+                                   const void* k, const vdsa_strides* k_strides,
+                                   const void* v, const vdsa_strides* v_strides,
+                                   void* o, const vdsa_strides* o_strides,
+                                   float* lse, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/*
+ * dual_branch_merge - gated sum of the two branch outputs (UltraGen section
+ * 4.1 "Time-Aware Global-Local Attention": a fusion factor combines the local
+ * and the global latent; here one factor per head):
+ *   out[b,h,n,:] = w_local[h] * o_local[b,h,n,:] + w_global[h] * o_global[b,h,n,:]
+ *
+ *   w_local  : device fp32 [heads], or NULL for all ones.
+ *   w_global : device fp32 [heads].
+ *   out      : may be exactly o_local (same pointer and strides, in place);
+ *              must not otherwise overlap o_local or o_global.
+ * Errors: VDSA_ERR_NULL, _SHAPE, _UNSUPPORTED, _ALIGN, _ALIAS, _HIP.
+ */
+vdsa_status dual_branch_merge(const vdsa_problem* prob,
+                              const void* o_local, const vdsa_strides* local_strides,
+                              const void* o_global, const vdsa_strides* global_strides,
+                              const float* w_local, const float* w_global,
+                              void* out, const vdsa_strides* out_strides, void* stream);
+
+/*
+ * kv_avgpool_fwd - the pooling step of global_pooled_attn_fwd on one tensor,
+ * exported so it can be checked and timed alone.  x_pooled is
+ * [batch, heads, M, head_dim] with its own strides; must not overlap x.
+ */
+vdsa_status kv_avgpool_fwd(const vdsa_problem* prob, const int32_t pool_hw[2],
+                           const void* x, const vdsa_strides* x_strides,
+                           void* x_pooled, const vdsa_strides* pooled_strides, void* stream);
+
+/* Effective work: 4 * head_dim FLOP per attended (query, key) token pair
+ * (2*head_dim for q.k, 2*head_dim for p*v), summed over batch and heads;
+ * partial tiles count their real tokens only.  Host only. */
+vdsa_status vdsa_sta_flops(const vdsa_problem* prob, const vdsa_sta_cfg* cfg, double* flops);
+vdsa_status vdsa_global_flops(const vdsa_problem* prob, const int32_t pool_hw[2], double* flops);
+
+const char* vdsa_status_string(vdsa_status s);
+const char* vdsa_last_error(void);   /* thread-local detail of the last failed call */
+int vdsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VDSA_H */

@@ -1,0 +1,56 @@
+"""Shared helpers of the GPU parity tests: tolerances, comparison and row
+sampling.  Test infrastructure only."""
+import numpy as np
+
+import oracle as R
+
+# bf16 inputs: max abs error <= 2e-2 and mean abs error <= 2e-3 against the
+# fp64 oracle; fp32 path: max abs error <= 1e-4.
+TOL = {"bf16": (2e-2, 2e-3), "f32": (1e-4, 1e-4)}
+
+
+def compare(got, ref, dtype, what=""):
+    """Element-by-element comparison of a GPU result (any array-like) with the
+    oracle's fp64 result; returns (max, mean) abs error, asserts the bar."""
+    g = R.to_f64(got)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    assert np.isfinite(g).all(), f"{what}: non-finite values"
+    err = np.abs(g - r)
+    mx, mean = float(err.max()), float(err.mean())
+    tmax, tmean = TOL[dtype]
+    assert mx <= tmax and mean <= tmean, f"{what}: max err {mx:.3e} (<= {tmax}), mean {mean:.3e} (<= {tmean})"
+    return mx, mean
+
+
+def sample_rows(grid, tile, shift, n_random_tiles=6, rows_per_tile=48, seed=0):
+    """Query rows from the corner tiles of the tile lattice, a few edge tiles
+    and random tiles; per tile its first and last token (tile-local raster
+    order) plus random ones.  Returns sorted token indices."""
+    rng = np.random.default_rng(seed)
+    counts = R.tile_counts(grid, tile, shift)
+    T, H, W = grid
+    picks = set()
+    for ct in (0, counts[0] - 1):
+        for ch in (0, counts[1] - 1):
+            for cw in (0, counts[2] - 1):
+                picks.add((ct, ch, cw))
+    picks.add((counts[0] // 2, 0, counts[2] // 2))
+    picks.add((0, counts[1] // 2, counts[2] - 1))
+    for _ in range(n_random_tiles):
+        picks.add(tuple(int(rng.integers(0, c)) for c in counts))
+    rows = []
+    for a in sorted(picks):
+        ext = [R.tile_extent(i, L, b, s) for i, L, b, s in zip(a, grid, tile, shift)]
+        tt, hh, ww = np.meshgrid(*[np.arange(lo, hi) for lo, hi in ext], indexing="ij")
+        toks = ((tt * H + hh) * W + ww).reshape(-1)
+        chosen = {int(toks[0]), int(toks[-1])}
+        if len(toks) > 2:
+            chosen.update(int(x) for x in rng.choice(toks, size=min(rows_per_tile, len(toks)), replace=False))
+        rows.extend(chosen)
+    return np.array(sorted(set(rows)), dtype=np.int64)
+
+
+def head_f64(x, b, h):
+    """One (batch, head) slice of a [B, heads, N, D] tensor as fp64 NumPy."""
+    return R.to_f64(x[b, h])

@@ -1,0 +1,175 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+Every error path is forced with argument values the host rejects before
+enqueueing anything; the fake device addresses used here are never
+dereferenced."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle as R
+from video_dit_sparse_amd import _lib as L
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "vdsa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH), reason="libvdsa.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(L.EXPORTED), names
+    lib = L.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    assert L.abi_version() == 1
+    for code in L.STATUS_NAMES:
+        assert L.lib().vdsa_status_string(code)
+
+
+# fake, 256-aligned device addresses: validation fails before any use
+Q, K, V, O, LSE, WS = (0x10000000 * (i + 1) for i in range(6))
+
+
+def prob(**kw):
+    d = dict(batch=1, heads=2, head_dim=128, grid=(4, 8, 8), dtype=L.VDSA_BF16, scale=0.125)
+    d.update(kw)
+    return L.make_problem(d["batch"], d["heads"], d["head_dim"], d["grid"], d["dtype"], d["scale"])
+
+
+def st(p, D=128):
+    N = p.grid_t * p.grid_h * p.grid_w
+    return L.Strides(p.heads * N * D, N * D, D)
+
+
+def sta(p, cfg, q=Q, k=K, v=V, o=O, lse=None, strides=None):
+    s = strides or {}
+    d = st(p, p.head_dim)
+    return L.lib().sta_attn_fwd(ctypes.byref(p), ctypes.byref(cfg) if cfg is not None else None,
+                                q, ctypes.byref(s.get("q", d)), k, ctypes.byref(s.get("k", d)),
+                                v, ctypes.byref(s.get("v", d)), o, ctypes.byref(s.get("o", d)), lse, None)
+
+
+GOOD_CFG = dict(tile=(2, 4, 4), window=(3, 3, 3), shift=(0, 0, 0))
+
+
+def cfg(**kw):
+    d = dict(GOOD_CFG)
+    d.update(kw)
+    return L.make_cfg(d["tile"], d["window"], d["shift"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(tile=(0, 4, 4)), "VDSA_ERR_WINDOW"),
+    (dict(window=(2, 3, 3)), "VDSA_ERR_WINDOW"),
+    (dict(window=(3, 0, 3)), "VDSA_ERR_WINDOW"),
+    (dict(shift=(2, 0, 0)), "VDSA_ERR_WINDOW"),
+    (dict(shift=(0, -1, 0)), "VDSA_ERR_WINDOW"),
+])
+def test_bad_window_config(kw, code):
+    assert sta(prob(), cfg(**kw)) == L.STATUS[code]
+    assert L.lib().vdsa_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), "VDSA_ERR_UNSUPPORTED"),
+    (dict(dtype=7), "VDSA_ERR_UNSUPPORTED"),
+    (dict(scale=float("nan")), "VDSA_ERR_UNSUPPORTED"),
+    (dict(scale=-1.0), "VDSA_ERR_UNSUPPORTED"),
+    (dict(heads=0), "VDSA_ERR_SHAPE"),
+    (dict(grid=(0, 8, 8)), "VDSA_ERR_SHAPE"),
+])
+def test_bad_problem(kw, code):
+    assert sta(prob(**kw), cfg()) == L.STATUS[code]
+
+
+def test_null_pointers():
+    p = prob()
+    assert L.lib().sta_attn_fwd(None, ctypes.byref(cfg()), Q, None, K, None, V, None, O, None, None, None) == 1
+    assert sta(p, None) == L.STATUS["VDSA_ERR_NULL"]
+    assert sta(p, cfg(), q=None) == L.STATUS["VDSA_ERR_NULL"]
+    assert sta(p, cfg(), o=None) == L.STATUS["VDSA_ERR_NULL"]
+
+
+def test_misaligned_pointer_and_stride():
+    p = prob()
+    assert sta(p, cfg(), k=K + 2) == L.STATUS["VDSA_ERR_ALIGN"]
+    bad = L.Strides(2 * 256 * 136, 256 * 136, 132)   # 132 bf16 = 264 bytes: not a multiple of 16
+    assert sta(p, cfg(), strides={"v": bad}) == L.STATUS["VDSA_ERR_ALIGN"]
+    assert sta(p, cfg(), lse=LSE + 2) == L.STATUS["VDSA_ERR_ALIGN"]
+
+
+def test_aliasing():
+    p = prob()
+    assert sta(p, cfg(), o=Q) == L.STATUS["VDSA_ERR_ALIAS"]
+    assert sta(p, cfg(), o=V + 1024) == L.STATUS["VDSA_ERR_ALIAS"]
+    assert sta(p, cfg(), lse=O + 64) == L.STATUS["VDSA_ERR_ALIAS"]
+    # output rows overlapping each other (token stride smaller than head_dim)
+    assert sta(p, cfg(), strides={"o": L.Strides(2 * 256 * 64, 256 * 64, 64)}) == L.STATUS["VDSA_ERR_ALIAS"]
+
+
+def test_offset_limit():
+    # 2^32 elements of token offset inside one head is beyond the kernels' addressing
+    p = prob(grid=(64, 256, 256))
+    big = L.Strides(0, 0, 1 << 20)
+    assert sta(p, cfg(), strides={"q": big}) == L.STATUS["VDSA_ERR_SHAPE"]
+
+
+def test_global_workspace_checks():
+    p = prob()
+    pool = (ctypes.c_int32 * 2)(4, 4)
+    n = ctypes.c_size_t()
+    assert L.lib().global_pooled_attn_workspace_size(ctypes.byref(p), pool, ctypes.byref(n)) == 0
+    M = 4 * 2 * 2
+    assert n.value == 2 * (((1 * 2 * M * 128 * 2) + 255) // 256 * 256)
+    d = st(p)
+    args = lambda ws, wsb, pl=pool: L.lib().global_pooled_attn_fwd(
+        ctypes.byref(p), pl, Q, ctypes.byref(d), K, ctypes.byref(d), V, ctypes.byref(d), O, ctypes.byref(d),
+        None, ws, wsb, None)
+    assert args(None, n.value) == L.STATUS["VDSA_ERR_WORKSPACE"]
+    assert args(WS, n.value - 1) == L.STATUS["VDSA_ERR_WORKSPACE"]
+    assert args(Q + 256, n.value) == L.STATUS["VDSA_ERR_ALIAS"]
+    assert args(WS, n.value, (ctypes.c_int32 * 2)(0, 4)) == L.STATUS["VDSA_ERR_WINDOW"]
+
+
+def test_merge_checks():
+    p = prob()
+    d = st(p)
+    m = lambda a, g, wl, wg, o: L.lib().dual_branch_merge(ctypes.byref(p), a, ctypes.byref(d), g, ctypes.byref(d),
+                                                           wl, wg, o, ctypes.byref(d), None)
+    assert m(Q, K, None, None, O) == L.STATUS["VDSA_ERR_NULL"]
+    assert m(Q, K, None, WS, K) == L.STATUS["VDSA_ERR_ALIAS"]          # out == o_global
+    assert m(Q, K, None, WS, Q + 512) == L.STATUS["VDSA_ERR_ALIAS"]    # partial overlap with o_local
+    assert m(Q, K, None, WS + 2, O) == L.STATUS["VDSA_ERR_ALIGN"]
+
+
+FLOP_CASES = [
+    ((4, 8, 8), (2, 4, 4), (3, 3, 3), (0, 0, 0)),
+    ((30, 48, 80), (6, 8, 8), (3, 3, 5), (0, 0, 0)),
+    ((21, 68, 120), (21, 17, 30), (1, 1, 1), (0, 0, 0)),
+    ((21, 90, 160), (4, 8, 8), (1, 1, 1), (0, 0, 0)),
+    ((21, 90, 160), (4, 8, 8), (1, 1, 1), (2, 4, 4)),
+    ((7, 13, 21), (3, 4, 8), (3, 3, 1), (1, 2, 4)),
+    ((5, 9, 11), (2, 3, 3), (1, 3, 5), (1, 0, 2)),
+]
+
+
+@pytest.mark.parametrize("grid,tile,window,shift", FLOP_CASES)
+def test_flop_counter_matches_oracle(grid, tile, window, shift):
+    got = L.sta_flops(1, 3, 128, grid, tile, window, shift)
+    assert got == R.sta_flops_ref(grid, tile, window, shift, head_dim=128, heads=3)
+
+
+def test_global_flop_counter_matches_oracle():
+    for grid, pool in [((21, 68, 120), (4, 4)), ((21, 136, 240), (8, 8)), ((3, 9, 10), (4, 3))]:
+        assert L.global_flops(1, 24, 128, grid, pool) == R.global_flops_ref(grid, pool, head_dim=128, heads=24)

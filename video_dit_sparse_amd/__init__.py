@@ -1,0 +1,18 @@
+"""Tile-window sparse attention for video latents on MI355X (gfx950).
+
+Python face of libvdsa.so: the three calls of the hot path
+(``sta_attn_fwd``, ``global_pooled_attn_fwd``, ``dual_branch_merge``), the
+pooling step alone (``kv_avgpool_fwd``) and the effective-work counters.
+"""
+from ._lib import (  # noqa: F401
+    VdsaError,
+    abi_version,
+    dual_branch_merge,
+    global_flops,
+    global_pooled_attn_fwd,
+    global_pooled_attn_workspace_size,
+    kv_avgpool_fwd,
+    lib,
+    sta_attn_fwd,
+    sta_flops,
+)

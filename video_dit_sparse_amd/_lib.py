@@ -1,0 +1,257 @@
+"""ctypes binding of libvdsa.so (include/vdsa.h).
+
+Argument marshalling only: torch tensors become device pointers and element
+strides, torch's current stream becomes the HIP stream, and every step of the
+computation runs in the library's kernels.  Torch supplies device memory for
+outputs and workspaces.  If the library is missing this module raises; there
+is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libvdsa.so")
+
+VDSA_F32, VDSA_BF16 = 0, 1
+STATUS_NAMES = {
+    0: "VDSA_OK", 1: "VDSA_ERR_NULL", 2: "VDSA_ERR_SHAPE", 3: "VDSA_ERR_WINDOW",
+    4: "VDSA_ERR_UNSUPPORTED", 5: "VDSA_ERR_ALIGN", 6: "VDSA_ERR_ALIAS",
+    7: "VDSA_ERR_WORKSPACE", 8: "VDSA_ERR_HIP",
+}
+STATUS = {v: k for k, v in STATUS_NAMES.items()}
+
+# every symbol include/vdsa.h declares
+EXPORTED = [
+    "sta_attn_fwd", "global_pooled_attn_workspace_size", "global_pooled_attn_fwd",
+    "dual_branch_merge", "kv_avgpool_fwd", "vdsa_sta_flops", "vdsa_global_flops",
+    "vdsa_status_string", "vdsa_last_error", "vdsa_abi_version",
+]
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("grid_t", ctypes.c_int32), ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
+                ("dtype", ctypes.c_int), ("scale", ctypes.c_float)]
+
+
+class StaCfg(ctypes.Structure):
+    _fields_ = [("tile", ctypes.c_int32 * 3), ("window", ctypes.c_int32 * 3), ("shift", ctypes.c_int32 * 3)]
+
+
+class Strides(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("n", ctypes.c_int64)]
+
+
+class VdsaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.name = STATUS_NAMES.get(status, str(status))
+        super().__init__(f"{self.name}: {detail}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libvdsa.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m video_dit_sparse_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, C, S = ctypes.POINTER(Problem), ctypes.POINTER(StaCfg), ctypes.POINTER(Strides)
+    vp, i32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
+    fp = ctypes.c_void_p  # float* passed as an address
+    L.sta_attn_fwd.argtypes = [P, C, vp, S, vp, S, vp, S, vp, S, fp, vp]
+    L.global_pooled_attn_workspace_size.argtypes = [P, i32p, ctypes.POINTER(ctypes.c_size_t)]
+    L.global_pooled_attn_fwd.argtypes = [P, i32p, vp, S, vp, S, vp, S, vp, S, fp, vp, ctypes.c_size_t, vp]
+    L.dual_branch_merge.argtypes = [P, vp, S, vp, S, fp, fp, vp, S, vp]
+    L.kv_avgpool_fwd.argtypes = [P, i32p, vp, S, vp, S, vp]
+    L.vdsa_sta_flops.argtypes = [P, C, ctypes.POINTER(ctypes.c_double)]
+    L.vdsa_global_flops.argtypes = [P, i32p, ctypes.POINTER(ctypes.c_double)]
+    L.vdsa_status_string.argtypes = [ctypes.c_int]
+    L.vdsa_status_string.restype = ctypes.c_char_p
+    L.vdsa_last_error.argtypes = []
+    L.vdsa_last_error.restype = ctypes.c_char_p
+    L.vdsa_abi_version.argtypes = []
+    for name in ("sta_attn_fwd", "global_pooled_attn_workspace_size", "global_pooled_attn_fwd",
+                 "dual_branch_merge", "kv_avgpool_fwd", "vdsa_sta_flops", "vdsa_global_flops",
+                 "vdsa_abi_version"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def check(status: int) -> None:
+    if status != 0:
+        raise VdsaError(status, lib().vdsa_last_error().decode())
+
+
+# ---------------------------------------------------------------- descriptors
+def make_problem(batch, heads, head_dim, grid, dtype: int, scale: float) -> Problem:
+    return Problem(int(batch), int(heads), int(head_dim), int(grid[0]), int(grid[1]), int(grid[2]),
+                   int(dtype), float(scale))
+
+
+def make_cfg(tile, window, shift=(0, 0, 0)) -> StaCfg:
+    c = StaCfg()
+    for i in range(3):
+        c.tile[i], c.window[i], c.shift[i] = int(tile[i]), int(window[i]), int(shift[i])
+    return c
+
+
+def _pool(pool_hw) -> ctypes.Array:
+    return (ctypes.c_int32 * 2)(int(pool_hw[0]), int(pool_hw[1]))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return VDSA_BF16
+    if t.dtype == torch.float32:
+        return VDSA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _strides(t) -> Strides:
+    if t.dim() != 4:
+        raise ValueError(f"expected a [batch, heads, N, head_dim] tensor, got shape {tuple(t.shape)}")
+    if t.stride(3) != 1:
+        raise ValueError("head_dim must be the contiguous dimension")
+    return Strides(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return _torch().cuda.current_stream().cuda_stream
+    return int(stream) if not hasattr(stream, "cuda_stream") else stream.cuda_stream
+
+
+def _problem_for(q, grid, scale) -> Problem:
+    B, Hh, N, D = q.shape
+    T, H, W = grid
+    if T * H * W != N:
+        raise ValueError(f"grid {tuple(grid)} has {T * H * W} tokens but tensors have N = {N}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    return make_problem(B, Hh, D, grid, _dtype_code(q), scale)
+
+
+def _same(q, *others):
+    for t in others:
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v (and outputs) must share shape, dtype and device")
+
+
+# ---------------------------------------------------------------- entry points
+def sta_attn_fwd(q, k, v, grid: Sequence[int], tile: Sequence[int], window: Sequence[int],
+                 shift: Sequence[int] = (0, 0, 0), scale: Optional[float] = None, out=None,
+                 lse=None, return_lse: bool = False, stream=None):
+    """Sliding-tile attention (see ``sta_attn_fwd`` in include/vdsa.h).
+
+    q, k, v: [B, heads, N, D] device tensors (bf16 or fp32), N = T*H*W.
+    Returns O (and LSE [B, heads, N] fp32 if requested).
+    """
+    torch = _torch()
+    _same(q, k, v)
+    prob = _problem_for(q, grid, scale)
+    cfg = make_cfg(tile, window, shift)
+    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    if lse is None and return_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    check(lib().sta_attn_fwd(ctypes.byref(prob), ctypes.byref(cfg),
+                             q.data_ptr(), ctypes.byref(_strides(q)), k.data_ptr(), ctypes.byref(_strides(k)),
+                             v.data_ptr(), ctypes.byref(_strides(v)), o.data_ptr(), ctypes.byref(_strides(o)),
+                             lse.data_ptr() if lse is not None else None, _stream(stream)))
+    return (o, lse) if (return_lse or lse is not None) else o
+
+
+def global_pooled_attn_workspace_size(batch, heads, head_dim, grid, pool_hw, dtype_code=VDSA_BF16) -> int:
+    prob = make_problem(batch, heads, head_dim, grid, dtype_code, 1.0)
+    n = ctypes.c_size_t()
+    check(lib().global_pooled_attn_workspace_size(ctypes.byref(prob), _pool(pool_hw), ctypes.byref(n)))
+    return n.value
+
+
+def global_pooled_attn_fwd(q, k, v, grid, pool_hw, scale=None, out=None, lse=None, return_lse=False,
+                           workspace=None, stream=None):
+    """Global branch: queries attend k_h x k_w average-pooled K/V
+    (``global_pooled_attn_fwd`` in include/vdsa.h).  Returns O (and LSE)."""
+    torch = _torch()
+    _same(q, k, v)
+    prob = _problem_for(q, grid, scale)
+    need = ctypes.c_size_t()
+    check(lib().global_pooled_attn_workspace_size(ctypes.byref(prob), _pool(pool_hw), ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    if lse is None and return_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    check(lib().global_pooled_attn_fwd(
+        ctypes.byref(prob), _pool(pool_hw), q.data_ptr(), ctypes.byref(_strides(q)),
+        k.data_ptr(), ctypes.byref(_strides(k)), v.data_ptr(), ctypes.byref(_strides(v)),
+        o.data_ptr(), ctypes.byref(_strides(o)), lse.data_ptr() if lse is not None else None,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return (o, lse) if (return_lse or lse is not None) else o
+
+
+def dual_branch_merge(o_local, o_global, w_global, w_local=None, out=None, stream=None):
+    """out = w_local[h] * o_local + w_global[h] * o_global (``dual_branch_merge``).
+
+    ``out=o_local`` merges in place."""
+    torch = _torch()
+    _same(o_local, o_global)
+    B, Hh, N, D = o_local.shape
+    prob = make_problem(B, Hh, D, (1, 1, N), _dtype_code(o_local), 1.0)
+    o = torch.empty_like(o_local, memory_format=torch.contiguous_format) if out is None else out
+    for w in (w_global, w_local):
+        if w is not None and (w.dtype != torch.float32 or w.numel() != Hh or not w.is_contiguous()):
+            raise ValueError("gates must be contiguous float32 tensors of length heads")
+    check(lib().dual_branch_merge(ctypes.byref(prob), o_local.data_ptr(), ctypes.byref(_strides(o_local)),
+                                  o_global.data_ptr(), ctypes.byref(_strides(o_global)),
+                                  w_local.data_ptr() if w_local is not None else None, w_global.data_ptr(),
+                                  o.data_ptr(), ctypes.byref(_strides(o)), _stream(stream)))
+    return o
+
+
+def kv_avgpool_fwd(x, grid, pool_hw, out=None, stream=None):
+    """k_h x k_w frame-wise average pooling of a [B, heads, N, D] tensor."""
+    torch = _torch()
+    B, Hh, N, D = x.shape
+    prob = _problem_for(x, grid, 1.0)
+    T, H, W = grid
+    M = T * (-(-H // pool_hw[0])) * (-(-W // pool_hw[1]))
+    y = torch.empty((B, Hh, M, D), dtype=x.dtype, device=x.device) if out is None else out
+    check(lib().kv_avgpool_fwd(ctypes.byref(prob), _pool(pool_hw), x.data_ptr(), ctypes.byref(_strides(x)),
+                               y.data_ptr(), ctypes.byref(_strides(y)), _stream(stream)))
+    return y
+
+
+def sta_flops(batch, heads, head_dim, grid, tile, window, shift=(0, 0, 0)) -> float:
+    """Effective FLOP of one sta_attn_fwd call (4*D per attended token pair)."""
+    prob = make_problem(batch, heads, head_dim, grid, VDSA_BF16, 1.0)
+    cfg = make_cfg(tile, window, shift)
+    f = ctypes.c_double()
+    check(lib().vdsa_sta_flops(ctypes.byref(prob), ctypes.byref(cfg), ctypes.byref(f)))
+    return f.value
+
+
+def global_flops(batch, heads, head_dim, grid, pool_hw) -> float:
+    prob = make_problem(batch, heads, head_dim, grid, VDSA_BF16, 1.0)
+    f = ctypes.c_double()
+    check(lib().vdsa_global_flops(ctypes.byref(prob), _pool(pool_hw), ctypes.byref(f)))
+    return f.value
+
+
+def abi_version() -> int:
+    return lib().vdsa_abi_version()

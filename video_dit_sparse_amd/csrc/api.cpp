@@ -1,0 +1,440 @@
+// Host side of the C ABI declared in include/vdsa.h: argument checks (all of
+// them before anything is enqueued), kernel parameter setup and dispatch,
+// effective-work counters and error strings.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <utility>
+
+#include "internal.h"
+#include "vdsa.h"
+
+namespace vdsa {
+int box_attn_bf16_block_m();
+int box_attn_f32_block_m();
+}  // namespace vdsa
+
+namespace {
+
+thread_local std::string g_last_error;
+
+vdsa_status fail(vdsa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+vdsa_status ok() {
+  g_last_error.clear();
+  return VDSA_OK;
+}
+
+size_t elem_size(vdsa_dtype t) { return t == VDSA_BF16 ? 2 : 4; }
+
+vdsa_status check_problem(const vdsa_problem* p) {
+  if (!p) return fail(VDSA_ERR_NULL, "problem descriptor is NULL");
+  if (p->batch <= 0 || p->heads <= 0 || p->grid_t <= 0 || p->grid_h <= 0 || p->grid_w <= 0)
+    return fail(VDSA_ERR_SHAPE, "batch, heads and grid dims must be > 0 (got batch=%d heads=%d grid=%dx%dx%d)",
+                p->batch, p->heads, p->grid_t, p->grid_h, p->grid_w);
+  if (p->dtype != VDSA_F32 && p->dtype != VDSA_BF16)
+    return fail(VDSA_ERR_UNSUPPORTED, "dtype %d is not VDSA_F32 or VDSA_BF16", (int)p->dtype);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(VDSA_ERR_UNSUPPORTED, "head_dim %d is not 64 or 128", p->head_dim);
+  if (!std::isfinite(p->scale) || p->scale < 0.f)
+    return fail(VDSA_ERR_UNSUPPORTED, "scale must be finite and >= 0 (got %g)", (double)p->scale);
+  const int64_t n = (int64_t)p->grid_t * p->grid_h * p->grid_w;
+  if (n >= (int64_t(1) << 31)) return fail(VDSA_ERR_SHAPE, "N = %lld tokens is too large", (long long)n);
+  return VDSA_OK;
+}
+
+int64_t n_tokens(const vdsa_problem* p) { return (int64_t)p->grid_t * p->grid_h * p->grid_w; }
+
+// A [batch, heads, rows, head_dim] view: checks and its byte range.
+struct View {
+  const char* name;
+  const void* ptr;
+  const vdsa_strides* st;
+  int64_t rows;
+  uintptr_t lo = 0, hi = 0;  // byte range [lo, hi)
+};
+
+vdsa_status check_view(const vdsa_problem* p, View& v, bool is_output) {
+  if (!v.ptr) return fail(VDSA_ERR_NULL, "%s pointer is NULL", v.name);
+  if (!v.st) return fail(VDSA_ERR_NULL, "%s strides pointer is NULL", v.name);
+  const size_t es = elem_size(p->dtype);
+  const int64_t ext[3] = {p->batch, p->heads, v.rows};
+  const int64_t str[3] = {v.st->b, v.st->h, v.st->n};
+  const char* nm[3] = {"batch", "head", "token"};
+  if ((uintptr_t)v.ptr % 16 != 0) return fail(VDSA_ERR_ALIGN, "%s pointer is not 16-byte aligned", v.name);
+  int64_t max_off = p->head_dim;
+  for (int d = 0; d < 3; ++d) {
+    if (ext[d] == 1) continue;  // the stride of an extent-1 dim is never used
+    if (str[d] <= 0) return fail(VDSA_ERR_SHAPE, "%s %s stride must be > 0 (got %lld)", v.name, nm[d], (long long)str[d]);
+    if ((str[d] * (int64_t)es) % 16 != 0)
+      return fail(VDSA_ERR_ALIGN, "%s %s stride %lld x %zu bytes is not a multiple of 16", v.name, nm[d],
+                  (long long)str[d], es);
+    max_off += (ext[d] - 1) * str[d];
+  }
+  const int64_t row_span = (v.rows - 1) * (v.rows > 1 ? str[2] : 0) + p->head_dim;
+  if (row_span >= (int64_t(1) << 32))
+    return fail(VDSA_ERR_SHAPE, "%s: token offsets within one head reach %lld elements (limit 2^32)", v.name,
+                (long long)row_span);
+  if (is_output) {
+    // rows of the output must not overlap each other: sort the used dims by
+    // stride; each stride must cover the span of all smaller ones.
+    std::pair<int64_t, int64_t> dims[3];  // (stride, extent)
+    int nd = 0;
+    for (int d = 0; d < 3; ++d)
+      if (ext[d] > 1) dims[nd++] = {str[d], ext[d]};
+    std::sort(dims, dims + nd);
+    int64_t span = p->head_dim;
+    for (int i = 0; i < nd; ++i) {
+      if (dims[i].first < span) return fail(VDSA_ERR_ALIAS, "%s: strides make output rows overlap each other", v.name);
+      span = dims[i].first * (dims[i].second - 1) + span;
+    }
+  }
+  v.lo = (uintptr_t)v.ptr;
+  v.hi = v.lo + (uintptr_t)(max_off * (int64_t)es);
+  return VDSA_OK;
+}
+
+bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
+
+vdsa_status check_sta_cfg(const vdsa_sta_cfg* c) {
+  if (!c) return fail(VDSA_ERR_NULL, "sta config is NULL");
+  const char* nm[3] = {"t", "h", "w"};
+  for (int d = 0; d < 3; ++d) {
+    if (c->tile[d] < 1) return fail(VDSA_ERR_WINDOW, "tile[%s] = %d must be >= 1", nm[d], c->tile[d]);
+    if (c->window[d] < 1 || c->window[d] % 2 == 0)
+      return fail(VDSA_ERR_WINDOW, "window[%s] = %d must be odd and >= 1", nm[d], c->window[d]);
+    if (c->shift[d] < 0 || c->shift[d] >= c->tile[d])
+      return fail(VDSA_ERR_WINDOW, "shift[%s] = %d must be in [0, tile = %d)", nm[d], c->shift[d], c->tile[d]);
+  }
+  return VDSA_OK;
+}
+
+int tiles_along(int L, int b, int s) { return (L + s + b - 1) / b; }
+
+// Largest number of real tokens in one tile along a dim.
+int max_tile_extent(int L, int b, int s) {
+  const int n = tiles_along(L, b, s);
+  int best = 0;
+  // interior tiles have b tokens; only the first and last can be partial
+  for (int i : {0, 1, n - 2, n - 1}) {
+    if (i < 0 || i >= n) continue;
+    const int lo = std::max(0, i * b - s), hi = std::min(L, (i + 1) * b - s);
+    best = std::max(best, hi - lo);
+  }
+  return best;
+}
+
+vdsa_status launch_attn(const vdsa_problem* prob, vdsa::BoxAttnParams& bp, hipStream_t stream) {
+  const int bm = prob->dtype == VDSA_BF16 ? vdsa::box_attn_bf16_block_m() : vdsa::box_attn_f32_block_m();
+  const int64_t mv = (int64_t)max_tile_extent(bp.qT, bp.bT, bp.sT) * max_tile_extent(bp.qH, bp.bH, bp.sH) *
+                     max_tile_extent(bp.qW, bp.bW, bp.sW);
+  bp.qblocks = (int32_t)((mv + bm - 1) / bm);
+  const int64_t total = (int64_t)bp.batch * bp.heads * bp.nT * bp.nH * bp.nW * bp.qblocks;
+  if (total >= (int64_t(1) << 31) / 256)
+    return fail(VDSA_ERR_SHAPE, "problem needs %lld workgroups, beyond the launch limit", (long long)total);
+  bp.total_wg = (int32_t)total;
+  bp.scale_log2e = prob->scale * 1.4426950408889634f;
+  hipError_t e = prob->dtype == VDSA_BF16 ? vdsa::launch_box_attn_bf16(bp, prob->head_dim, stream)
+                                          : vdsa::launch_box_attn_f32(bp, prob->head_dim, stream);
+  if (e != hipSuccess) return fail(VDSA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+void set_qkvo(vdsa::BoxAttnParams& bp, const View& q, const View& k, const View& v, const View& o) {
+  bp.q = q.ptr;
+  bp.k = k.ptr;
+  bp.v = v.ptr;
+  bp.o = const_cast<void*>(o.ptr);
+  bp.q_sb = q.st->b; bp.q_sh = q.st->h; bp.q_sn = q.st->n;
+  bp.k_sb = k.st->b; bp.k_sh = k.st->h; bp.k_sn = k.st->n;
+  bp.v_sb = v.st->b; bp.v_sh = v.st->h; bp.v_sn = v.st->n;
+  bp.o_sb = o.st->b; bp.o_sh = o.st->h; bp.o_sn = o.st->n;
+}
+
+vdsa_status check_pool(const vdsa_problem* p, const int32_t* pool) {
+  if (!pool) return fail(VDSA_ERR_NULL, "pool_hw is NULL");
+  if (pool[0] < 1 || pool[1] < 1) return fail(VDSA_ERR_WINDOW, "pool sizes must be >= 1 (got %d x %d)", pool[0], pool[1]);
+  (void)p;
+  return VDSA_OK;
+}
+
+int64_t pooled_tokens(const vdsa_problem* p, const int32_t* pool) {
+  return (int64_t)p->grid_t * ((p->grid_h + pool[0] - 1) / pool[0]) * ((p->grid_w + pool[1] - 1) / pool[1]);
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t pooled_bytes(const vdsa_problem* p, const int32_t* pool) {
+  return align_up((size_t)p->batch * p->heads * pooled_tokens(p, pool) * p->head_dim * elem_size(p->dtype), 256);
+}
+
+vdsa_status check_lse(const vdsa_problem* p, float* lse, uintptr_t& lo, uintptr_t& hi) {
+  lo = hi = 0;
+  if (!lse) return VDSA_OK;
+  if ((uintptr_t)lse % 4 != 0) return fail(VDSA_ERR_ALIGN, "lse pointer is not 4-byte aligned");
+  lo = (uintptr_t)lse;
+  hi = lo + (uintptr_t)((int64_t)p->batch * p->heads * n_tokens(p) * 4);
+  return VDSA_OK;
+}
+
+vdsa::PoolParams pool_params(const vdsa_problem* p, const int32_t* pool, const void* x, const vdsa_strides* xs,
+                             void* y, const vdsa_strides* ys) {
+  vdsa::PoolParams pp{};
+  pp.x = x;
+  pp.y = y;
+  pp.x_sb = xs->b; pp.x_sh = xs->h; pp.x_sn = xs->n;
+  pp.y_sb = ys->b; pp.y_sh = ys->h; pp.y_sn = ys->n;
+  pp.batch = p->batch;
+  pp.heads = p->heads;
+  pp.head_dim = p->head_dim;
+  pp.T = p->grid_t; pp.H = p->grid_h; pp.W = p->grid_w;
+  pp.kh = pool[0]; pp.kw = pool[1];
+  pp.Hp = (p->grid_h + pool[0] - 1) / pool[0];
+  pp.Wp = (p->grid_w + pool[1] - 1) / pool[1];
+  return pp;
+}
+
+}  // namespace
+
+extern "C" {
+
+int vdsa_abi_version(void) { return VDSA_ABI_VERSION; }
+
+const char* vdsa_status_string(vdsa_status s) {
+  switch (s) {
+    case VDSA_OK: return "ok";
+    case VDSA_ERR_NULL: return "null pointer";
+    case VDSA_ERR_SHAPE: return "invalid shape";
+    case VDSA_ERR_WINDOW: return "invalid tile, window, shift or pool";
+    case VDSA_ERR_UNSUPPORTED: return "unsupported head_dim, dtype or scale";
+    case VDSA_ERR_ALIGN: return "misaligned pointer or stride";
+    case VDSA_ERR_ALIAS: return "output overlaps an input";
+    case VDSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case VDSA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* vdsa_last_error(void) { return g_last_error.c_str(); }
+
+vdsa_status sta_attn_fwd(const vdsa_problem* prob, const vdsa_sta_cfg* cfg, const void* q,
+                         const vdsa_strides* q_strides, const void* k, const vdsa_strides* k_strides,
+                         const void* v, const vdsa_strides* v_strides, void* o,
+                         const vdsa_strides* o_strides, float* lse, void* stream) {
+  vdsa_status s;
+  if ((s = check_problem(prob)) != VDSA_OK) return s;
+  if ((s = check_sta_cfg(cfg)) != VDSA_OK) return s;
+  const int64_t N = n_tokens(prob);
+  View vq{"q", q, q_strides, N}, vk{"k", k, k_strides, N}, vv{"v", v, v_strides, N}, vo{"o", o, o_strides, N};
+  if ((s = check_view(prob, vq, false)) != VDSA_OK) return s;
+  if ((s = check_view(prob, vk, false)) != VDSA_OK) return s;
+  if ((s = check_view(prob, vv, false)) != VDSA_OK) return s;
+  if ((s = check_view(prob, vo, true)) != VDSA_OK) return s;
+  uintptr_t l0, l1;
+  if ((s = check_lse(prob, lse, l0, l1)) != VDSA_OK) return s;
+  for (const View* in : {&vq, &vk, &vv})
+    if (overlaps(vo.lo, vo.hi, in->lo, in->hi)) return fail(VDSA_ERR_ALIAS, "o overlaps %s", in->name);
+  if (lse) {
+    for (const View* in : {&vq, &vk, &vv, &vo})
+      if (overlaps(l0, l1, in->lo, in->hi)) return fail(VDSA_ERR_ALIAS, "lse overlaps %s", in->name);
+  }
+
+  vdsa::BoxAttnParams bp{};
+  set_qkvo(bp, vq, vk, vv, vo);
+  bp.lse = lse;
+  bp.batch = prob->batch;
+  bp.heads = prob->heads;
+  bp.qT = prob->grid_t; bp.qH = prob->grid_h; bp.qW = prob->grid_w;
+  bp.bT = cfg->tile[0]; bp.bH = cfg->tile[1]; bp.bW = cfg->tile[2];
+  bp.sT = cfg->shift[0]; bp.sH = cfg->shift[1]; bp.sW = cfg->shift[2];
+  bp.nT = tiles_along(bp.qT, bp.bT, bp.sT);
+  bp.nH = tiles_along(bp.qH, bp.bH, bp.sH);
+  bp.nW = tiles_along(bp.qW, bp.bW, bp.sW);
+  bp.rT = (cfg->window[0] - 1) / 2; bp.rH = (cfg->window[1] - 1) / 2; bp.rW = (cfg->window[2] - 1) / 2;
+  bp.kT = bp.qT; bp.kH = bp.qH; bp.kW = bp.qW;
+  bp.dense_keys = 0;
+  return launch_attn(prob, bp, (hipStream_t)stream);
+}
+
+vdsa_status global_pooled_attn_workspace_size(const vdsa_problem* prob, const int32_t pool_hw[2], size_t* bytes) {
+  vdsa_status s;
+  if ((s = check_problem(prob)) != VDSA_OK) return s;
+  if ((s = check_pool(prob, pool_hw)) != VDSA_OK) return s;
+  if (!bytes) return fail(VDSA_ERR_NULL, "bytes is NULL");
+  *bytes = 2 * pooled_bytes(prob, pool_hw);
+  return ok();
+}
+
+vdsa_status kv_avgpool_fwd(const vdsa_problem* prob, const int32_t pool_hw[2], const void* x,
+                           const vdsa_strides* x_strides, void* x_pooled, const vdsa_strides* pooled_strides,
+                           void* stream) {
+  vdsa_status s;
+  if ((s = check_problem(prob)) != VDSA_OK) return s;
+  if ((s = check_pool(prob, pool_hw)) != VDSA_OK) return s;
+  const int64_t M = pooled_tokens(prob, pool_hw);
+  View vx{"x", x, x_strides, n_tokens(prob)}, vy{"x_pooled", x_pooled, pooled_strides, M};
+  if ((s = check_view(prob, vx, false)) != VDSA_OK) return s;
+  if ((s = check_view(prob, vy, true)) != VDSA_OK) return s;
+  if (overlaps(vx.lo, vx.hi, vy.lo, vy.hi)) return fail(VDSA_ERR_ALIAS, "x_pooled overlaps x");
+  const vdsa::PoolParams pp = pool_params(prob, pool_hw, x, x_strides, x_pooled, pooled_strides);
+  hipError_t e = vdsa::launch_avgpool(pp, prob->dtype == VDSA_BF16, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(VDSA_ERR_HIP, "pooling launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+vdsa_status global_pooled_attn_fwd(const vdsa_problem* prob, const int32_t pool_hw[2], const void* q,
+                                   const vdsa_strides* q_strides, const void* k, const vdsa_strides* k_strides,
+                                   const void* v, const vdsa_strides* v_strides, void* o,
+                                   const vdsa_strides* o_strides, float* lse, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  vdsa_status s;
+  if ((s = check_problem(prob)) != VDSA_OK) return s;
+  if ((s = check_pool(prob, pool_hw)) != VDSA_OK) return s;
+  const int64_t N = n_tokens(prob);
+  const int64_t M = pooled_tokens(prob, pool_hw);
+  View vq{"q", q, q_strides, N}, vk{"k", k, k_strides, N}, vv{"v", v, v_strides, N}, vo{"o", o, o_strides, N};
+  if ((s = check_view(prob, vq, false)) != VDSA_OK) return s;
+  if ((s = check_view(prob, vk, false)) != VDSA_OK) return s;
+  if ((s = check_view(prob, vv, false)) != VDSA_OK) return s;
+  if ((s = check_view(prob, vo, true)) != VDSA_OK) return s;
+  uintptr_t l0, l1;
+  if ((s = check_lse(prob, lse, l0, l1)) != VDSA_OK) return s;
+  const size_t need = 2 * pooled_bytes(prob, pool_hw);
+  if (!workspace) return fail(VDSA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (workspace_bytes < need)
+    return fail(VDSA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  if ((uintptr_t)workspace % 16 != 0) return fail(VDSA_ERR_ALIGN, "workspace is not 16-byte aligned");
+  const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + need;
+  for (const View* in : {&vq, &vk, &vv})
+    if (overlaps(vo.lo, vo.hi, in->lo, in->hi)) return fail(VDSA_ERR_ALIAS, "o overlaps %s", in->name);
+  for (const View* in : {&vq, &vk, &vv, &vo})
+    if (overlaps(w0, w1, in->lo, in->hi)) return fail(VDSA_ERR_ALIAS, "workspace overlaps %s", in->name);
+  if (lse) {
+    for (const View* in : {&vq, &vk, &vv, &vo})
+      if (overlaps(l0, l1, in->lo, in->hi)) return fail(VDSA_ERR_ALIAS, "lse overlaps %s", in->name);
+    if (overlaps(l0, l1, w0, w1)) return fail(VDSA_ERR_ALIAS, "lse overlaps workspace");
+  }
+
+  // pooled K then pooled V, each [batch, heads, M, head_dim] contiguous
+  const size_t half = pooled_bytes(prob, pool_hw);
+  void* kp = workspace;
+  void* vp = (char*)workspace + half;
+  vdsa_strides ps{(int64_t)prob->heads * M * prob->head_dim, M * prob->head_dim, prob->head_dim};
+  hipError_t e = vdsa::launch_avgpool(pool_params(prob, pool_hw, k, k_strides, kp, &ps), prob->dtype == VDSA_BF16,
+                                      (hipStream_t)stream);
+  if (e == hipSuccess)
+    e = vdsa::launch_avgpool(pool_params(prob, pool_hw, v, v_strides, vp, &ps), prob->dtype == VDSA_BF16,
+                             (hipStream_t)stream);
+  if (e != hipSuccess) return fail(VDSA_ERR_HIP, "pooling launch failed: %s", hipGetErrorString(e));
+
+  vdsa::BoxAttnParams bp{};
+  View vkp{"k_pooled", kp, &ps, M}, vvp{"v_pooled", vp, &ps, M};
+  set_qkvo(bp, vq, vkp, vvp, vo);
+  bp.lse = lse;
+  bp.batch = prob->batch;
+  bp.heads = prob->heads;
+  bp.qT = prob->grid_t; bp.qH = prob->grid_h; bp.qW = prob->grid_w;
+  // one query tile covering the whole grid; every query sees every pooled key
+  bp.bT = bp.qT; bp.bH = bp.qH; bp.bW = bp.qW;
+  bp.sT = bp.sH = bp.sW = 0;
+  bp.nT = bp.nH = bp.nW = 1;
+  bp.rT = bp.rH = bp.rW = 0;
+  bp.kT = prob->grid_t;
+  bp.kH = (prob->grid_h + pool_hw[0] - 1) / pool_hw[0];
+  bp.kW = (prob->grid_w + pool_hw[1] - 1) / pool_hw[1];
+  bp.dense_keys = 1;
+  return launch_attn(prob, bp, (hipStream_t)stream);
+}
+
+vdsa_status dual_branch_merge(const vdsa_problem* prob, const void* o_local, const vdsa_strides* local_strides,
+                              const void* o_global, const vdsa_strides* global_strides, const float* w_local,
+                              const float* w_global, void* out, const vdsa_strides* out_strides, void* stream) {
+  vdsa_status s;
+  if ((s = check_problem(prob)) != VDSA_OK) return s;
+  const int64_t N = n_tokens(prob);
+  View va{"o_local", o_local, local_strides, N}, vg{"o_global", o_global, global_strides, N},
+      vo{"out", out, out_strides, N};
+  if ((s = check_view(prob, va, false)) != VDSA_OK) return s;
+  if ((s = check_view(prob, vg, false)) != VDSA_OK) return s;
+  if ((s = check_view(prob, vo, true)) != VDSA_OK) return s;
+  if (!w_global) return fail(VDSA_ERR_NULL, "w_global is NULL");
+  if ((uintptr_t)w_global % 4 != 0 || (w_local && (uintptr_t)w_local % 4 != 0))
+    return fail(VDSA_ERR_ALIGN, "gate pointers must be 4-byte aligned");
+  const bool in_place = out == o_local && out_strides->b == local_strides->b && out_strides->h == local_strides->h &&
+                        out_strides->n == local_strides->n;
+  if (!in_place && overlaps(vo.lo, vo.hi, va.lo, va.hi)) return fail(VDSA_ERR_ALIAS, "out overlaps o_local");
+  if (overlaps(vo.lo, vo.hi, vg.lo, vg.hi)) return fail(VDSA_ERR_ALIAS, "out overlaps o_global");
+  const uintptr_t g0 = (uintptr_t)w_global, g1 = g0 + 4 * (uintptr_t)prob->heads;
+  if (overlaps(vo.lo, vo.hi, g0, g1)) return fail(VDSA_ERR_ALIAS, "out overlaps w_global");
+  if (w_local) {
+    const uintptr_t a0 = (uintptr_t)w_local, a1 = a0 + 4 * (uintptr_t)prob->heads;
+    if (overlaps(vo.lo, vo.hi, a0, a1)) return fail(VDSA_ERR_ALIAS, "out overlaps w_local");
+  }
+  vdsa::MergeParams mp{};
+  mp.a = o_local;
+  mp.g = o_global;
+  mp.w_a = w_local;
+  mp.w_g = w_global;
+  mp.out = out;
+  mp.a_sb = local_strides->b; mp.a_sh = local_strides->h; mp.a_sn = local_strides->n;
+  mp.g_sb = global_strides->b; mp.g_sh = global_strides->h; mp.g_sn = global_strides->n;
+  mp.o_sb = out_strides->b; mp.o_sh = out_strides->h; mp.o_sn = out_strides->n;
+  mp.batch = prob->batch;
+  mp.heads = prob->heads;
+  mp.head_dim = prob->head_dim;
+  mp.n_tokens = N;
+  hipError_t e = vdsa::launch_merge(mp, prob->dtype == VDSA_BF16, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(VDSA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+vdsa_status vdsa_sta_flops(const vdsa_problem* prob, const vdsa_sta_cfg* cfg, double* flops) {
+  vdsa_status s;
+  if ((s = check_problem(prob)) != VDSA_OK) return s;
+  if ((s = check_sta_cfg(cfg)) != VDSA_OK) return s;
+  if (!flops) return fail(VDSA_ERR_NULL, "flops is NULL");
+  // The window mask is a product over dims and tile sizes factorise, so the
+  // attended-pair count is the product of per-dim counts
+  //   sum_a size(a) * sum_{|c-a| <= r} size(c).
+  const int L[3] = {prob->grid_t, prob->grid_h, prob->grid_w};
+  double pairs = 1.0;
+  for (int d = 0; d < 3; ++d) {
+    const int b = cfg->tile[d], sh = cfg->shift[d], r = (cfg->window[d] - 1) / 2;
+    const int n = tiles_along(L[d], b, sh);
+    auto size = [&](int i) { return std::min(L[d], (i + 1) * b - sh) - std::max(0, i * b - sh); };
+    double acc = 0.0;
+    for (int a = 0; a < n; ++a) {
+      double keys = 0.0;
+      for (int c = std::max(0, a - r); c <= std::min(n - 1, a + r); ++c) keys += size(c);
+      acc += size(a) * keys;
+    }
+    pairs *= acc;
+  }
+  *flops = 4.0 * prob->head_dim * prob->batch * prob->heads * pairs;
+  return ok();
+}
+
+vdsa_status vdsa_global_flops(const vdsa_problem* prob, const int32_t pool_hw[2], double* flops) {
+  vdsa_status s;
+  if ((s = check_problem(prob)) != VDSA_OK) return s;
+  if ((s = check_pool(prob, pool_hw)) != VDSA_OK) return s;
+  if (!flops) return fail(VDSA_ERR_NULL, "flops is NULL");
+  *flops = 4.0 * prob->head_dim * prob->batch * prob->heads * (double)n_tokens(prob) *
+           (double)pooled_tokens(prob, pool_hw);
+  return ok();
+}
+
+}  // extern "C"

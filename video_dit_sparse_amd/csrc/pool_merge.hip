@@ -1,0 +1,148 @@
+// Memory-bound helpers of the global-local path:
+//  * frame-wise k_h x k_w average pooling of K or V (UltraGen, arXiv
+//    2510.18775, summary section 4.2: compression with stride k inside each
+//    frame before global attention; here the stride-k depthwise convolution
+//    with uniform weights, i.e. the cell mean);
+//  * the per-head gated merge of the local and global outputs (UltraGen
+//    summary section 4.1: a fusion factor combines the two branches).
+//
+// Both kernels move 16-byte chunks: one thread per (row, chunk), so 16
+// (bf16, head_dim 128) consecutive threads cover one 256-byte row and a wave
+// reads whole rows; accumulation is in fp32.
+#include "internal.h"
+
+namespace vdsa {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int NTHREADS = 256;
+
+template <bool BF16>
+struct Chunk;
+
+template <>
+struct Chunk<true> {
+  static constexpr int E = 8;
+  static __device__ __forceinline__ void unpack(const u32x4& u, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(u[i] << 16);
+      f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ u32x4 pack(const float* f) {
+    bf16x8 b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b[i] = (__bf16)f[i];
+    return __builtin_bit_cast(u32x4, b);
+  }
+};
+
+template <>
+struct Chunk<false> {
+  static constexpr int E = 4;
+  static __device__ __forceinline__ void unpack(const u32x4& u, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(u[i]);
+  }
+  static __device__ __forceinline__ u32x4 pack(const float* f) {
+    u32x4 u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = __float_as_uint(f[i]);
+    return u;
+  }
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(NTHREADS) void avgpool_kernel(const PoolParams p) {
+  using C = Chunk<BF16>;
+  const int cpr = p.head_dim / C::E;  // chunks per row
+  const int M = p.T * p.Hp * p.Wp;
+  const int64_t total = (int64_t)p.batch * p.heads * M * cpr;
+  const size_t esz = BF16 ? 2 : 4;
+  for (int64_t idx = (int64_t)blockIdx.x * NTHREADS + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * NTHREADS) {
+    const int ch = (int)(idx % cpr);
+    const int64_t row = idx / cpr;
+    const int m = (int)(row % M);
+    const int bh = (int)(row / M);
+    const int h = bh % p.heads, b = bh / p.heads;
+    const int j = m % p.Wp, i = (m / p.Wp) % p.Hp, t = m / (p.Wp * p.Hp);
+    const int h0 = i * p.kh, h1 = min(p.H, h0 + p.kh);
+    const int w0 = j * p.kw, w1 = min(p.W, w0 + p.kw);
+    const char* xb = (const char*)p.x + (b * p.x_sb + h * p.x_sh) * esz + ch * 16;
+    float acc[C::E];
+#pragma unroll
+    for (int e = 0; e < C::E; ++e) acc[e] = 0.f;
+    for (int hh = h0; hh < h1; ++hh) {
+      for (int ww = w0; ww < w1; ++ww) {
+        const int64_t tok = ((int64_t)t * p.H + hh) * p.W + ww;
+        float f[C::E];
+        C::unpack(*(const u32x4*)(xb + tok * p.x_sn * esz), f);
+#pragma unroll
+        for (int e = 0; e < C::E; ++e) acc[e] += f[e];
+      }
+    }
+    const float inv = 1.f / (float)((h1 - h0) * (w1 - w0));
+#pragma unroll
+    for (int e = 0; e < C::E; ++e) acc[e] *= inv;
+    char* yb = (char*)p.y + ((b * p.y_sb + h * p.y_sh) + (int64_t)m * p.y_sn) * esz + ch * 16;
+    *(u32x4*)yb = C::pack(acc);
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(NTHREADS) void merge_kernel(const MergeParams p) {
+  using C = Chunk<BF16>;
+  const int cpr = p.head_dim / C::E;
+  const int64_t total = (int64_t)p.batch * p.heads * p.n_tokens * cpr;
+  const size_t esz = BF16 ? 2 : 4;
+  for (int64_t idx = (int64_t)blockIdx.x * NTHREADS + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * NTHREADS) {
+    const int ch = (int)(idx % cpr);
+    const int64_t row = idx / cpr;
+    const int64_t n = row % p.n_tokens;
+    const int bh = (int)(row / p.n_tokens);
+    const int h = bh % p.heads, b = bh / p.heads;
+    const float wa = p.w_a ? p.w_a[h] : 1.f;
+    const float wg = p.w_g[h];
+    float fa[C::E], fg[C::E];
+    C::unpack(*(const u32x4*)((const char*)p.a + (b * p.a_sb + h * p.a_sh + n * p.a_sn) * esz + ch * 16), fa);
+    C::unpack(*(const u32x4*)((const char*)p.g + (b * p.g_sb + h * p.g_sh + n * p.g_sn) * esz + ch * 16), fg);
+#pragma unroll
+    for (int e = 0; e < C::E; ++e) fa[e] = fmaf(wg, fg[e], wa * fa[e]);
+    *(u32x4*)((char*)p.out + (b * p.o_sb + h * p.o_sh + n * p.o_sn) * esz + ch * 16) = C::pack(fa);
+  }
+}
+
+int grid_for(int64_t work) {
+  int64_t blocks = (work + NTHREADS - 1) / NTHREADS;
+  const int64_t cap = 256 * 8 * 16;  // enough waves to saturate HBM; the loop strides the rest
+  return (int)(blocks < cap ? (blocks > 0 ? blocks : 1) : cap);
+}
+
+}  // namespace
+
+hipError_t launch_avgpool(const PoolParams& p, int bf16, hipStream_t stream) {
+  const int cpr = p.head_dim / (bf16 ? 8 : 4);
+  const int64_t work = (int64_t)p.batch * p.heads * p.T * p.Hp * p.Wp * cpr;
+  if (bf16)
+    hipLaunchKernelGGL(avgpool_kernel<true>, dim3(grid_for(work)), dim3(NTHREADS), 0, stream, p);
+  else
+    hipLaunchKernelGGL(avgpool_kernel<false>, dim3(grid_for(work)), dim3(NTHREADS), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeParams& p, int bf16, hipStream_t stream) {
+  const int cpr = p.head_dim / (bf16 ? 8 : 4);
+  const int64_t work = (int64_t)p.batch * p.heads * p.n_tokens * cpr;
+  if (bf16)
+    hipLaunchKernelGGL(merge_kernel<true>, dim3(grid_for(work)), dim3(NTHREADS), 0, stream, p);
+  else
+    hipLaunchKernelGGL(merge_kernel<false>, dim3(grid_for(work)), dim3(NTHREADS), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace vdsa

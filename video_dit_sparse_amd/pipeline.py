@@ -1,0 +1,56 @@
+"""The hot path of one workload as a sequence of library calls.
+
+Local branch: one ``sta_attn_fwd`` per lattice shift (two for the
+cross-window pair: the plain tile lattice, then the half-tile-shifted one, as
+in UltraGen's alternating window partitions, summary section 4.3).  Global
+branch, where the workload has one: ``global_pooled_attn_fwd`` over K/V pooled
+k_h x k_w, then ``dual_branch_merge`` with the per-head gate (w_local = 1).
+Every step runs in libvdsa.so's kernels on the current torch stream.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import torch
+
+from . import _lib as L
+from .workloads import Workload
+
+
+class Buffers:
+    """Outputs and workspace of one workload, allocated once and reused."""
+
+    def __init__(self, w: Workload, q: torch.Tensor):
+        self.local = [torch.empty_like(q, memory_format=torch.contiguous_format) for _ in w.shifts]
+        self.lse = [torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) for _ in w.shifts]
+        self.glob = self.glob_lse = self.merged = self.workspace = None
+        if w.pool_hw is not None:
+            self.glob = torch.empty_like(q, memory_format=torch.contiguous_format)
+            self.glob_lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+            self.merged = torch.empty_like(q, memory_format=torch.contiguous_format)
+            nbytes = L.global_pooled_attn_workspace_size(w.batch, w.heads, w.head_dim, w.grid, w.pool_hw,
+                                                         L.VDSA_BF16 if w.dtype == "bf16" else L.VDSA_F32)
+            self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+
+
+def run(w: Workload, q, k, v, gate: Optional[torch.Tensor], buf: Buffers, with_lse: bool = False) -> Dict:
+    """One pass of the workload's hot path; returns the output tensors."""
+    for i, shift in enumerate(w.shifts):
+        L.sta_attn_fwd(q, k, v, w.grid, w.tile, w.window, shift, scale=w.softmax_scale,
+                       out=buf.local[i], lse=buf.lse[i] if with_lse else None)
+    out = {"local": buf.local, "lse": buf.lse if with_lse else None}
+    if w.pool_hw is not None:
+        L.global_pooled_attn_fwd(q, k, v, w.grid, w.pool_hw, scale=w.softmax_scale, out=buf.glob,
+                                 lse=buf.glob_lse if with_lse else None, workspace=buf.workspace)
+        L.dual_branch_merge(buf.local[0], buf.glob, gate, out=buf.merged)
+        out.update(glob=buf.glob, glob_lse=buf.glob_lse if with_lse else None, merged=buf.merged,
+                   workspace=buf.workspace)
+    return out
+
+
+def flops(w: Workload) -> Dict[str, float]:
+    """Effective FLOP per step, per branch."""
+    f = {"local": sum(L.sta_flops(w.batch, w.heads, w.head_dim, w.grid, w.tile, w.window, s) for s in w.shifts)}
+    if w.pool_hw is not None:
+        f["global"] = L.global_flops(w.batch, w.heads, w.head_dim, w.grid, w.pool_hw)
+    return f
