@@ -13,7 +13,7 @@
 //
 // Per 64-key block and wave (32 queries):
 //   S^T = K Q^T      (keys x queries; K from LDS, Q^T resident in registers)
-//   online softmax   (fp32, exp2 with scale*log2(e) folded into one FMA;
+//   online softmax   (fp32, v_exp_f32 with scale*log2(e) folded into one FMA;
 //                     row statistics live in one lane pair, so the only
 //                     cross-lane step is one exchange with lane ^ 32)
 //   O^T += V^T P^T   (P^T taken straight from the S^T accumulators)
@@ -23,6 +23,19 @@
 // Key order inside a 32-key MFMA block is permuted (bits 2 and 3 of the row
 // index swapped) so that the eight P values a lane holds per 16-key chunk are
 // eight consecutive keys; the V^T operand is then one 16-byte LDS read.
+//
+// Data movement per block (double-buffered LDS, one barrier per block):
+//   K  : global -> LDS directly (global_load_lds_dwordx4, no registers), into
+//        "k-planes": plane ks holds head_dim elements [16ks, 16ks+16) of all
+//        64 keys, 32 bytes per key.  Each S^T operand read is then one
+//        contiguous 1 KB per wave.
+//   V  : global -> registers -> LDS transposed ("v-planes": plane kc holds
+//        keys [16kc, 16kc+16) of every head_dim row, 32 bytes per row, rows
+//        XOR-swizzled by kc).  The lane mapping and the swizzle make the
+//        transposing 8-byte stores free of bank conflicts; each V^T operand
+//        read is one contiguous 1 KB per wave.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace vdsa {
@@ -33,10 +46,13 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BLOCK_M = 128;   // queries per workgroup
 constexpr int BLOCK_N = 64;    // keys per iteration
 constexpr int NTHREADS = 256;  // 4 waves of 64
+// s_waitcnt with vmcnt = 0 and expcnt / lgkmcnt left at their maxima
+constexpr int WAIT_VMCNT0 = 0x0F70;
 
 __device__ __forceinline__ int swap_bits23(int i) {
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
@@ -88,14 +104,18 @@ __device__ __forceinline__ void tile_boxes(const BoxAttnParams& p, int tile, Box
 
 template <int HD>
 __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAttnParams p) {
-  constexpr int NCH = HD / 8;          // 16-byte chunks per row
-  constexpr int KSTEPS = HD / 16;      // MFMA steps over head_dim
-  constexpr int NB = HD / 32;          // 32-row blocks of O^T
-  constexpr int RPT = HD / 32;         // key rows loaded per thread (NCH * 64 / 256)
-  static_assert(NCH * BLOCK_N == NTHREADS * RPT, "load mapping");
+  constexpr int KSTEPS = HD / 16;          // MFMA steps over head_dim = k-planes
+  constexpr int NB = HD / 32;              // 32-row blocks of O^T
+  constexpr int RPT = HD / 32;             // V key rows loaded per thread
+  constexpr int NLR = BLOCK_N / RPT;       // threads sharing one V chunk column
+  constexpr int KPLANE = BLOCK_N * 32;     // bytes
+  constexpr int VPLANE = HD * 32;          // bytes
+  constexpr int K_STAGE = KSTEPS * KPLANE;
+  constexpr int STAGE = K_STAGE + 4 * VPLANE;
+  constexpr int DMA_PER_WAVE = KSTEPS * 2 / 4;  // 1 KB K-plane segments per wave
+  static_assert(NLR * (HD / 8) == NTHREADS, "V load mapping");
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][BLOCK_N * HD];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_vt[2][HD * BLOCK_N];
+  __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -121,15 +141,17 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
   const int kvol = kb.et * kb.eh * kb.ew;
   const int nkb = (kvol + BLOCK_N - 1) / BLOCK_N;
 
-  const uint16_t* __restrict__ qp = (const uint16_t*)p.q + b * p.q_sb + h * p.q_sh;
-  const uint16_t* __restrict__ kp = (const uint16_t*)p.k + b * p.k_sb + h * p.k_sh;
-  const uint16_t* __restrict__ vp = (const uint16_t*)p.v + b * p.v_sb + h * p.v_sh;
-  uint16_t* __restrict__ op = (uint16_t*)p.o + b * p.o_sb + h * p.o_sh;
+  const char* __restrict__ qp = (const char*)p.q + 2 * (b * p.q_sb + h * p.q_sh);
+  const char* __restrict__ kp = (const char*)p.k + 2 * (b * p.k_sb + h * p.k_sh);
+  const char* __restrict__ vp = (const char*)p.v + 2 * (b * p.v_sb + h * p.v_sh);
+  char* __restrict__ op = (char*)p.o + 2 * (b * p.o_sb + h * p.o_sh);
+  const uint32_t q_row = 2u * (uint32_t)p.q_sn, k_row = 2u * (uint32_t)p.k_sn;
+  const uint32_t v_row = 2u * (uint32_t)p.v_sn, o_row = 2u * (uint32_t)p.o_sn;
 
   // ---- this lane's query (MFMA column l32 of wave `wave`)
   const int jq = q0 + wave * 32 + l32;
   const bool q_valid = jq < qvol;
-  int qtok;
+  uint32_t qtok;
   {
     const int j = min(jq, qvol - 1);
     const int plane = qb.eh * qb.ew;
@@ -137,21 +159,20 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
     const int r = j - jt * plane;
     const int jh = r / qb.ew;
     const int jw = r - jh * qb.ew;
-    qtok = ((qb.t0 + jt) * p.qH + qb.h0 + jh) * p.qW + qb.w0 + jw;
+    qtok = (uint32_t)(((qb.t0 + jt) * p.qH + qb.h0 + jh) * p.qW + qb.w0 + jw);
   }
   bf16x8 qf[KSTEPS];
   {
-    const uint16_t* src = qp + (uint32_t)qtok * (uint32_t)p.q_sn + 8 * g;
+    const char* src = qp + qtok * q_row + 16 * g;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
-      qf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + 16 * ks));
+    for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + 32 * ks));
   }
 
   // ---- key box addressing: key j -> token, via two divisions by invariants
   const FastDiv fd_plane = make_fastdiv((uint32_t)(kb.eh * kb.ew));
   const FastDiv fd_row = make_fastdiv((uint32_t)kb.ew);
   auto key_token = [&](int j) -> uint32_t {
-    j = min(j, kvol - 1);
+    j = min(j, kvol - 1);   // keys past the box repeat the last key; masked later
     const uint32_t jt = fast_div((uint32_t)j, fd_plane);
     const uint32_t r = (uint32_t)j - jt * fd_plane.d;
     const uint32_t jh = fast_div(r, fd_row);
@@ -159,47 +180,53 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
     return ((kb.t0 + jt) * p.kH + kb.h0 + jh) * p.kW + kb.w0 + jw;
   };
 
-  // Load mapping: thread owns chunk `lc` (8 head_dim elements) of key rows
-  // RPT*lr .. RPT*lr+RPT-1 of the block.
-  const int lc = tid % NCH;
-  const int lr = tid / NCH;
-  u32x4 kreg[RPT], vreg[RPT];
-  auto load_block = [&](int blk) {
+  // V mapping: thread owns 16-byte chunk vc (head_dim [8vc, 8vc+8)) of keys
+  // RPT*vr .. RPT*vr+RPT-1.
+  const int vr = tid % NLR;
+  const int vc = tid / NLR;
+  u32x4 vreg[RPT];
+
+  // Issue the global reads of block `blk` into LDS stage `stage` (K) and
+  // registers (V).
+  auto load_block = [&](int blk, int stage) {
     const uint32_t my_tok = key_token(blk * BLOCK_N + lane);
+    char* kst = lds + stage * STAGE;
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+      const int seg = i & 1;                          // key rows [32seg, 32seg+32)
+      const int plane = wave * (DMA_PER_WAVE / 2) + (i >> 1);
+      const uint32_t tok = (uint32_t)__shfl((int)my_tok, 32 * seg + (lane >> 1), 64);
+      const char* src = kp + tok * k_row + (2 * plane + (lane & 1)) * 16;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(kst + plane * KPLANE + seg * 1024), 16, 0, 0);
+    }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const uint32_t tok = (uint32_t)__shfl((int)my_tok, RPT * lr + i, 64);
-      kreg[i] = *(const u32x4*)(kp + tok * (uint32_t)p.k_sn + 8 * lc);
-      vreg[i] = *(const u32x4*)(vp + tok * (uint32_t)p.v_sn + 8 * lc);
+      const uint32_t tok = (uint32_t)__shfl((int)my_tok, RPT * vr + i, 64);
+      vreg[i] = *(const u32x4*)(vp + tok * v_row + vc * 16);
     }
   };
-  auto store_block = [&](int stage) {
-    uint16_t* kd = lds_k[stage];
-    uint16_t* vd = lds_vt[stage];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int row = RPT * lr + i;
-      *(u32x4*)(kd + row * HD + ((lc ^ (row & (NCH - 1))) * 8)) = kreg[i];
-    }
-    // V^T: element (d, key) with d = 8*lc + e; this thread's RPT keys are
-    // consecutive, so each d gets one RPT*2-byte store.
-    const int key0 = RPT * lr;
-    const int kchunk = key0 >> 3, kin = key0 & 7;
+  // Transpose the V registers into the v-planes of `stage`:
+  // byte offset of (key k, row d) = (k>>4)*VPLANE + ((d ^ (k>>4))*32) + ((k>>3)&1)*16 + (k&7)*2.
+  auto store_v = [&](int stage) {
+    char* vst = lds + stage * STAGE + K_STAGE;
+    const int k0 = RPT * vr;
+    const int kc = k0 >> 4;
+    const int within = ((k0 >> 3) & 1) * 16 + (k0 & 7) * 2;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int d = 8 * lc + e;
+      const int d = 8 * vc + e;
       const int w = e >> 1, hi = e & 1;
-      uint16_t vals[RPT];
+      uint32_t vals[RPT];
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) vals[i] = (uint16_t)(hi ? (vreg[i][w] >> 16) : (vreg[i][w] & 0xffffu));
-      uint16_t* dst = vd + d * BLOCK_N + ((kchunk ^ (d & 7)) * 8) + kin;
+      for (int i = 0; i < RPT; ++i) vals[i] = hi ? (vreg[i][w] >> 16) : (vreg[i][w] & 0xffffu);
+      char* dst = vst + kc * VPLANE + ((d ^ kc) * 32) + within;
       if constexpr (RPT == 4) {
         u32x2 pk;
-        pk[0] = (uint32_t)vals[0] | ((uint32_t)vals[1] << 16);
-        pk[1] = (uint32_t)vals[2] | ((uint32_t)vals[3] << 16);
+        pk[0] = vals[0] | (vals[1] << 16);
+        pk[1] = vals[2] | (vals[3] << 16);
         *(u32x2*)dst = pk;
       } else {
-        *(uint32_t*)dst = (uint32_t)vals[0] | ((uint32_t)vals[1] << 16);
+        *(uint32_t*)dst = vals[0] | (vals[1] << 16);
       }
     }
   };
@@ -211,43 +238,41 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
   float l_run = 0.f;         // this lane's share of the running denominator
   const float c = p.scale_log2e;
 
-  load_block(0);
-  store_block(0);
+  load_block(0, 0);
+  store_v(0);
+  __builtin_amdgcn_s_waitcnt(WAIT_VMCNT0);
   __syncthreads();
 
-  const int krow_a = swap_bits23(l32);   // key row this lane feeds to the S^T MFMA
+  const int k_rd = (swap_bits23(l32)) * 32 + g * 16;   // this lane's S^T operand row/half
+  int v_rd[4];                                          // this lane's V^T operand per kc
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) v_rd[kc] = kc * VPLANE + ((l32 ^ kc) * 32) + g * 16;
 
-  for (int blk = 0; blk < nkb; ++blk) {
+  // One 64-key block.  Only the last block of the box can hold keys past its
+  // end; it is the only one that runs the masking code.
+  auto process = [&](int blk, auto partial_tag) {
+    constexpr bool PARTIAL = decltype(partial_tag)::value;
     const int stage = blk & 1;
     const bool more = blk + 1 < nkb;
-    if (more) load_block(blk + 1);
+    if (more) load_block(blk + 1, stage ^ 1);
 
     // S^T = K Q^T for two 32-key halves
-    const uint16_t* kd = lds_k[stage];
+    const char* kst = lds + stage * STAGE;
     f32x16 s[2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       s[sb] = f32x16{};
-      const int row = sb * 32 + krow_a;
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int ch = 2 * ks + g;
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(kd + row * HD + ((ch ^ (row & (NCH - 1))) * 8)));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(kst + ks * KPLANE + sb * 1024 + k_rd));
         s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[sb], 0, 0, 0);
       }
     }
 
     // online softmax over this block's keys (register v of half sb holds key
-    // 32*sb + 16*(v/8) + 8*g + v%8)
-    const bool partial = (blk + 1) * BLOCK_N > kvol;
-    if (partial) {
-      const int kbase = blk * BLOCK_N + 8 * g;
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (kbase + 32 * sb + 16 * (v >> 3) + (v & 7) >= kvol) s[sb][v] = -INFINITY;
-    }
+    // 32*sb + 16*(v/8) + 8*g + v%8 of the block).  Keys past the box end are
+    // copies of the box's last key, so they may take part in the max; their
+    // probabilities are zeroed.
     float mx = s[0][0];
 #pragma unroll
     for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[0][v]);
@@ -256,12 +281,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m_run, mx * c);
     if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {   // rescale only when some max grew
-      const float corr = exp2f(m_run - m_new);
+      const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= corr;
 #pragma unroll
       for (int i = 0; i < NB; ++i) oacc[i] *= corr;
     }
     m_run = m_new;
+    const int nvalid = PARTIAL ? kvol - blk * BLOCK_N : BLOCK_N;
     bf16x8 pf[4];
     float lsum = 0.f;
 #pragma unroll
@@ -271,8 +297,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
         bf16x8 pk;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          float pv = exp2f(fmaf(s[sb][8 * hlf + e], c, -m_new));
-          if (partial && s[sb][8 * hlf + e] == -INFINITY) pv = 0.f;
+          // v_exp_f32 directly: arguments are <= 0, results in [0, 1]
+          float pv = __builtin_amdgcn_exp2f(fmaf(s[sb][8 * hlf + e], c, -m_new));
+          if constexpr (PARTIAL) {
+            if (32 * sb + 16 * hlf + 8 * g + e >= nvalid) pv = 0.f;
+          }
           lsum += pv;
           pk[e] = (__bf16)pv;
         }
@@ -282,28 +311,32 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
     l_run += lsum;
 
     // O^T += V^T P^T
-    const uint16_t* vd = lds_vt[stage];
+    const char* vst = lds + stage * STAGE + K_STAGE;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
-      const int ch = 2 * kc + g;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int d = 32 * nb + l32;
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(vd + d * BLOCK_N + ((ch ^ (d & 7)) * 8)));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(vst + v_rd[kc] + nb * 1024));
         oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kc], oacc[nb], 0, 0, 0);
       }
     }
 
-    if (more) store_block(stage ^ 1);
+    if (more) store_v(stage ^ 1);
+    __builtin_amdgcn_s_waitcnt(WAIT_VMCNT0);   // K of the next block has landed in LDS
     __syncthreads();
-  }
+  };
+
+  const bool last_partial = kvol % BLOCK_N != 0;
+  const int nfull = last_partial ? nkb - 1 : nkb;
+  for (int blk = 0; blk < nfull; ++blk) process(blk, std::false_type{});
+  if (last_partial) process(nkb - 1, std::true_type{});
 
   // ---- epilogue: normalise and store (lane owns query l32; register v of
   // block nb holds head_dim index 32*nb + 8*(v/4) + 4*g + v%4)
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.f / l_tot;
   if (q_valid) {
-    uint16_t* dst = op + (uint32_t)qtok * (uint32_t)p.o_sn + 4 * g;
+    char* dst = op + qtok * o_row + 8 * g;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -311,11 +344,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
         bf16x4 ov;
 #pragma unroll
         for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(oacc[nb][4 * r4 + e] * inv);
-        *(u32x2*)(dst + 32 * nb + 8 * r4) = __builtin_bit_cast(u32x2, ov);
+        *(u32x2*)(dst + 64 * nb + 16 * r4) = __builtin_bit_cast(u32x2, ov);
       }
     if (p.lse != nullptr && g == 0) {
       const int64_t N = (int64_t)p.qT * p.qH * p.qW;
-      p.lse[((int64_t)b * p.heads + h) * N + qtok] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
+      p.lse[((int64_t)b * p.heads + h) * N + qtok] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
     }
   }
 }
