@@ -27,8 +27,8 @@
  *     fp32 accumulation and fp32 softmax.  VDSA_F32: fp32 throughout.
  *   - Alignment: every tensor pointer 16-byte aligned; every batch, head and
  *     token stride times the element size a multiple of 16 bytes.
- *   - Size limit: within one (batch, head), the largest element offset
- *     ((N-1)*stride_n + head_dim) must be below 2^32.
+ *   - Size limit: within one (batch, head), the largest byte offset
+ *     ((N-1)*stride_n + head_dim) * element size must be below 2^32.
  */
 #ifndef VDSA_H
 #define VDSA_H

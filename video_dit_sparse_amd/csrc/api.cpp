@@ -84,9 +84,10 @@ vdsa_status check_view(const vdsa_problem* p, View& v, bool is_output) {
                   (long long)str[d], es);
     max_off += (ext[d] - 1) * str[d];
   }
-  const int64_t row_span = (v.rows - 1) * (v.rows > 1 ? str[2] : 0) + p->head_dim;
+  // kernels address one (batch, head) slice with 32-bit byte offsets
+  const int64_t row_span = ((v.rows - 1) * (v.rows > 1 ? str[2] : 0) + p->head_dim) * (int64_t)es;
   if (row_span >= (int64_t(1) << 32))
-    return fail(VDSA_ERR_SHAPE, "%s: token offsets within one head reach %lld elements (limit 2^32)", v.name,
+    return fail(VDSA_ERR_SHAPE, "%s: token offsets within one head reach %lld bytes (limit 2^32)", v.name,
                 (long long)row_span);
   if (is_output) {
     // rows of the output must not overlap each other: sort the used dims by

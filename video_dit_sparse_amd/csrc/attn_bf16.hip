@@ -25,15 +25,18 @@
 // eight consecutive keys; the V^T operand is then one 16-byte LDS read.
 //
 // Data movement per block (double-buffered LDS, one barrier per block):
-//   K  : global -> LDS directly (global_load_lds_dwordx4, no registers), into
-//        "k-planes": plane ks holds head_dim elements [16ks, 16ks+16) of all
-//        64 keys, 32 bytes per key.  Each S^T operand read is then one
-//        contiguous 1 KB per wave.
+//   K  : global -> LDS directly (buffer_load_dwordx4 ... lds, no registers),
+//        into "k-planes": plane ks holds head_dim elements [16ks, 16ks+16) of
+//        all 64 keys as [32-key half][8-element half][32 keys][16 bytes].
+//        Each S^T operand read is one contiguous 1 KB per wave, and any 16
+//        consecutive lanes read 256 contiguous bytes.
 //   V  : global -> registers -> LDS transposed ("v-planes": plane kc holds
-//        keys [16kc, 16kc+16) of every head_dim row, 32 bytes per row, rows
-//        XOR-swizzled by kc).  The lane mapping and the swizzle make the
-//        transposing 8-byte stores free of bank conflicts; each V^T operand
-//        read is one contiguous 1 KB per wave.
+//        keys [16kc, 16kc+16) of every head_dim row as
+//        [32-row block][8-key half][32 rows][16 bytes], rows XOR-swizzled by
+//        (kc, half)).  The lane mapping and the swizzle make the transposing
+//        stores free of bank conflicts; each V^T operand read is again one
+//        contiguous 1 KB per wave.
+// Global reads use buffer resources (scalar base + 32-bit lane offsets).
 #include <type_traits>
 
 #include "internal.h"
@@ -47,12 +50,15 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
+// raw buffer resource word 3 for gfx9-class parts (32-bit data format)
+constexpr int BUF_FLAGS = 0x00020000;
 
 constexpr int BLOCK_M = 128;   // queries per workgroup
 constexpr int BLOCK_N = 64;    // keys per iteration
 constexpr int NTHREADS = 256;  // 4 waves of 64
 // s_waitcnt with vmcnt = 0 and expcnt / lgkmcnt left at their maxima
 constexpr int WAIT_VMCNT0 = 0x0F70;
+constexpr float RESCALE_MARGIN = 8.f;
 
 __device__ __forceinline__ int swap_bits23(int i) {
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
@@ -119,7 +125,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
@@ -142,8 +148,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
   const int nkb = (kvol + BLOCK_N - 1) / BLOCK_N;
 
   const char* __restrict__ qp = (const char*)p.q + 2 * (b * p.q_sb + h * p.q_sh);
-  const char* __restrict__ kp = (const char*)p.k + 2 * (b * p.k_sb + h * p.k_sh);
-  const char* __restrict__ vp = (const char*)p.v + 2 * (b * p.v_sb + h * p.v_sh);
+  const char* kp = (const char*)p.k + 2 * (b * p.k_sb + h * p.k_sh);
+  const char* vp = (const char*)p.v + 2 * (b * p.v_sb + h * p.v_sh);
+  // the byte range one head's keys can reach: (kT*kH*kW - 1) rows + one row of head_dim
+  const uint32_t krange = ((uint32_t)(p.kT * p.kH * p.kW) - 1u) * 2u * (uint32_t)p.k_sn + 2u * HD;
+  const uint32_t vrange = ((uint32_t)(p.kT * p.kH * p.kW) - 1u) * 2u * (uint32_t)p.v_sn + 2u * HD;
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, (int)krange, BUF_FLAGS);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vp, 0, (int)vrange, BUF_FLAGS);
   char* __restrict__ op = (char*)p.o + 2 * (b * p.o_sb + h * p.o_sh);
   const uint32_t q_row = 2u * (uint32_t)p.q_sn, k_row = 2u * (uint32_t)p.k_sn;
   const uint32_t v_row = 2u * (uint32_t)p.v_sn, o_row = 2u * (uint32_t)p.o_sn;
@@ -190,43 +201,47 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
   // registers (V).
   auto load_block = [&](int blk, int stage) {
     const uint32_t my_tok = key_token(blk * BLOCK_N + lane);
-    char* kst = lds + stage * STAGE;
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i) {
-      const int seg = i & 1;                          // key rows [32seg, 32seg+32)
+      const int sb = i & 1;                           // key rows [32sb, 32sb+32)
       const int plane = wave * (DMA_PER_WAVE / 2) + (i >> 1);
-      const uint32_t tok = (uint32_t)__shfl((int)my_tok, 32 * seg + (lane >> 1), 64);
-      const char* src = kp + tok * k_row + (2 * plane + (lane & 1)) * 16;
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(kst + plane * KPLANE + seg * 1024), 16, 0, 0);
+      // lane L fills key row 32sb + L%32, head_dim half L/32 of the plane
+      const uint32_t tok = (uint32_t)__shfl((int)my_tok, 32 * sb + l32, 64);
+      const uint32_t off = tok * k_row + (uint32_t)(2 * plane + g) * 16u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void*)(lds + stage * STAGE + plane * KPLANE + sb * 1024),
+                                               16, (int)off, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const uint32_t tok = (uint32_t)__shfl((int)my_tok, RPT * vr + i, 64);
-      vreg[i] = *(const u32x4*)(vp + tok * v_row + vc * 16);
+      vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrsrc, (int)(tok * v_row + vc * 16), 0, 0));
     }
   };
-  // Transpose the V registers into the v-planes of `stage`:
-  // byte offset of (key k, row d) = (k>>4)*VPLANE + ((d ^ (k>>4))*32) + ((k>>3)&1)*16 + (k&7)*2.
+  // Transpose the V registers into the v-planes of `stage`: element (key k,
+  // head_dim row d = 32nb + r) sits at byte
+  //   (k>>4)*VPLANE + nb*1024 + ((k>>3)&1)*512 + (r ^ swz)*16 + (k&7)*2,
+  //   swz = (k>>4) | (((k>>3)&1) << 2).
   auto store_v = [&](int stage) {
     char* vst = lds + stage * STAGE + K_STAGE;
     const int k0 = RPT * vr;
-    const int kc = k0 >> 4;
-    const int within = ((k0 >> 3) & 1) * 16 + (k0 & 7) * 2;
+    const int kc = k0 >> 4, half = (k0 >> 3) & 1;
+    const int swz = kc | (half << 2);
+    char* base = vst + kc * VPLANE + half * 512 + (k0 & 7) * 2;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int d = 8 * vc + e;
-      const int w = e >> 1, hi = e & 1;
-      uint32_t vals[RPT];
-#pragma unroll
-      for (int i = 0; i < RPT; ++i) vals[i] = hi ? (vreg[i][w] >> 16) : (vreg[i][w] & 0xffffu);
-      char* dst = vst + kc * VPLANE + ((d ^ kc) * 32) + within;
+      const int w = e >> 1;
+      // v_perm_b32 byte selectors: low halves (0x05040100) or high halves
+      // (0x07060302) of two words packed into one
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      char* dst = base + (d >> 5) * 1024 + (((d & 31) ^ swz) * 16);
       if constexpr (RPT == 4) {
         u32x2 pk;
-        pk[0] = vals[0] | (vals[1] << 16);
-        pk[1] = vals[2] | (vals[3] << 16);
+        pk[0] = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel);
+        pk[1] = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], sel);
         *(u32x2*)dst = pk;
       } else {
-        *(uint32_t*)dst = vals[0] | (vals[1] << 16);
+        *(uint32_t*)dst = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel);
       }
     }
   };
@@ -243,10 +258,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
   __builtin_amdgcn_s_waitcnt(WAIT_VMCNT0);
   __syncthreads();
 
-  const int k_rd = (swap_bits23(l32)) * 32 + g * 16;   // this lane's S^T operand row/half
-  int v_rd[4];                                          // this lane's V^T operand per kc
+  const int k_rd = g * 512 + swap_bits23(l32) * 16;   // this lane's S^T operand (key row, half)
+  int v_rd[4];                                         // this lane's V^T operand per kc
 #pragma unroll
-  for (int kc = 0; kc < 4; ++kc) v_rd[kc] = kc * VPLANE + ((l32 ^ kc) * 32) + g * 16;
+  for (int kc = 0; kc < 4; ++kc) v_rd[kc] = kc * VPLANE + g * 512 + ((l32 ^ (kc | (g << 2))) * 16);
 
   // One 64-key block.  Only the last block of the box can hold keys past its
   // end; it is the only one that runs the masking code.
@@ -278,15 +293,20 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
     for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[0][v]);
 #pragma unroll
     for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[1][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx * c);
-    if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {   // rescale only when some max grew
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+    // Lazy rescale: keep the reference max m_run until some query's block
+    // max exceeds it by more than RESCALE_MARGIN (log2 units).  Until then
+    // probabilities stay below 2^RESCALE_MARGIN, well inside bf16/fp32 range,
+    // and the final normalisation by the same reference is exact.
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + RESCALE_MARGIN)) {
+      const float m_new = fmaxf(m_run, mx);
       const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= corr;
 #pragma unroll
       for (int i = 0; i < NB; ++i) oacc[i] *= corr;
+      m_run = m_new;
     }
-    m_run = m_new;
+    const float m_new = m_run;
     const int nvalid = PARTIAL ? kvol - blk * BLOCK_N : BLOCK_N;
     bf16x8 pf[4];
     float lsum = 0.f;
