@@ -110,6 +110,22 @@ def test_sta_deterministic_and_no_stray_writes():
     compare(o.reshape(4, N, 128).cpu(), ro, "bf16", "batch 2")
 
 
+def test_reference_raise_pass():
+    """Keys late in each key box whose logits jump far above the first keys'
+    seen: the kernel must raise its softmax reference and repeat the walk."""
+    grid, tile, window = (2, 16, 32), (2, 8, 8), (1, 3, 5)
+    N = int(np.prod(grid))
+    q, k, v = [WL.make_tensor((1, 2, N, 128), torch.float32, DEV, seed=31 + i) for i in range(3)]
+    w = torch.arange(N, device=DEV) % grid[2]
+    k[:, :, w >= 20] *= 40.0
+    q, k, v = q.bfloat16(), k.bfloat16(), v.bfloat16()
+    o, lse = V.sta_attn_fwd(q, k, v, grid, tile, window, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle_sta(q, k, v, grid, tile, window, (0, 0, 0), 128 ** -0.5)
+    compare(o[0].cpu(), ro, "bf16", "reference raise")
+    compare(lse[0].cpu(), rl, "bf16", "reference raise lse")
+
+
 def test_heads_permute():
     grid, tile, window = (4, 16, 16), (2, 4, 4), (1, 3, 3)
     N = int(np.prod(grid))
