@@ -49,6 +49,11 @@ SMALL_STA = [
     ("full_window_bf16", (4, 12, 20), (2, 4, 4), (3, 5, 9), (0, 0, 0), 1, 128, "bf16"),
     ("big_tile_bf16", (3, 17, 30), (3, 17, 30), (1, 1, 1), (0, 0, 0), 1, 128, "bf16"),
     ("single_token_grid_bf16", (1, 1, 1), (1, 1, 1), (1, 1, 1), (0, 0, 0), 1, 128, "bf16"),
+    # 384- and 192-token tiles run the 48-queries-per-wave kernel
+    ("tile384_bf16", (12, 16, 24), (6, 8, 8), (1, 3, 3), (0, 0, 0), 2, 128, "bf16"),
+    ("tile384_shift_bf16", (11, 13, 21), (6, 8, 8), (3, 1, 3), (3, 4, 4), 1, 128, "bf16"),
+    ("tile192_bf16", (6, 16, 24), (3, 8, 8), (3, 3, 3), (0, 0, 0), 2, 128, "bf16"),
+    ("tile192_shift_bf16", (7, 12, 20), (3, 8, 8), (1, 3, 1), (1, 4, 4), 1, 128, "bf16"),
 ]
 
 

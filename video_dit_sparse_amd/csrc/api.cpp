@@ -138,18 +138,51 @@ int max_tile_extent(int L, int b, int s) {
   return best;
 }
 
+// bf16 kernel shapes: queries per workgroup and the kernel that runs them.
+struct Bf16Shape {
+  int block_m;
+  int m16_waves;   // 0 = the 128-query 32x32 kernel
+};
+
+// Largest block whose padding wastes at most 1/8 of the launched query slots,
+// else the least padding.
+Bf16Shape choose_bf16_shape(int64_t max_tile_vol, int head_dim) {
+  const Bf16Shape m32{vdsa::box_attn_bf16_block_m(), 0};
+  if (head_dim != 128) return m32;
+  const Bf16Shape shapes[] = {{384, 8}, {192, 4}, m32};
+  Bf16Shape best = m32;
+  double best_waste = 2.0;
+  for (const Bf16Shape& sh : shapes) {
+    const int64_t blocks = (max_tile_vol + sh.block_m - 1) / sh.block_m;
+    const double waste = (double)(blocks * sh.block_m - max_tile_vol) / (double)(blocks * sh.block_m);
+    if (waste <= 0.125) return sh;
+    if (waste < best_waste) {
+      best_waste = waste;
+      best = sh;
+    }
+  }
+  return best;
+}
+
 vdsa_status launch_attn(const vdsa_problem* prob, vdsa::BoxAttnParams& bp, hipStream_t stream) {
-  const int bm = prob->dtype == VDSA_BF16 ? vdsa::box_attn_bf16_block_m() : vdsa::box_attn_f32_block_m();
   const int64_t mv = (int64_t)max_tile_extent(bp.qT, bp.bT, bp.sT) * max_tile_extent(bp.qH, bp.bH, bp.sH) *
                      max_tile_extent(bp.qW, bp.bW, bp.sW);
-  bp.qblocks = (int32_t)((mv + bm - 1) / bm);
+  Bf16Shape shape{vdsa::box_attn_f32_block_m(), 0};
+  if (prob->dtype == VDSA_BF16) shape = choose_bf16_shape(mv, prob->head_dim);
+  bp.qblocks = (int32_t)((mv + shape.block_m - 1) / shape.block_m);
+  bp.variant = shape.m16_waves;
   const int64_t total = (int64_t)bp.batch * bp.heads * bp.nT * bp.nH * bp.nW * bp.qblocks;
-  if (total >= (int64_t(1) << 31) / 256)
+  if (total >= (int64_t(1) << 31) / 512)
     return fail(VDSA_ERR_SHAPE, "problem needs %lld workgroups, beyond the launch limit", (long long)total);
   bp.total_wg = (int32_t)total;
   bp.scale_log2e = prob->scale * 1.4426950408889634f;
-  hipError_t e = prob->dtype == VDSA_BF16 ? vdsa::launch_box_attn_bf16(bp, prob->head_dim, stream)
-                                          : vdsa::launch_box_attn_f32(bp, prob->head_dim, stream);
+  hipError_t e;
+  if (prob->dtype == VDSA_F32)
+    e = vdsa::launch_box_attn_f32(bp, prob->head_dim, stream);
+  else if (shape.m16_waves != 0)
+    e = vdsa::launch_box_attn_bf16_m16(bp, shape.m16_waves, stream);
+  else
+    e = vdsa::launch_box_attn_bf16(bp, prob->head_dim, stream);
   if (e != hipSuccess) return fail(VDSA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -1,0 +1,333 @@
+// Tile-window ("box") attention forward for head_dim 128, bf16 in/out, fp32
+// accumulation, on 16x16x32 matrix-core products (v_mfma_f32_16x16x32_bf16),
+// with 48 queries per wave.
+//
+// Same method as attn_bf16.hip: the keys of a query tile (the union of the
+// key tiles in its window, Sliding Tile Attention, arXiv 2502.04507,
+// abstract) form one box of tokens, walked in 64-key blocks with every key's
+// address computed from its box coordinates.  What differs is the work split:
+// each wave owns three 16-query MFMA columns (48 queries) that share every K
+// and V operand it reads, and a workgroup of NW waves owns 48*NW queries
+// (384 = one 6x8x8 tile with NW = 8, 192 = one 3x8x8 tile with NW = 4).
+// Every 64-key block loaded into LDS thus feeds 3x the queries of a
+// 128-query workgroup, and every LDS operand read feeds 1.5x the products.
+//
+// Per 32-key chunk c of a block, per wave:
+//   S^T = K Q^T   for two 16-key MFMA row tiles t x three 16-query tiles;
+//                 K rows are permuted so that row r of tile t is key
+//                 8*(r/4) + 4t + r%4 of the chunk: lane group G = lane/16 then
+//                 holds keys 8G .. 8G+7 of its query after the two tiles.
+//   softmax       fp32, v_exp_f32 with scale*log2(e) folded into one FMA; the
+//                 max of a query spans the four lane groups (two exchanges).
+//   O^T += V^T P^T with P^T straight from the S^T accumulators (those eight
+//                 consecutive keys are one MFMA k-slice) and V^T from LDS.
+//
+// LDS (double-buffered, one barrier per block), all in 1 KB MFMA operand
+// fragments, each read as one contiguous 1 KB per wave:
+//   K fragment (c, t, ks): lane L holds head_dim [32ks + 8(L/16), +8) of key
+//     row 8*((L%16)/4) + 4t + L%4 of chunk c; filled by direct global->LDS
+//     loads (buffer_load_dwordx4 ... lds).
+//   V fragment (c, dt): lane L = 16G + p holds keys 8G .. 8G+7 of chunk c at
+//     head_dim 16dt + p, stored at piece 16G + (p ^ ((G << 1) | c)); filled by
+//     transposing register copies of V, the XOR making those stores free of
+//     bank conflicts.
+#include <type_traits>
+
+#include "box_common.h"
+
+namespace vdsa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int BUF_FLAGS = 0x00020000;   // raw buffer resource word 3 (gfx9-class)
+
+constexpr int HD = 128;
+constexpr int BLOCK_N = 64;   // keys per block
+constexpr int QT = 3;         // 16-query tiles per wave
+constexpr int KS = HD / 32;   // 32-wide head_dim steps of the S^T product
+constexpr int ND = HD / 16;   // 16-row head_dim tiles of O^T
+constexpr int NFRAG_K = 2 * 2 * KS;   // (chunk, t, ks)
+constexpr int NFRAG_V = 2 * ND;       // (chunk, dt)
+constexpr int K_STAGE = NFRAG_K * 1024;
+constexpr int V_STAGE = NFRAG_V * 1024;
+constexpr int STAGE = K_STAGE + V_STAGE;
+constexpr int WAIT_VMCNT0 = 0x0F70;   // s_waitcnt vmcnt(0), other counters untouched
+constexpr float RESCALE_MARGIN = 8.f;
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 2) void box_attn_bf16_m16_kernel(const BoxAttnParams p) {
+  constexpr int BLOCK_M = NW * 16 * QT;
+  constexpr int KDMA_W = NFRAG_K / NW;           // K fragments loaded per wave per block
+  constexpr int VPT = BLOCK_N * HD / 8 / (NW * 64);   // V 16-byte chunks per thread (2 or 4)
+  constexpr int NKG = BLOCK_N / VPT;             // threads per V head_dim chunk
+  static_assert(KDMA_W * NW == NFRAG_K && VPT * NKG == BLOCK_N && (VPT == 2 || VPT == 4), "split");
+
+  __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15;
+  const int G = lane >> 4;   // lane group
+
+  // ---- which (batch, head, query tile, query block) this workgroup owns
+  const int wg = xcd_remap(blockIdx.x, p.total_wg);
+  const int qblk = wg % p.qblocks;
+  const int rest = wg / p.qblocks;
+  const int ntiles = p.nT * p.nH * p.nW;
+  const int tile = rest % ntiles;
+  const int bh = rest / ntiles;
+  const int h = bh % p.heads;
+  const int b = bh / p.heads;
+
+  Box qb, kb;
+  tile_boxes(p, tile, qb, kb);
+  const int qvol = qb.et * qb.eh * qb.ew;
+  const int q0 = qblk * BLOCK_M;
+  if (q0 >= qvol) return;  // uniform over the workgroup
+  const int kvol = kb.et * kb.eh * kb.ew;
+  const int nkb = (kvol + BLOCK_N - 1) / BLOCK_N;
+
+  const char* __restrict__ qp = (const char*)p.q + 2 * (b * p.q_sb + h * p.q_sh);
+  const char* kp = (const char*)p.k + 2 * (b * p.k_sb + h * p.k_sh);
+  const char* vp = (const char*)p.v + 2 * (b * p.v_sb + h * p.v_sh);
+  const uint32_t nkeys = (uint32_t)(p.kT * p.kH * p.kW);
+  const uint32_t krange = (nkeys - 1u) * 2u * (uint32_t)p.k_sn + 2u * HD;
+  const uint32_t vrange = (nkeys - 1u) * 2u * (uint32_t)p.v_sn + 2u * HD;
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, (int)krange, BUF_FLAGS);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vp, 0, (int)vrange, BUF_FLAGS);
+  char* __restrict__ op = (char*)p.o + 2 * (b * p.o_sb + h * p.o_sh);
+  const uint32_t q_row = 2u * (uint32_t)p.q_sn, k_row = 2u * (uint32_t)p.k_sn;
+  const uint32_t v_row = 2u * (uint32_t)p.v_sn, o_row = 2u * (uint32_t)p.o_sn;
+
+  // ---- this lane's queries: column l16 of each of the wave's three tiles
+  uint32_t qtok[QT];
+  bool q_valid[QT];
+  bf16x8 qf[QT][KS];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int jq = q0 + wave * 16 * QT + 16 * qt + l16;
+    q_valid[qt] = jq < qvol;
+    const int j = min(jq, qvol - 1);
+    const int plane = qb.eh * qb.ew;
+    const int jt = j / plane;
+    const int r = j - jt * plane;
+    const int jh = r / qb.ew;
+    const int jw = r - jh * qb.ew;
+    qtok[qt] = (uint32_t)(((qb.t0 + jt) * p.qH + qb.h0 + jh) * p.qW + qb.w0 + jw);
+    const char* src = qp + qtok[qt] * q_row + 16 * G;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[qt][ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + 64 * ks));
+  }
+
+  // ---- key box addressing: key j -> token, via two divisions by invariants
+  const FastDiv fd_plane = make_fastdiv((uint32_t)(kb.eh * kb.ew));
+  const FastDiv fd_row = make_fastdiv((uint32_t)kb.ew);
+  auto key_token = [&](int j) -> uint32_t {
+    j = min(j, kvol - 1);   // keys past the box repeat the last key; masked later
+    const uint32_t jt = fast_div((uint32_t)j, fd_plane);
+    const uint32_t r = (uint32_t)j - jt * fd_plane.d;
+    const uint32_t jh = fast_div(r, fd_row);
+    const uint32_t jw = r - jh * fd_row.d;
+    return ((kb.t0 + jt) * p.kH + kb.h0 + jh) * p.kW + kb.w0 + jw;
+  };
+
+  // K DMA: lane L of fragment (c, t, ks) fetches key row 32c + 8*((L%16)/4) +
+  // 4t + L%4, head_dim chunk 4ks + L/16.
+  const int k_row_in_chunk = 8 * (l16 >> 2) + (l16 & 3);
+  // V load mapping: thread owns head_dim chunk vc (8 elements) of keys
+  // VPT*vk .. VPT*vk + VPT-1.
+  const int vk = tid % NKG;
+  const int vc = tid / NKG;
+  u32x4 vreg[VPT];
+
+  auto load_block = [&](int blk, int stage) {
+    const uint32_t my_tok = key_token(blk * BLOCK_N + lane);
+    char* st = lds + stage * STAGE;
+#pragma unroll
+    for (int i = 0; i < KDMA_W; ++i) {
+      const int f = wave * KDMA_W + i;           // fragment = (c*2 + t)*KS + ks
+      const int ks = f % KS, t = (f / KS) & 1, c = f / (2 * KS);
+      const uint32_t tok = (uint32_t)__shfl((int)my_tok, 32 * c + 4 * t + k_row_in_chunk, 64);
+      const uint32_t off = tok * k_row + (uint32_t)(4 * ks + G) * 16u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void*)(st + f * 1024), 16, (int)off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const uint32_t tok = (uint32_t)__shfl((int)my_tok, VPT * vk + i, 64);
+      vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrsrc, (int)(tok * v_row + vc * 16), 0, 0));
+    }
+  };
+  // Transposing store of the V registers into the V fragments of `stage`.
+  auto store_v = [&](int stage) {
+    char* vst = lds + stage * STAGE + K_STAGE;
+    const int k0 = VPT * vk;
+    const int c = k0 >> 5, kg = (k0 & 31) >> 3;
+    const int sig = (kg << 1) | c;
+    char* base = vst + c * ND * 1024 + kg * 256 + (k0 & 7) * 2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = 8 * vc + e;
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;   // high or low bf16 halves
+      char* dst = base + (d >> 4) * 1024 + (((d & 15) ^ sig) * 16);
+      if constexpr (VPT == 4) {
+        u32x2 pk;
+        pk[0] = __builtin_amdgcn_perm(vreg[1][e >> 1], vreg[0][e >> 1], sel);
+        pk[1] = __builtin_amdgcn_perm(vreg[3][e >> 1], vreg[2][e >> 1], sel);
+        *(u32x2*)dst = pk;
+      } else {
+        *(uint32_t*)dst = __builtin_amdgcn_perm(vreg[1][e >> 1], vreg[0][e >> 1], sel);
+      }
+    }
+  };
+
+  // V operand read offset per chunk c: piece 16G + (l16 ^ ((G << 1) | c))
+  int v_rd[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) v_rd[c] = K_STAGE + c * ND * 1024 + (16 * G + (l16 ^ ((G << 1) | c))) * 16;
+
+  f32x4 oacc[ND][QT];
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = f32x4{};
+  float m_run[QT], l_run[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    m_run[qt] = -INFINITY;
+    l_run[qt] = 0.f;
+  }
+  const float cl2 = p.scale_log2e;
+
+  load_block(0, 0);
+  store_v(0);
+  __builtin_amdgcn_s_waitcnt(WAIT_VMCNT0);
+  __syncthreads();
+
+  auto process = [&](int blk, auto partial_tag) {
+    constexpr bool PARTIAL = decltype(partial_tag)::value;
+    const int stage = blk & 1;
+    const bool more = blk + 1 < nkb;
+    if (more) load_block(blk + 1, stage ^ 1);
+    const char* st = lds + stage * STAGE;
+    const int nvalid = PARTIAL ? kvol - blk * BLOCK_N : BLOCK_N;
+
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      // S^T for the chunk: s[t][qt] register v = key 32c + 8G + 4t + v, query 16qt + l16
+      f32x4 s[2][QT];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) s[t][qt] = f32x4{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + ((c * 2 + t) * KS + ks) * 1024 + lane * 16));
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt)
+            s[t][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qt][ks], s[t][qt], 0, 0, 0);
+        }
+      }
+      // online softmax over the chunk's 32 keys
+      float mx[QT];
+      bool grow = false;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        float m = fmaxf(fmaxf(s[0][qt][0], s[0][qt][1]), fmaxf(s[0][qt][2], s[0][qt][3]));
+        m = fmaxf(m, fmaxf(fmaxf(s[1][qt][0], s[1][qt][1]), fmaxf(s[1][qt][2], s[1][qt][3])));
+        m = fmaxf(m, __shfl_xor(m, 16, 64));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        mx[qt] = m * cl2;
+        grow = grow || (mx[qt] > m_run[qt] + RESCALE_MARGIN);
+      }
+      // Lazy rescale: keep each query's reference max until some max in the
+      // wave grows by more than RESCALE_MARGIN (log2 units); probabilities
+      // stay below 2^RESCALE_MARGIN and the final normalisation by the same
+      // reference is exact.
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          const float m_new = fmaxf(m_run[qt], mx[qt]);
+          const float corr = __builtin_amdgcn_exp2f(m_run[qt] - m_new);
+          l_run[qt] *= corr;
+#pragma unroll
+          for (int dt = 0; dt < ND; ++dt) oacc[dt][qt] *= corr;
+          m_run[qt] = m_new;
+        }
+      }
+      bf16x8 pf[QT];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        float lsum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float pv = __builtin_amdgcn_exp2f(fmaf(s[e >> 2][qt][e & 3], cl2, -m_run[qt]));
+          if constexpr (PARTIAL) {
+            if (32 * c + 8 * G + e >= nvalid) pv = 0.f;
+          }
+          lsum += pv;
+          pf[qt][e] = (__bf16)pv;
+        }
+        l_run[qt] += lsum;
+      }
+      // O^T += V^T P^T for the chunk
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + v_rd[c] + dt * 1024));
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          oacc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[qt], oacc[dt][qt], 0, 0, 0);
+      }
+    }
+
+    if (more) store_v(stage ^ 1);
+    __builtin_amdgcn_s_waitcnt(WAIT_VMCNT0);   // K of the next block has landed in LDS
+    __syncthreads();
+  };
+
+  const bool last_partial = kvol % BLOCK_N != 0;
+  const int nfull = last_partial ? nkb - 1 : nkb;
+  for (int blk = 0; blk < nfull; ++blk) process(blk, std::false_type{});
+  if (last_partial) process(nkb - 1, std::true_type{});
+
+  // ---- epilogue: O^T register v of tile (dt, qt) is head_dim 16dt + 4G + v
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    float l_tot = l_run[qt] + __shfl_xor(l_run[qt], 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    const float inv = 1.f / l_tot;
+    if (q_valid[qt]) {
+      char* dst = op + qtok[qt] * o_row + 8 * G;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) {
+        bf16x4 ov;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) ov[v] = (__bf16)(oacc[dt][qt][v] * inv);
+        *(u32x2*)(dst + 32 * dt) = __builtin_bit_cast(u32x2, ov);
+      }
+      if (p.lse != nullptr && G == 0) {
+        const int64_t N = (int64_t)p.qT * p.qH * p.qW;
+        p.lse[((int64_t)b * p.heads + h) * N + qtok[qt]] =
+            (m_run[qt] + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_box_attn_bf16_m16(const BoxAttnParams& p, int nw, hipStream_t stream) {
+  const dim3 grid(p.total_wg), block(64 * nw);
+  if (nw == 8)
+    hipLaunchKernelGGL(box_attn_bf16_m16_kernel<8>, grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL(box_attn_bf16_m16_kernel<4>, grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace vdsa

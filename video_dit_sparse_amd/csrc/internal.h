@@ -48,6 +48,7 @@ struct BoxAttnParams {
   int32_t kT, kH, kW;
   int32_t dense_keys;
   int32_t qblocks;            // query blocks per tile
+  int32_t variant;            // which kernel shape the launcher runs (set by the host)
   int32_t total_wg;           // batch * heads * tiles * qblocks
   float scale_log2e;          // scale * log2(e)
 };
@@ -79,6 +80,8 @@ struct MergeParams {
 // Launchers: return hipSuccess or the launch error.  They assume the
 // parameters were validated.
 hipError_t launch_box_attn_bf16(const BoxAttnParams& p, int head_dim, hipStream_t stream);
+// head_dim 128 only: 48 queries per wave, nw = 8 (384 per workgroup) or 4 (192).
+hipError_t launch_box_attn_bf16_m16(const BoxAttnParams& p, int nw, hipStream_t stream);
 hipError_t launch_box_attn_f32(const BoxAttnParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_avgpool(const PoolParams& p, int bf16, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int bf16, hipStream_t stream);
