@@ -249,7 +249,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
     for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[0][v]);
 #pragma unroll
     for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[1][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+    mx = xhalf_max(mx) * c;
     // Lazy rescale: keep the reference max m_run until some query's block
     // max exceeds it by more than RESCALE_MARGIN (log2 units).  Until then
     // probabilities stay below 2^RESCALE_MARGIN, well inside bf16/fp32 range,
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
 
   // ---- epilogue: normalise and store (lane owns query l32; register v of
   // block nb holds head_dim index 32*nb + 8*(v/4) + 4*g + v%4)
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = xhalf_sum(l_run);
   const float inv = 1.f / l_tot;
   if (q_valid) {
     char* dst = op + qtok * o_row + 8 * g;

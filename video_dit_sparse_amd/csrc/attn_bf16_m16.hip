@@ -240,9 +240,7 @@ __global__ __launch_bounds__(NW * 64, 2) void box_attn_bf16_m16_kernel(const Box
       for (int qt = 0; qt < QT; ++qt) {
         float m = fmaxf(fmaxf(s[0][qt][0], s[0][qt][1]), fmaxf(s[0][qt][2], s[0][qt][3]));
         m = fmaxf(m, fmaxf(fmaxf(s[1][qt][0], s[1][qt][1]), fmaxf(s[1][qt][2], s[1][qt][3])));
-        m = fmaxf(m, __shfl_xor(m, 16, 64));
-        m = fmaxf(m, __shfl_xor(m, 32, 64));
-        mx[qt] = m * cl2;
+        mx[qt] = xrow4_max(m) * cl2;
         grow = grow || (mx[qt] > m_run[qt] + RESCALE_MARGIN);
       }
       // Lazy rescale: keep each query's reference max until some max in the
@@ -298,8 +296,7 @@ __global__ __launch_bounds__(NW * 64, 2) void box_attn_bf16_m16_kernel(const Box
   // ---- epilogue: O^T register v of tile (dt, qt) is head_dim 16dt + 4G + v
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    float l_tot = l_run[qt] + __shfl_xor(l_run[qt], 16, 64);
-    l_tot += __shfl_xor(l_tot, 32, 64);
+    const float l_tot = xrow4_sum(l_run[qt]);
     const float inv = 1.f / l_tot;
     if (q_valid[qt]) {
       char* dst = op + qtok[qt] * o_row + 8 * G;
