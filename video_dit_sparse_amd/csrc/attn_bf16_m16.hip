@@ -40,6 +40,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -58,6 +59,7 @@ constexpr int V_STAGE = NFRAG_V * 1024;
 constexpr int STAGE = K_STAGE + V_STAGE;
 constexpr int WAIT_VMCNT0 = 0x0F70;   // s_waitcnt vmcnt(0), other counters untouched
 constexpr float RESCALE_MARGIN = 8.f;
+__device__ constexpr bf16x2 kOnes2 = {(__bf16)1.f, (__bf16)1.f};
 
 template <int NW>
 __global__ __launch_bounds__(NW * 64, 2) void box_attn_bf16_m16_kernel(const BoxAttnParams p) {
@@ -261,17 +263,23 @@ __global__ __launch_bounds__(NW * 64, 2) void box_attn_bf16_m16_kernel(const Box
       bf16x8 pf[QT];
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        float lsum = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float pv = __builtin_amdgcn_exp2f(fmaf(s[e >> 2][qt][e & 3], cl2, -m_run[qt]));
           if constexpr (PARTIAL) {
             if (32 * c + 8 * G + e >= nvalid) pv = 0.f;
           }
-          lsum += pv;
           pf[qt][e] = (__bf16)pv;
         }
-        l_run[qt] += lsum;
+        // the denominator sums the bf16-rounded probabilities the P*V product
+        // uses, two per v_dot2_f32_bf16 against (1, 1)
+        float acc = l_run[qt];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 pr = {pf[qt][e], pf[qt][e + 1]};
+          acc = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, acc, false);
+        }
+        l_run[qt] = acc;
       }
       // O^T += V^T P^T for the chunk
 #pragma unroll
