@@ -27,7 +27,10 @@ METRIC = "effective attention TFLOP/s + ms/call (720P-shape STA, bf16); % MFMA p
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "sta_bf16_720p_counters.md")
-KERNEL_SOURCES = [os.path.join(ROOT, "video_dit_sparse_amd", "csrc", f) for f in ("attn_bf16.hip", "internal.h")]
+# 384-token (6x8x8) tiles at head_dim 128 run the 8-wave kernel of attn_bf16_pp.hip
+ROOFLINE_KERNEL = "box_attn_bf16_pp_kernel"
+KERNEL_SOURCES = [os.path.join(ROOT, "video_dit_sparse_amd", "csrc", f)
+                  for f in ("attn_bf16_pp.hip", "box_common.h", "internal.h")]
 
 
 def log(*a):
@@ -169,7 +172,7 @@ def main():
     traffic = measured_traffic() if w.name == "sta_720p" else None
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "box_attn_bf16_kernel<128>", "launch_ms": round(launch_ms, 4),
+                "kernel": ROOFLINE_KERNEL, "launch_ms": round(launch_ms, 4),
                 "flop_per_launch": launch_flops}
 
     extra = {}

@@ -52,6 +52,8 @@ SMALL_STA = [
     # 384- and 192-token tiles run the 48-queries-per-wave kernel
     ("tile384_bf16", (12, 16, 24), (6, 8, 8), (1, 3, 3), (0, 0, 0), 2, 128, "bf16"),
     ("tile384_shift_bf16", (11, 13, 21), (6, 8, 8), (3, 1, 3), (3, 4, 4), 1, 128, "bf16"),
+    # self-window with shifted partial tiles: key boxes of 1, 2 (ragged), 3 and 6 blocks
+    ("tile384_self_shift_bf16", (12, 16, 16), (6, 8, 8), (1, 1, 1), (3, 4, 4), 2, 128, "bf16"),
     ("tile192_bf16", (6, 16, 24), (3, 8, 8), (3, 3, 3), (0, 0, 0), 2, 128, "bf16"),
     ("tile192_shift_bf16", (7, 12, 20), (3, 8, 8), (1, 3, 1), (1, 4, 4), 1, 128, "bf16"),
 ]

@@ -16,6 +16,7 @@
 
 namespace vdsa {
 int box_attn_bf16_block_m();
+int box_attn_bf16_pp_block_m();
 int box_attn_f32_block_m();
 }  // namespace vdsa
 
@@ -139,17 +140,18 @@ int max_tile_extent(int L, int b, int s) {
 }
 
 // bf16 kernel shapes: queries per workgroup and the kernel that runs them.
+enum Bf16Kernel { K_M32 = 0, K_M16_4W = 1, K_PP_8W = 2 };
 struct Bf16Shape {
   int block_m;
-  int m16_waves;   // 0 = the 128-query 32x32 kernel
+  Bf16Kernel kernel;
 };
 
 // Largest block whose padding wastes at most 1/8 of the launched query slots,
 // else the least padding.
 Bf16Shape choose_bf16_shape(int64_t max_tile_vol, int head_dim) {
-  const Bf16Shape m32{vdsa::box_attn_bf16_block_m(), 0};
+  const Bf16Shape m32{vdsa::box_attn_bf16_block_m(), K_M32};
   if (head_dim != 128) return m32;
-  const Bf16Shape shapes[] = {{384, 8}, {192, 4}, m32};
+  const Bf16Shape shapes[] = {{vdsa::box_attn_bf16_pp_block_m(), K_PP_8W}, {192, K_M16_4W}, m32};
   Bf16Shape best = m32;
   double best_waste = 2.0;
   for (const Bf16Shape& sh : shapes) {
@@ -167,10 +169,10 @@ Bf16Shape choose_bf16_shape(int64_t max_tile_vol, int head_dim) {
 vdsa_status launch_attn(const vdsa_problem* prob, vdsa::BoxAttnParams& bp, hipStream_t stream) {
   const int64_t mv = (int64_t)max_tile_extent(bp.qT, bp.bT, bp.sT) * max_tile_extent(bp.qH, bp.bH, bp.sH) *
                      max_tile_extent(bp.qW, bp.bW, bp.sW);
-  Bf16Shape shape{vdsa::box_attn_f32_block_m(), 0};
+  Bf16Shape shape{vdsa::box_attn_f32_block_m(), K_M32};
   if (prob->dtype == VDSA_BF16) shape = choose_bf16_shape(mv, prob->head_dim);
   bp.qblocks = (int32_t)((mv + shape.block_m - 1) / shape.block_m);
-  bp.variant = shape.m16_waves;
+  bp.variant = (int32_t)shape.kernel;
   const int64_t total = (int64_t)bp.batch * bp.heads * bp.nT * bp.nH * bp.nW * bp.qblocks;
   if (total >= (int64_t(1) << 31) / 512)
     return fail(VDSA_ERR_SHAPE, "problem needs %lld workgroups, beyond the launch limit", (long long)total);
@@ -179,8 +181,10 @@ vdsa_status launch_attn(const vdsa_problem* prob, vdsa::BoxAttnParams& bp, hipSt
   hipError_t e;
   if (prob->dtype == VDSA_F32)
     e = vdsa::launch_box_attn_f32(bp, prob->head_dim, stream);
-  else if (shape.m16_waves != 0)
-    e = vdsa::launch_box_attn_bf16_m16(bp, shape.m16_waves, stream);
+  else if (shape.kernel == K_PP_8W)
+    e = vdsa::launch_box_attn_bf16_pp(bp, stream);
+  else if (shape.kernel == K_M16_4W)
+    e = vdsa::launch_box_attn_bf16_m16(bp, stream);
   else
     e = vdsa::launch_box_attn_bf16(bp, prob->head_dim, stream);
   if (e != hipSuccess) return fail(VDSA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));

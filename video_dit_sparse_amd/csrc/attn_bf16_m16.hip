@@ -7,10 +7,11 @@
 // abstract) form one box of tokens, walked in 64-key blocks with every key's
 // address computed from its box coordinates.  What differs is the work split:
 // each wave owns three 16-query MFMA columns (48 queries) that share every K
-// and V operand it reads, and a workgroup of NW waves owns 48*NW queries
-// (384 = one 6x8x8 tile with NW = 8, 192 = one 3x8x8 tile with NW = 4).
-// Every 64-key block loaded into LDS thus feeds 3x the queries of a
-// 128-query workgroup, and every LDS operand read feeds 1.5x the products.
+// and V operand it reads, and a workgroup of NW = 4 waves owns 192 queries
+// (one 3x8x8 tile; 384-query tiles run on the 8-wave kernel of
+// attn_bf16_pp.hip).  Every 64-key block loaded into LDS thus feeds 1.5x the
+// queries of a 128-query workgroup, and every LDS operand read feeds 1.5x the
+// products.
 //
 // Per 32-key chunk c of a block, per wave:
 //   S^T = K Q^T   for two 16-key MFMA row tiles t x three 16-query tiles;
@@ -326,12 +327,8 @@ __global__ __launch_bounds__(NW * 64, 2) void box_attn_bf16_m16_kernel(const Box
 
 }  // namespace
 
-hipError_t launch_box_attn_bf16_m16(const BoxAttnParams& p, int nw, hipStream_t stream) {
-  const dim3 grid(p.total_wg), block(64 * nw);
-  if (nw == 8)
-    hipLaunchKernelGGL(box_attn_bf16_m16_kernel<8>, grid, block, 0, stream, p);
-  else
-    hipLaunchKernelGGL(box_attn_bf16_m16_kernel<4>, grid, block, 0, stream, p);
+hipError_t launch_box_attn_bf16_m16(const BoxAttnParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(box_attn_bf16_m16_kernel<4>, dim3(p.total_wg), dim3(4 * 64), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -1,0 +1,450 @@
+// Tile-window ("box") attention forward for head_dim 128, bf16 in/out, fp32
+// accumulation, 384 queries per workgroup (one 6x8x8 query tile), with the
+// matrix-core work of one half of the workgroup overlapping the softmax of
+// the other half.
+//
+// Same method as the other box kernels: the keys of a query tile (the union of
+// the key tiles in its window, Sliding Tile Attention, arXiv 2502.04507,
+// abstract) form one box of tokens, walked in 64-key blocks (two 32-key
+// chunks) with every key's address computed from its box coordinates; each
+// wave owns three 16-query tiles of v_mfma_f32_16x16x32_bf16 (48 queries).
+//
+// Schedule.  Eight waves, two per SIMD: group A (waves 0-3) and group B
+// (waves 4-7) hold one wave on every SIMD each.  Every wave alternates two
+// kinds of phase:
+//   M  matrix-core phase: P*V of the previous chunk (plus the row sums of P,
+//      below) and S^T = K Q^T of the current chunk, 51 MFMAs;
+//   V  softmax phase of the current chunk (VALU and exp only).
+// Group B runs one phase behind group A and a workgroup barrier separates
+// consecutive phases, so on each SIMD one wave issues MFMAs while the other
+// runs its softmax.  Every wave passes the same number of barriers: B takes
+// one extra before its first phase, A one after its last.
+//
+// Per wave and 64-key block b the phases are
+//   M(b,0): P*V(b-1, chunk 1), S(b, chunk 0)   V(b,0): softmax(b, chunk 0)
+//   M(b,1): P*V(b, chunk 0),   S(b, chunk 1)   V(b,1): softmax(b, chunk 1)
+// with one trailing P*V after the last block.
+//
+// LDS: a ring of three stages of (16 KB K fragments + 16 KB V^T fragments),
+// each fragment the 1 KB operand of one MFMA, read as one contiguous 1 KB per
+// wave.  Block b+2 is requested at the start of M(b,1): K by direct
+// global->LDS loads, V into registers, stored transposed into its V^T
+// fragments in V(b+1,0).  K of block b+1 must have landed before group A's
+// M(b+1,0): A waits for it at the end of V(b,1), B at the end of M(b,1) (the
+// same barrier), each keeping the loads of block b+2 in flight.  The stage a
+// block overwrites was last read three phases before its first write.
+//
+// Fragment layouts (lane L = 16G + p of a wave):
+//   K fragment (c, t, ks): lane L holds head_dim [32ks + 8G, +8) of key row
+//     8*(p/4) + 4t + p%4 of chunk c, so that after the two 16-row tiles t the
+//     lane group G holds keys 8G .. 8G+7 of its query;
+//   V^T fragment (c, dt): lane L holds keys 8G .. 8G+7 of chunk c at head_dim
+//     16dt + p, stored at piece 16G + (p ^ ((G << 1) | c)) so that the
+//     transposing stores are free of bank conflicts.
+//
+// Softmax: probabilities are exp2(s*scale*log2(e) - m) for a per-query
+// reference m that is raised only when some score of the wave exceeds it by
+// more than RESCALE_MARGIN (log2 units), so probabilities stay below
+// 2^RESCALE_MARGIN and the final normalisation by the same reference is
+// exact.  Each lane tests its own eight scores of a query (a chunk maximum
+// exceeds the threshold exactly when one of its lanes' maxima does); the
+// cross-lane maximum is formed only when some lane fires.  The row sums of P
+// (the softmax denominators) come from the matrix core: an all-ones A operand
+// times the P^T operand puts each query's chunk sum in every row of a 16x16
+// product, accumulated in fp32 like O^T.
+#include <type_traits>
+
+#include "box_common.h"
+
+namespace vdsa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+constexpr int BUF_FLAGS = 0x00020000;   // raw buffer resource word 3 (gfx9-class)
+
+constexpr int HD = 128;
+constexpr int BLOCK_N = 64;             // keys per block
+constexpr int QT = 3;                   // 16-query tiles per wave
+constexpr int NW = 8;                   // waves per workgroup
+constexpr int BLOCK_M = NW * 16 * QT;   // 384 queries per workgroup
+constexpr int KS = HD / 32;             // 32-wide head_dim steps of S^T
+constexpr int ND = HD / 16;             // 16-row head_dim tiles of O^T
+constexpr int NFRAG_K = 2 * 2 * KS;     // (chunk, t, ks)
+constexpr int K_STAGE = NFRAG_K * 1024;
+constexpr int V_STAGE = 2 * ND * 1024;  // (chunk, dt)
+constexpr int STAGE = K_STAGE + V_STAGE;
+constexpr int NSTAGE = 3;
+constexpr int KDMA_W = NFRAG_K / NW;                 // K fragments loaded per wave per block
+constexpr int VPT = BLOCK_N * HD / 8 / (NW * 64);    // V 16-byte chunks per thread
+constexpr int NKG = BLOCK_N / VPT;                   // threads per V head_dim chunk
+constexpr int NLOAD = KDMA_W + VPT;                  // vector-memory loads per wave per block
+constexpr int PF = 4;                                // operand fragments read ahead in an M phase
+constexpr float RESCALE_MARGIN = 8.f;
+static_assert(KDMA_W * NW == NFRAG_K && VPT == 2 && VPT * NKG == BLOCK_N, "work split");
+
+// s_waitcnt immediate: vmcnt(vm), lgkmcnt(lgkm), expcnt untouched
+__device__ __forceinline__ constexpr int wait_enc(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
+}
+
+// Phase boundary: this wave's LDS accesses are complete, then a workgroup
+// barrier.  Outstanding global loads stay in flight.  Neither the compiler's
+// scheduler nor its memory optimisations move work across it.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(wait_enc(63, 0));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Wait until at most `keep` of this wave's vector-memory loads are in flight.
+__device__ __forceinline__ void vm_wait(bool keep_one_block) {
+  if (keep_one_block)
+    __builtin_amdgcn_s_waitcnt(wait_enc(NLOAD, 15));
+  else
+    __builtin_amdgcn_s_waitcnt(wait_enc(0, 15));
+}
+
+// Empty asm statements that claim to rewrite their operands: the values are
+// computed before this point, so the work of a phase cannot sink into the next.
+__device__ __forceinline__ void pin(f32x4& a, f32x4& b, f32x4& c) { asm volatile("" : "+v"(a), "+v"(b), "+v"(c)); }
+__device__ __forceinline__ void pin(float& a, float& b, float& c) { asm volatile("" : "+v"(a), "+v"(b), "+v"(c)); }
+__device__ __forceinline__ void pin(bf16x8& x) {
+  u32x4 u = __builtin_bit_cast(u32x4, x);
+  asm volatile("" : "+v"(u));
+  x = __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ bf16x8 lds_frag(const char* p) { return __builtin_bit_cast(bf16x8, *(const u32x4*)p); }
+
+__global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttnParams p) {
+  __shared__ __attribute__((aligned(16))) char lds[NSTAGE * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15;
+  const int G = lane >> 4;
+  const bool grp_b = wave >= NW / 2;   // waves w and w + 4 share a SIMD
+
+  // ---- which (batch, head, query tile, query block) this workgroup owns
+  const int wg = xcd_remap(blockIdx.x, p.total_wg);
+  const int qblk = wg % p.qblocks;
+  const int rest = wg / p.qblocks;
+  const int ntiles = p.nT * p.nH * p.nW;
+  const int tile = rest % ntiles;
+  const int bh = rest / ntiles;
+  const int h = bh % p.heads;
+  const int b = bh / p.heads;
+
+  Box qb, kb;
+  tile_boxes(p, tile, qb, kb);
+  const int qvol = qb.et * qb.eh * qb.ew;
+  const int q0 = qblk * BLOCK_M;
+  if (q0 >= qvol) return;  // uniform over the workgroup, before any barrier
+  const int kvol = kb.et * kb.eh * kb.ew;
+  const int nkb = (kvol + BLOCK_N - 1) / BLOCK_N;
+
+  const char* __restrict__ qp = (const char*)p.q + 2 * (b * p.q_sb + h * p.q_sh);
+  const char* kp = (const char*)p.k + 2 * (b * p.k_sb + h * p.k_sh);
+  const char* vp = (const char*)p.v + 2 * (b * p.v_sb + h * p.v_sh);
+  const uint32_t nkeys = (uint32_t)(p.kT * p.kH * p.kW);
+  const uint32_t krange = (nkeys - 1u) * 2u * (uint32_t)p.k_sn + 2u * HD;
+  const uint32_t vrange = (nkeys - 1u) * 2u * (uint32_t)p.v_sn + 2u * HD;
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, (int)krange, BUF_FLAGS);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vp, 0, (int)vrange, BUF_FLAGS);
+  char* __restrict__ op = (char*)p.o + 2 * (b * p.o_sb + h * p.o_sh);
+  const uint32_t q_row = 2u * (uint32_t)p.q_sn, k_row = 2u * (uint32_t)p.k_sn;
+  const uint32_t v_row = 2u * (uint32_t)p.v_sn, o_row = 2u * (uint32_t)p.o_sn;
+
+  // ---- this lane's queries: column l16 of each of the wave's three tiles
+  uint32_t qtok[QT];
+  bool q_valid[QT];
+  bf16x8 qf[QT][KS];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int jq = q0 + wave * 16 * QT + 16 * qt + l16;
+    q_valid[qt] = jq < qvol;
+    const int j = min(jq, qvol - 1);
+    const int plane = qb.eh * qb.ew;
+    const int jt = j / plane;
+    const int r = j - jt * plane;
+    const int jh = r / qb.ew;
+    const int jw = r - jh * qb.ew;
+    qtok[qt] = (uint32_t)(((qb.t0 + jt) * p.qH + qb.h0 + jh) * p.qW + qb.w0 + jw);
+    const char* src = qp + qtok[qt] * q_row + 16 * G;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[qt][ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + 64 * ks));
+  }
+
+  // ---- key box addressing: key j -> token, via two divisions by invariants
+  const FastDiv fd_plane = make_fastdiv((uint32_t)(kb.eh * kb.ew));
+  const FastDiv fd_row = make_fastdiv((uint32_t)kb.ew);
+  auto key_token = [&](int j) -> uint32_t {
+    j = min(j, kvol - 1);   // keys past the box repeat the last key; masked later
+    const uint32_t jt = fast_div((uint32_t)j, fd_plane);
+    const uint32_t r = (uint32_t)j - jt * fd_plane.d;
+    const uint32_t jh = fast_div(r, fd_row);
+    const uint32_t jw = r - jh * fd_row.d;
+    return ((kb.t0 + jt) * p.kH + kb.h0 + jh) * p.kW + kb.w0 + jw;
+  };
+  auto stage_of = [&](int blk) -> char* { return lds + (blk % NSTAGE) * STAGE; };
+
+  // K: lane L of fragment (c, t, ks) fetches key row 32c + 8*((L%16)/4) +
+  // 4t + L%4, head_dim chunk 4ks + L/16.  V: thread owns head_dim chunk vc
+  // (8 elements) of keys VPT*vk .. VPT*vk + VPT-1.
+  const int k_row_in_chunk = 8 * (l16 >> 2) + (l16 & 3);
+  const int vk = tid % NKG;
+  const int vc = tid / NKG;
+  u32x4 vreg[VPT];
+  auto load_block = [&](int blk) {
+    const uint32_t my_tok = key_token(blk * BLOCK_N + lane);
+    char* st = stage_of(blk);
+#pragma unroll
+    for (int i = 0; i < KDMA_W; ++i) {
+      const int f = wave * KDMA_W + i;           // fragment = (c*2 + t)*KS + ks
+      const int ks = f % KS, t = (f / KS) & 1, c = f / (2 * KS);
+      const uint32_t tok = (uint32_t)__shfl((int)my_tok, 32 * c + 4 * t + k_row_in_chunk, 64);
+      const uint32_t off = tok * k_row + (uint32_t)(4 * ks + G) * 16u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void*)(st + f * 1024), 16, (int)off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const uint32_t tok = (uint32_t)__shfl((int)my_tok, VPT * vk + i, 64);
+      vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrsrc, (int)(tok * v_row + vc * 16), 0, 0));
+    }
+  };
+  // Transposing store of the V registers: element e of the thread's two keys
+  // (head_dim 8vc + e) goes to a fixed offset in the stage's V^T area.
+  uint32_t vw_off[8];
+  {
+    const int k0 = VPT * vk;
+    const int c = k0 >> 5, kg = (k0 & 31) >> 3;
+    const int sig = (kg << 1) | c;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = 8 * vc + e;
+      vw_off[e] = (uint32_t)(c * ND * 1024 + kg * 256 + (k0 & 7) * 2 + (d >> 4) * 1024 + (((d & 15) ^ sig) * 16));
+    }
+  }
+  auto store_v = [&](int blk) {
+    const uint32_t vbase = (uint32_t)(uintptr_t)(stage_of(blk) + K_STAGE);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;   // high or low bf16 halves
+      *(lds_u32*)(uintptr_t)(vbase + vw_off[e]) = __builtin_amdgcn_perm(vreg[1][e >> 1], vreg[0][e >> 1], sel);
+    }
+  };
+
+  // V^T operand read offset per chunk c: piece 16G + (l16 ^ ((G << 1) | c))
+  int v_rd[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) v_rd[c] = K_STAGE + c * ND * 1024 + (16 * G + (l16 ^ ((G << 1) | c))) * 16;
+
+  f32x4 oacc[ND][QT];
+  f32x4 lacc[QT];    // row sums of P, the same value in all four registers
+  float m_run[QT];   // per-query reference maximum (log2 units)
+  float m_thr[QT];   // m_run + RESCALE_MARGIN
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) oacc[dt][qt] = f32x4{};
+    lacc[qt] = f32x4{};
+    m_run[qt] = -INFINITY;
+    m_thr[qt] = -INFINITY;
+  }
+  bf16x8 ones8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones8[e] = (__bf16)1.f;
+  const float cl2 = p.scale_log2e;
+
+  // ---- M phase: the 8 V^T fragments of chunk cv of st_v (P*V, fragments
+  // 0..7, the first PF read by prefetch_pv in the preceding V phase), then the
+  // 8 K fragments of chunk ck of st_k (S, fragments 8..15 in (ks, t) order so
+  // that dependent products are six MFMAs apart).  Reads run PF ahead.
+  bf16x8 fb[16];
+  auto frag_ptr = [&](const char* st_v, int cv, const char* st_k, int ck, int i) -> const char* {
+    if (i < 8) return st_v + v_rd[cv] + i * 1024;
+    const int j = i - 8, ks = j >> 1, t = j & 1;
+    return st_k + ((ck * 2 + t) * KS + ks) * 1024 + lane * 16;
+  };
+  auto prefetch_pv = [&](const char* st_v, int cv) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) fb[i] = lds_frag(st_v + v_rd[cv] + i * 1024);
+  };
+  f32x4 s[2][QT];
+  bf16x8 pf[QT];
+  auto mphase = [&](bool with_pv, const char* st_v, int cv, bool with_s, const char* st_k, int ck) {
+    const int i0 = with_pv ? 0 : 8;
+    const int i1 = with_s ? 16 : 8;
+    if (!with_pv) {
+#pragma unroll
+      for (int i = 8; i < 8 + PF; ++i) fb[i] = lds_frag(frag_ptr(st_v, cv, st_k, ck, i));
+    }
+    if (with_s) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) s[t][qt] = f32x4{};
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i < i0 || i >= i1) continue;
+      if (i + PF < i1) fb[i + PF] = lds_frag(frag_ptr(st_v, cv, st_k, ck, i + PF));
+      __builtin_amdgcn_sched_barrier(0);
+      if (i < 8) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          oacc[i][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[i], pf[qt], oacc[i][qt], 0, 0, 0);
+        if (i == 3) {
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt)
+            lacc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pf[qt], lacc[qt], 0, 0, 0);
+        }
+      } else {
+        const int j = i - 8, ks = j >> 1, t = j & 1;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          s[t][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[i], qf[qt][ks], s[t][qt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (with_pv) {
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) pin(oacc[dt][0], oacc[dt][1], oacc[dt][2]);
+      pin(lacc[0], lacc[1], lacc[2]);
+    }
+    if (with_s) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) pin(s[t][0], s[t][1], s[t][2]);
+    }
+  };
+
+  // ---- V phase: online softmax of one chunk; nvalid = keys of the block
+  // from this chunk on (masking only in the last, partial block).
+  auto softmax = [&](int nvalid, auto partial_tag) {
+    constexpr bool PARTIAL = decltype(partial_tag)::value;
+    float lmax[QT];
+    bool grow = false;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float m = fmaxf(fmaxf(s[0][qt][0], s[0][qt][1]), fmaxf(s[0][qt][2], s[0][qt][3]));
+      m = fmaxf(m, fmaxf(fmaxf(s[1][qt][0], s[1][qt][1]), fmaxf(s[1][qt][2], s[1][qt][3])));
+      lmax[qt] = m;
+      grow = grow || (m * cl2 > m_thr[qt]);
+    }
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const float m_new = fmaxf(m_run[qt], xrow4_max(lmax[qt]) * cl2);
+        const float corr = __builtin_amdgcn_exp2f(m_run[qt] - m_new);
+        lacc[qt] *= corr;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) oacc[dt][qt] *= corr;
+        m_run[qt] = m_new;
+        m_thr[qt] = m_new + RESCALE_MARGIN;
+      }
+    }
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float pv = __builtin_amdgcn_exp2f(fmaf(s[e >> 2][qt][e & 3], cl2, -m_run[qt]));
+        if constexpr (PARTIAL) {
+          if (8 * G + e >= nvalid) pv = 0.f;
+        }
+        pf[qt][e] = (__bf16)pv;
+      }
+      pin(pf[qt]);
+    }
+    pin(m_run[0], m_run[1], m_run[2]);
+  };
+
+  // ---- prologue: block 0 complete in LDS, block 1 in flight
+  load_block(0);
+  store_v(0);
+  if (nkb > 1) load_block(1);
+  vm_wait(nkb > 1);
+  phase_barrier();
+  if (grp_b) phase_barrier();
+
+  auto do_block = [&](int blk, auto partial_tag) {
+    const char* st = stage_of(blk);
+    const int nvalid = kvol - blk * BLOCK_N;
+    const bool more2 = blk + 2 < nkb;
+    // M(blk, 0)
+    __builtin_amdgcn_s_setprio(1);
+    if (blk > 0)
+      mphase(true, stage_of(blk - 1), 1, true, st, 0);
+    else
+      mphase(false, st, 0, true, st, 0);
+    __builtin_amdgcn_s_setprio(0);
+    phase_barrier();
+    // V(blk, 0)
+    prefetch_pv(st, 0);
+    softmax(nvalid, partial_tag);
+    if (blk + 1 < nkb) store_v(blk + 1);
+    phase_barrier();
+    // M(blk, 1)
+    __builtin_amdgcn_s_setprio(1);
+    if (more2) load_block(blk + 2);
+    mphase(true, st, 0, true, st, 1);
+    __builtin_amdgcn_s_setprio(0);
+    if (grp_b) vm_wait(more2);   // K of block blk+1 has landed
+    phase_barrier();
+    // V(blk, 1)
+    prefetch_pv(st, 1);
+    softmax(nvalid - 32, partial_tag);
+    if (!grp_b) vm_wait(more2);
+    phase_barrier();
+  };
+  const bool last_partial = kvol % BLOCK_N != 0;
+  const int nfull = last_partial ? nkb - 1 : nkb;
+  for (int blk = 0; blk < nfull; ++blk) do_block(blk, std::false_type{});
+  if (last_partial) do_block(nkb - 1, std::true_type{});
+  __builtin_amdgcn_s_setprio(1);
+  mphase(true, stage_of(nkb - 1), 1, false, stage_of(nkb - 1), 0);
+  __builtin_amdgcn_s_setprio(0);
+  if (!grp_b) phase_barrier();
+
+  // ---- epilogue: O^T register v of tile (dt, qt) is head_dim 16dt + 4G + v
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const float l_tot = lacc[qt][0];
+    const float inv = 1.f / l_tot;
+    if (q_valid[qt]) {
+      char* dst = op + qtok[qt] * o_row + 8 * G;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) {
+        bf16x4 ov;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) ov[v] = (__bf16)(oacc[dt][qt][v] * inv);
+        *(u32x2*)(dst + 32 * dt) = __builtin_bit_cast(u32x2, ov);
+      }
+      if (p.lse != nullptr && G == 0) {
+        const int64_t N = (int64_t)p.qT * p.qH * p.qW;
+        p.lse[((int64_t)b * p.heads + h) * N + qtok[qt]] =
+            (m_run[qt] + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_box_attn_bf16_pp(const BoxAttnParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(box_attn_bf16_pp_kernel, dim3(p.total_wg), dim3(NW * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+int box_attn_bf16_pp_block_m() { return BLOCK_M; }
+
+}  // namespace vdsa

@@ -80,8 +80,11 @@ struct MergeParams {
 // Launchers: return hipSuccess or the launch error.  They assume the
 // parameters were validated.
 hipError_t launch_box_attn_bf16(const BoxAttnParams& p, int head_dim, hipStream_t stream);
-// head_dim 128 only: 48 queries per wave, nw = 8 (384 per workgroup) or 4 (192).
-hipError_t launch_box_attn_bf16_m16(const BoxAttnParams& p, int nw, hipStream_t stream);
+// head_dim 128 only, 48 queries per wave: 4 waves (192 queries per workgroup).
+hipError_t launch_box_attn_bf16_m16(const BoxAttnParams& p, hipStream_t stream);
+// head_dim 128 only, 48 queries per wave: 8 waves (384 queries per workgroup)
+// in two groups whose matrix-core and softmax phases alternate.
+hipError_t launch_box_attn_bf16_pp(const BoxAttnParams& p, hipStream_t stream);
 hipError_t launch_box_attn_f32(const BoxAttnParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_avgpool(const PoolParams& p, int bf16, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int bf16, hipStream_t stream);
