@@ -29,6 +29,10 @@
  *     token stride times the element size a multiple of 16 bytes.
  *   - Size limit: within one (batch, head), the largest byte offset
  *     ((N-1)*stride_n + head_dim) * element size must be below 2^32.
+ *   - Inputs must be finite.  The kernels are built without NaN handling in
+ *     their maximum operations, so a NaN or infinity in Q, K, V or the gate
+ *     gives unspecified (possibly non-NaN) outputs for the rows it reaches;
+ *     it is never an error and never faults.
  */
 #ifndef VDSA_H
 #define VDSA_H
