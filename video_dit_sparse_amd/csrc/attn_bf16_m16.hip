@@ -18,10 +18,16 @@
 //                 K rows are permuted so that row r of tile t is key
 //                 8*(r/4) + 4t + r%4 of the chunk: lane group G = lane/16 then
 //                 holds keys 8G .. 8G+7 of its query after the two tiles.
-//   softmax       fp32, v_exp_f32 with scale*log2(e) folded into one FMA; the
-//                 max of a query spans the four lane groups (two exchanges).
+//   softmax       fp32, v_exp_f32 with scale*log2(e) folded into one FMA,
+//                 against a lazy per-query reference raised only when some
+//                 score of the wave exceeds it by more than RESCALE_MARGIN;
+//                 each lane tests its own eight scores, and the cross-lane
+//                 maximum (two exchanges) is formed only when one fires.
 //   O^T += V^T P^T with P^T straight from the S^T accumulators (those eight
-//                 consecutive keys are one MFMA k-slice) and V^T from LDS.
+//                 consecutive keys are one MFMA k-slice) and V^T from LDS;
+//                 an all-ones A operand times the same P^T gives the row sums
+//                 of P (the softmax denominators) on the matrix core.
+// Operand fragments are read RA ahead of the MFMAs that use them.
 //
 // LDS (double-buffered, one barrier per block), all in 1 KB MFMA operand
 // fragments, each read as one contiguous 1 KB per wave:
@@ -41,7 +47,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -60,7 +65,7 @@ constexpr int V_STAGE = NFRAG_V * 1024;
 constexpr int STAGE = K_STAGE + V_STAGE;
 constexpr int WAIT_VMCNT0 = 0x0F70;   // s_waitcnt vmcnt(0), other counters untouched
 constexpr float RESCALE_MARGIN = 8.f;
-__device__ constexpr bf16x2 kOnes2 = {(__bf16)1.f, (__bf16)1.f};
+constexpr int RA = 3;   // operand fragments read ahead of their MFMAs
 
 template <int NW>
 __global__ __launch_bounds__(NW * 64, 2) void box_attn_bf16_m16_kernel(const BoxAttnParams p) {
@@ -199,12 +204,16 @@ __global__ __launch_bounds__(NW * 64, 2) void box_attn_bf16_m16_kernel(const Box
   for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = f32x4{};
-  float m_run[QT], l_run[QT];
+  float m_run[QT];
+  f32x4 lacc[QT];   // row sums of P (all-ones A operand times P^T)
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     m_run[qt] = -INFINITY;
-    l_run[qt] = 0.f;
+    lacc[qt] = f32x4{};
   }
+  bf16x8 ones8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones8[e] = (__bf16)1.f;
   const float cl2 = p.scale_log2e;
 
   load_block(0, 0);
@@ -225,37 +234,45 @@ __global__ __launch_bounds__(NW * 64, 2) void box_attn_bf16_m16_kernel(const Box
       // S^T for the chunk: s[t][qt] register v = key 32c + 8G + 4t + v, query 16qt + l16
       f32x4 s[2][QT];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) s[t][qt] = f32x4{};
+      {
+        // K fragments in (ks, t) order, read RA ahead of their products
+        auto kfp = [&](int i) { return st + ((c * 2 + (i & 1)) * KS + (i >> 1)) * 1024 + lane * 16; };
+        bf16x8 kb[8];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + ((c * 2 + t) * KS + ks) * 1024 + lane * 16));
+        for (int i = 0; i < RA; ++i) kb[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)kfp(i));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (i + RA < 8) kb[i + RA] = __builtin_bit_cast(bf16x8, *(const u32x4*)kfp(i + RA));
+          __builtin_amdgcn_sched_barrier(0);
+          const int ks = i >> 1, t = i & 1;
 #pragma unroll
           for (int qt = 0; qt < QT; ++qt)
-            s[t][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qt][ks], s[t][qt], 0, 0, 0);
+            s[t][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[i], qf[qt][ks], s[t][qt], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // online softmax over the chunk's 32 keys
-      float mx[QT];
+      // online softmax over the chunk's 32 keys.  Lazy rescale: keep each
+      // query's reference max until some score of the wave exceeds it by more
+      // than RESCALE_MARGIN (log2 units); each lane tests its own eight scores
+      // of a query, and the cross-lane maximum is formed only when one fires.
+      float lmax[QT];
       bool grow = false;
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
         float m = fmaxf(fmaxf(s[0][qt][0], s[0][qt][1]), fmaxf(s[0][qt][2], s[0][qt][3]));
         m = fmaxf(m, fmaxf(fmaxf(s[1][qt][0], s[1][qt][1]), fmaxf(s[1][qt][2], s[1][qt][3])));
-        mx[qt] = xrow4_max(m) * cl2;
-        grow = grow || (mx[qt] > m_run[qt] + RESCALE_MARGIN);
+        lmax[qt] = m;
+        grow = grow || (m * cl2 > m_run[qt] + RESCALE_MARGIN);
       }
-      // Lazy rescale: keep each query's reference max until some max in the
-      // wave grows by more than RESCALE_MARGIN (log2 units); probabilities
-      // stay below 2^RESCALE_MARGIN and the final normalisation by the same
-      // reference is exact.
       if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
-          const float m_new = fmaxf(m_run[qt], mx[qt]);
+          const float m_new = fmaxf(m_run[qt], xrow4_max(lmax[qt]) * cl2);
           const float corr = __builtin_amdgcn_exp2f(m_run[qt] - m_new);
-          l_run[qt] *= corr;
+          lacc[qt] *= corr;
 #pragma unroll
           for (int dt = 0; dt < ND; ++dt) oacc[dt][qt] *= corr;
           m_run[qt] = m_new;
@@ -272,23 +289,26 @@ __global__ __launch_bounds__(NW * 64, 2) void box_attn_bf16_m16_kernel(const Box
           }
           pf[qt][e] = (__bf16)pv;
         }
-        // the denominator sums the bf16-rounded probabilities the P*V product
-        // uses, two per v_dot2_f32_bf16 against (1, 1)
-        float acc = l_run[qt];
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const bf16x2 pr = {pf[qt][e], pf[qt][e + 1]};
-          acc = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, acc, false);
-        }
-        l_run[qt] = acc;
       }
-      // O^T += V^T P^T for the chunk
+      // O^T += V^T P^T for the chunk, V^T fragments read RA ahead
+      {
+        bf16x8 vb[ND];
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + v_rd[c] + dt * 1024));
+        for (int i = 0; i < RA; ++i) vb[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + v_rd[c] + i * 1024));
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-          oacc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[qt], oacc[dt][qt], 0, 0, 0);
+        for (int dt = 0; dt < ND; ++dt) {
+          if (dt + RA < ND) vb[dt + RA] = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + v_rd[c] + (dt + RA) * 1024));
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt)
+            oacc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[dt], pf[qt], oacc[dt][qt], 0, 0, 0);
+          if (dt == 3) {
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt)
+              lacc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pf[qt], lacc[qt], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
 
@@ -305,7 +325,7 @@ __global__ __launch_bounds__(NW * 64, 2) void box_attn_bf16_m16_kernel(const Box
   // ---- epilogue: O^T register v of tile (dt, qt) is head_dim 16dt + 4G + v
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    const float l_tot = xrow4_sum(l_run[qt]);
+    const float l_tot = lacc[qt][0];
     const float inv = 1.f / l_tot;
     if (q_valid[qt]) {
       char* dst = op + qtok[qt] * o_row + 8 * G;
