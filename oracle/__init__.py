@@ -20,6 +20,8 @@ from .ref import (  # noqa: F401
     pooled_grid,
     global_ref,
     merge_ref,
+    merge_lse_ref,
+    union_attention_ref,
     sta_pair_count_ref,
     sta_flops_ref,
     global_flops_ref,

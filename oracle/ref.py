@@ -47,8 +47,8 @@ __all__ = [
     "to_f64", "token_coords", "tile_index", "tile_counts", "tile_extent",
     "window_radius", "sta_mask_row", "sta_ref", "dense_ref",
     "attention_weights_ref", "pooled_grid", "pool_ref", "global_ref",
-    "merge_ref", "sta_pair_count_ref", "sta_flops_ref", "global_flops_ref",
-    "dense_flops_ref",
+    "merge_ref", "merge_lse_ref", "union_attention_ref", "sta_pair_count_ref",
+    "sta_flops_ref", "global_flops_ref", "dense_flops_ref",
 ]
 
 
@@ -261,6 +261,46 @@ def merge_ref(o_local, o_global, w_local, w_global) -> np.ndarray:
     wg = to_f64(w_global).reshape(heads)
     shape = (heads,) + (1,) * (ol.ndim - 1)
     return wl.reshape(shape) * ol + wg.reshape(shape) * og
+
+
+def merge_lse_ref(o_a, lse_a, o_b, lse_b):
+    """Exact merge of two attention results over disjoint key sets A and B.
+
+    Reading of UltraGen §4.1's fusion of the local and the global latent as
+    one softmax over the union of both key sets: with Z_X = exp(LSE_X),
+    O = (Z_A O_A + Z_B O_B) / (Z_A + Z_B) and LSE = log(Z_A + Z_B).
+    ``o_*``: ``[..., D]``; ``lse_*``: ``[...]`` (natural log).  Returns (O, LSE).
+    """
+    oa, ob = to_f64(o_a), to_f64(o_b)
+    la, lb = to_f64(lse_a), to_f64(lse_b)
+    m = np.maximum(la, lb)
+    ea, eb = np.exp(la - m), np.exp(lb - m)
+    z = ea + eb
+    return (ea[..., None] * oa + eb[..., None] * ob) / z[..., None], m + np.log(z)
+
+
+def union_attention_ref(q, k, v, grid, tile, window, shift, k_pooled, v_pooled, scale=None, rows=None):
+    """Each query attends the union of its sliding-tile window keys (as in
+    ``sta_ref``) and every pooled key (as in ``global_ref``): one softmax over
+    the concatenated key list, evaluated by the definition.  Returns (O, LSE).
+    """
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    kp, vp = to_f64(k_pooled), to_f64(v_pooled)
+    N, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    radius = window_radius(window)
+    ti = tile_index(token_coords(grid), tile, shift)
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.empty((len(rows), v.shape[1]))
+    lse = np.empty(len(rows))
+    for j, n in enumerate(rows):
+        keys = np.nonzero(sta_mask_row(ti, ti[n], radius))[0]
+        kk = np.concatenate([k[keys], kp], axis=0)
+        vv = np.concatenate([v[keys], vp], axis=0)
+        oj, lj = _softmax_attend(q[n:n + 1], kk, vv, scale)
+        o[j], lse[j] = oj[0], lj[0]
+    return o, lse
 
 
 # --------------------------------------------------------------------------

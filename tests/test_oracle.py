@@ -299,6 +299,66 @@ def test_merge_special_cases_and_linearity():
     np.testing.assert_array_equal(R.merge_ref(ol[perm], og[perm], None, g[perm]), m[perm])
 
 
+# ---------------------------------------------------------------- exact (LSE) merge
+@pytest.mark.parametrize("grid,tile,window,shift,pool", [
+    ((4, 6, 8), (2, 3, 4), (1, 1, 1), (0, 0, 0), (2, 2)),
+    ((3, 7, 9), (2, 4, 4), (3, 1, 3), (1, 2, 2), (3, 4)),
+])
+def test_merge_lse_equals_one_softmax_over_union(grid, tile, window, shift, pool):
+    # merging the two branch results by their LSEs must equal attention over
+    # the explicit union of window keys and pooled keys, built row by row
+    N = int(np.prod(grid))
+    q, k, v = randn(100, N, 8), randn(101, N, 8), randn(102, N, 8)
+    kp, vp = R.pool_ref(k, grid, pool), R.pool_ref(v, grid, pool)
+    ol, ll = R.sta_ref(q, k, v, grid, tile, window, shift)
+    og, lg = R.global_ref(q, kp, vp)
+    om, lm = R.merge_lse_ref(ol, ll, og, lg)
+    ou, lu = R.union_attention_ref(q, k, v, grid, tile, window, shift, kp, vp)
+    np.testing.assert_allclose(om, ou, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lm, lu, rtol=0, atol=1e-12)
+
+
+def test_merge_lse_limits_and_invariance():
+    oa, ob = randn(110, 5, 6), randn(111, 5, 6)
+    la, lb = randn(112, 5) * 4, randn(113, 5) * 4
+    # an empty second branch (LSE -inf) leaves the first unchanged
+    o, l = R.merge_lse_ref(oa, la, ob, np.full(5, -np.inf))
+    np.testing.assert_allclose(o, oa, atol=1e-15)
+    np.testing.assert_allclose(l, la, atol=1e-15)
+    # equal partition functions average the outputs and add log 2
+    o, l = R.merge_lse_ref(oa, la, ob, la)
+    np.testing.assert_allclose(o, 0.5 * (oa + ob), atol=1e-15)
+    np.testing.assert_allclose(l, la + math.log(2.0), atol=1e-14)
+    # a common offset of both LSEs moves the merged LSE and nothing else
+    o1, l1 = R.merge_lse_ref(oa, la, ob, lb)
+    o2, l2 = R.merge_lse_ref(oa, la + 7.5, ob, lb + 7.5)
+    np.testing.assert_allclose(o2, o1, atol=1e-14)
+    np.testing.assert_allclose(l2, l1 + 7.5, atol=1e-13)
+    # symmetric in the two branches
+    o3, l3 = R.merge_lse_ref(ob, lb, oa, la)
+    np.testing.assert_allclose(o3, o1, atol=1e-15)
+    np.testing.assert_allclose(l3, l1, atol=1e-15)
+
+
+def test_union_attention_two_key_closed_form():
+    # grid 1x1x2, unit tiles, window 1: each query's local key is itself; one
+    # pooled key (cell 1x2) is the mean of the two keys.  Logits chosen so the
+    # weights are 1/4 and 3/4 exactly for query 0.
+    q = np.array([[1.0, 0.0], [0.0, 1.0]])
+    k = np.array([[0.0, 2.0], [2.0 * math.log(3.0), -2.0]])   # pooled key = (ln 3, 0)
+    v = np.array([[4.0, -8.0], [6.0, 2.0]])                     # pooled value = (5, -3)
+    kp, vp = R.pool_ref(k, (1, 1, 2), (1, 2)), R.pool_ref(v, (1, 1, 2), (1, 2))
+    np.testing.assert_allclose(kp, [[math.log(3.0), 0.0]], atol=1e-15)
+    o, lse = R.union_attention_ref(q, k, v, (1, 1, 2), (1, 1, 1), (1, 1, 1), (0, 0, 0), kp, vp, scale=1.0)
+    # query 0: logits 0 (own key) and ln 3 (pooled)
+    np.testing.assert_allclose(o[0], [0.25 * 4 + 0.75 * 5, 0.25 * -8 + 0.75 * -3], atol=1e-14)
+    np.testing.assert_allclose(lse[0], math.log(4.0), atol=1e-14)
+    # query 1: logits -2 (own key) and 0 (pooled)
+    w = 1.0 / (1.0 + math.exp(-2.0))
+    np.testing.assert_allclose(o[1], [(1 - w) * 6 + w * 5, (1 - w) * 2 + w * -3], atol=1e-14)
+    np.testing.assert_allclose(lse[1], math.log(math.exp(-2.0) + 1.0), atol=1e-14)
+
+
 # ---------------------------------------------------------------- effective work
 @pytest.mark.parametrize("grid,tile,window,shift", SPARSE_CASES[1:] + FULL_WINDOW_CASES)
 def test_pair_count_brute_force(grid, tile, window, shift):
