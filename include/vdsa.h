@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define VDSA_ABI_VERSION 1
+#define VDSA_ABI_VERSION 2
 
 typedef enum {
   VDSA_OK = 0,
@@ -166,6 +166,78 @@ vdsa_status dual_branch_merge(const vdsa_problem* prob,
                               const void* o_global, const vdsa_strides* global_strides,
                               const float* w_local, const float* w_global,
                               void* out, const vdsa_strides* out_strides, void* stream);
+
+/*
+ * How two branch outputs are combined (UltraGen section 4.1 "Time-Aware
+ * Global-Local Attention" fuses the local and the global latent):
+ *   VDSA_MERGE_GATED: out = w_local[h] * o_local + w_global[h] * o_global, the
+ *                     per-head gate of dual_branch_merge;
+ *   VDSA_MERGE_LSE:   one softmax over the union of both branches' key sets,
+ *                     from their log-sum-exps (natural log):
+ *                       a = 1 / (1 + exp(lse_global - lse_local)),
+ *                       out = a * o_local + (1 - a) * o_global,
+ *                       lse = log(exp(lse_local) + exp(lse_global)).
+ *                     Exact when the key sets are disjoint (window tokens vs
+ *                     pooled tokens).
+ */
+typedef enum {
+  VDSA_MERGE_GATED = 0,
+  VDSA_MERGE_LSE = 1
+} vdsa_merge_mode;
+
+/*
+ * dual_branch_merge_lse - the VDSA_MERGE_LSE combination of two attention
+ * outputs given their log-sum-exps.
+ *
+ *   lse_local, lse_global : device fp32 [batch, heads, N] contiguous (as
+ *                           written by sta_attn_fwd / global_pooled_attn_fwd).
+ *   out                   : may be exactly o_local or exactly o_global (same
+ *                           pointer and strides); must not otherwise overlap them.
+ *   lse_out               : nullable, [batch, heads, N] fp32 contiguous; may be
+ *                           exactly lse_local or lse_global; must not otherwise
+ *                           overlap any argument.
+ * Errors: VDSA_ERR_NULL, _SHAPE, _UNSUPPORTED, _ALIGN, _ALIAS, _HIP.
+ */
+vdsa_status dual_branch_merge_lse(const vdsa_problem* prob,
+                                  const void* o_local, const vdsa_strides* local_strides,
+                                  const float* lse_local,
+                                  const void* o_global, const vdsa_strides* global_strides,
+                                  const float* lse_global,
+                                  void* out, const vdsa_strides* out_strides, float* lse_out,
+                                  void* stream);
+
+/*
+ * global_pooled_attn_merge_fwd - global_pooled_attn_fwd with the merge of
+ * `mode` fused into the attention epilogue: the global branch's output never
+ * reaches memory; each query row reads o_local (and lse_local) and writes the
+ * merged row, saving the separate merge pass (one read and one write of a
+ * [batch, heads, N, head_dim] tensor).
+ *
+ *   mode       : VDSA_MERGE_GATED (w_global required, w_local nullable =>
+ *                ones; lse_local ignored) or VDSA_MERGE_LSE (lse_local
+ *                required, w_* ignored).
+ *   o_local    : the local branch output, [batch, heads, N, head_dim] in the
+ *                problem dtype.
+ *   lse_local  : device fp32 [batch, heads, N] contiguous.
+ *   out        : may be exactly o_local (same pointer and strides); must not
+ *                otherwise overlap o_local, and must not overlap q, k, v or
+ *                the workspace.
+ *   lse_out    : nullable, [batch, heads, N] fp32 contiguous: the merged LSE
+ *                in LSE mode, the global branch's LSE in GATED mode.  May be
+ *                exactly lse_local.
+ *   workspace  : as global_pooled_attn_fwd (global_pooled_attn_workspace_size).
+ * Errors: as global_pooled_attn_fwd.
+ */
+vdsa_status global_pooled_attn_merge_fwd(const vdsa_problem* prob, const int32_t pool_hw[2],
+                                         const void* q, const vdsa_strides* q_strides,
+                                         const void* k, const vdsa_strides* k_strides,
+                                         const void* v, const vdsa_strides* v_strides,
+                                         vdsa_merge_mode mode,
+                                         const void* o_local, const vdsa_strides* local_strides,
+                                         const float* lse_local,
+                                         const float* w_local, const float* w_global,
+                                         void* out, const vdsa_strides* out_strides, float* lse_out,
+                                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * kv_avgpool_fwd - the pooling step of global_pooled_attn_fwd on one tensor,

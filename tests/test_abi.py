@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert L.abi_version() == 1
+    assert L.abi_version() == 2
     for code in L.STATUS_NAMES:
         assert L.lib().vdsa_status_string(code)
 
@@ -151,6 +151,51 @@ def test_merge_checks():
     assert m(Q, K, None, WS, K) == L.STATUS["VDSA_ERR_ALIAS"]          # out == o_global
     assert m(Q, K, None, WS, Q + 512) == L.STATUS["VDSA_ERR_ALIAS"]    # partial overlap with o_local
     assert m(Q, K, None, WS + 2, O) == L.STATUS["VDSA_ERR_ALIGN"]
+
+
+def test_merge_lse_checks():
+    p = prob()
+    d = st(p)
+    LSE2 = WS   # a second LSE array
+    m = lambda a, la, g, lg, o, lo: L.lib().dual_branch_merge_lse(
+        ctypes.byref(p), a, ctypes.byref(d), la, g, ctypes.byref(d), lg, o, ctypes.byref(d), lo, None)
+    assert m(Q, None, K, LSE2, O, None) == L.STATUS["VDSA_ERR_NULL"]
+    assert m(Q, LSE, K, None, O, None) == L.STATUS["VDSA_ERR_NULL"]
+    assert m(Q, LSE + 2, K, LSE2, O, None) == L.STATUS["VDSA_ERR_ALIGN"]
+    assert m(Q, LSE, K, LSE2, Q + 512, None) == L.STATUS["VDSA_ERR_ALIAS"]    # partial overlap with o_local
+    assert m(Q, LSE, K, LSE2, K + 256, None) == L.STATUS["VDSA_ERR_ALIAS"]    # partial overlap with o_global
+    assert m(Q, LSE, K, LSE2, O, O + 64) == L.STATUS["VDSA_ERR_ALIAS"]        # lse_out inside out
+    assert m(Q, LSE, K, LSE2, O, LSE + 4) == L.STATUS["VDSA_ERR_ALIAS"]       # lse_out straddles lse_local
+    assert m(Q, LSE, K, LSE2, O, LSE2 + 8) == L.STATUS["VDSA_ERR_ALIAS"]      # lse_out straddles lse_global
+    assert m(Q, LSE, K, LSE2, LSE, None) == L.STATUS["VDSA_ERR_ALIAS"]        # out over lse_local
+
+
+def test_fused_global_merge_checks():
+    p = prob()
+    d = st(p)
+    pool = (ctypes.c_int32 * 2)(4, 4)
+    n = ctypes.c_size_t()
+    assert L.lib().global_pooled_attn_workspace_size(ctypes.byref(p), pool, ctypes.byref(n)) == 0
+    OL, GATE = 0x80000000, 0x90000000
+
+    def f(mode, ol=OL, lse_l=None, wl=None, wg=GATE, out=O, lse_out=None, ws=WS, wsb=None):
+        return L.lib().global_pooled_attn_merge_fwd(
+            ctypes.byref(p), pool, Q, ctypes.byref(d), K, ctypes.byref(d), V, ctypes.byref(d), mode,
+            ol, ctypes.byref(d), lse_l, wl, wg, out, ctypes.byref(d), lse_out, ws,
+            n.value if wsb is None else wsb, None)
+    assert f(7) == L.STATUS["VDSA_ERR_UNSUPPORTED"]
+    assert f(-1) == L.STATUS["VDSA_ERR_UNSUPPORTED"]
+    assert f(L.VDSA_MERGE_GATED, wg=None) == L.STATUS["VDSA_ERR_NULL"]
+    assert f(L.VDSA_MERGE_GATED, wg=GATE + 2) == L.STATUS["VDSA_ERR_ALIGN"]
+    assert f(L.VDSA_MERGE_LSE, lse_l=None) == L.STATUS["VDSA_ERR_NULL"]
+    assert f(L.VDSA_MERGE_LSE, lse_l=LSE + 1) == L.STATUS["VDSA_ERR_ALIGN"]
+    assert f(L.VDSA_MERGE_GATED, ol=None) == L.STATUS["VDSA_ERR_NULL"]
+    assert f(L.VDSA_MERGE_GATED, out=OL + 512) == L.STATUS["VDSA_ERR_ALIAS"]       # out straddles o_local
+    assert f(L.VDSA_MERGE_GATED, ol=WS + 256) == L.STATUS["VDSA_ERR_ALIAS"]        # o_local in the workspace
+    assert f(L.VDSA_MERGE_GATED, out=Q) == L.STATUS["VDSA_ERR_ALIAS"]              # out over q
+    assert f(L.VDSA_MERGE_LSE, lse_l=LSE, lse_out=LSE + 4) == L.STATUS["VDSA_ERR_ALIAS"]
+    assert f(L.VDSA_MERGE_LSE, lse_l=O + 64) == L.STATUS["VDSA_ERR_ALIAS"]         # lse_local inside out
+    assert f(L.VDSA_MERGE_GATED, wsb=n.value - 1) == L.STATUS["VDSA_ERR_WORKSPACE"]
 
 
 FLOP_CASES = [

@@ -2,14 +2,18 @@
 
 Python face of libvdsa.so: the three calls of the hot path
 (``sta_attn_fwd``, ``global_pooled_attn_fwd``, ``dual_branch_merge``), the
-pooling step alone (``kv_avgpool_fwd``) and the effective-work counters.
+exact log-sum-exp merge (``dual_branch_merge_lse``), the global branch with
+either merge fused into it (``global_pooled_attn_merge_fwd``), the pooling
+step alone (``kv_avgpool_fwd``) and the effective-work counters.
 """
 from ._lib import (  # noqa: F401
     VdsaError,
     abi_version,
     dual_branch_merge,
+    dual_branch_merge_lse,
     global_flops,
     global_pooled_attn_fwd,
+    global_pooled_attn_merge_fwd,
     global_pooled_attn_workspace_size,
     kv_avgpool_fwd,
     lib,

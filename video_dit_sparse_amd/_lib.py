@@ -27,9 +27,12 @@ STATUS = {v: k for k, v in STATUS_NAMES.items()}
 # every symbol include/vdsa.h declares
 EXPORTED = [
     "sta_attn_fwd", "global_pooled_attn_workspace_size", "global_pooled_attn_fwd",
-    "dual_branch_merge", "kv_avgpool_fwd", "vdsa_sta_flops", "vdsa_global_flops",
+    "dual_branch_merge", "dual_branch_merge_lse", "global_pooled_attn_merge_fwd",
+    "kv_avgpool_fwd", "vdsa_sta_flops", "vdsa_global_flops",
     "vdsa_status_string", "vdsa_last_error", "vdsa_abi_version",
 ]
+VDSA_MERGE_GATED, VDSA_MERGE_LSE = 0, 1
+MERGE_MODES = {"gated": VDSA_MERGE_GATED, "lse": VDSA_MERGE_LSE}
 
 
 class Problem(ctypes.Structure):
@@ -71,6 +74,9 @@ def lib() -> ctypes.CDLL:
     L.global_pooled_attn_workspace_size.argtypes = [P, i32p, ctypes.POINTER(ctypes.c_size_t)]
     L.global_pooled_attn_fwd.argtypes = [P, i32p, vp, S, vp, S, vp, S, vp, S, fp, vp, ctypes.c_size_t, vp]
     L.dual_branch_merge.argtypes = [P, vp, S, vp, S, fp, fp, vp, S, vp]
+    L.dual_branch_merge_lse.argtypes = [P, vp, S, fp, vp, S, fp, vp, S, fp, vp]
+    L.global_pooled_attn_merge_fwd.argtypes = [P, i32p, vp, S, vp, S, vp, S, ctypes.c_int, vp, S, fp, fp, fp,
+                                               vp, S, fp, vp, ctypes.c_size_t, vp]
     L.kv_avgpool_fwd.argtypes = [P, i32p, vp, S, vp, S, vp]
     L.vdsa_sta_flops.argtypes = [P, C, ctypes.POINTER(ctypes.c_double)]
     L.vdsa_global_flops.argtypes = [P, i32p, ctypes.POINTER(ctypes.c_double)]
@@ -222,6 +228,67 @@ def dual_branch_merge(o_local, o_global, w_global, w_local=None, out=None, strea
                                   w_local.data_ptr() if w_local is not None else None, w_global.data_ptr(),
                                   o.data_ptr(), ctypes.byref(_strides(o)), _stream(stream)))
     return o
+
+
+def _lse_arg(t, shape, name):
+    torch = _torch()
+    if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor of shape {tuple(shape)}")
+    return t.data_ptr()
+
+
+def dual_branch_merge_lse(o_local, lse_local, o_global, lse_global, out=None, lse_out=None,
+                          return_lse=False, stream=None):
+    """One softmax over the union of both branches' keys, from their LSEs
+    (``dual_branch_merge_lse``).  ``out=o_local`` merges in place.  Returns O
+    (and the merged LSE if requested)."""
+    torch = _torch()
+    _same(o_local, o_global)
+    B, Hh, N, D = o_local.shape
+    prob = make_problem(B, Hh, D, (1, 1, N), _dtype_code(o_local), 1.0)
+    o = torch.empty_like(o_local, memory_format=torch.contiguous_format) if out is None else out
+    if lse_out is None and return_lse:
+        lse_out = torch.empty((B, Hh, N), dtype=torch.float32, device=o_local.device)
+    check(lib().dual_branch_merge_lse(
+        ctypes.byref(prob), o_local.data_ptr(), ctypes.byref(_strides(o_local)), _lse_arg(lse_local, (B, Hh, N), "lse_local"),
+        o_global.data_ptr(), ctypes.byref(_strides(o_global)), _lse_arg(lse_global, (B, Hh, N), "lse_global"),
+        o.data_ptr(), ctypes.byref(_strides(o)),
+        _lse_arg(lse_out, (B, Hh, N), "lse_out") if lse_out is not None else None, _stream(stream)))
+    return (o, lse_out) if (return_lse or lse_out is not None) else o
+
+
+def global_pooled_attn_merge_fwd(q, k, v, grid, pool_hw, o_local, mode="gated", lse_local=None,
+                                 w_global=None, w_local=None, scale=None, out=None, lse_out=None,
+                                 return_lse=False, workspace=None, stream=None):
+    """Global branch with the merge fused into its epilogue
+    (``global_pooled_attn_merge_fwd``): ``mode`` "gated" (w_global, optional
+    w_local) or "lse" (lse_local).  ``out=o_local`` merges in place.  Returns
+    the merged O (and lse_out if requested)."""
+    torch = _torch()
+    _same(q, k, v, o_local)
+    B, Hh, N, D = q.shape
+    prob = _problem_for(q, grid, scale)
+    need = ctypes.c_size_t()
+    check(lib().global_pooled_attn_workspace_size(ctypes.byref(prob), _pool(pool_hw), ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    if lse_out is None and return_lse:
+        lse_out = torch.empty((B, Hh, N), dtype=torch.float32, device=q.device)
+    for w in (w_global, w_local):
+        if w is not None and (w.dtype != torch.float32 or w.numel() != Hh or not w.is_contiguous()):
+            raise ValueError("gates must be contiguous float32 tensors of length heads")
+    check(lib().global_pooled_attn_merge_fwd(
+        ctypes.byref(prob), _pool(pool_hw), q.data_ptr(), ctypes.byref(_strides(q)),
+        k.data_ptr(), ctypes.byref(_strides(k)), v.data_ptr(), ctypes.byref(_strides(v)),
+        MERGE_MODES[mode], o_local.data_ptr(), ctypes.byref(_strides(o_local)),
+        _lse_arg(lse_local, (B, Hh, N), "lse_local") if lse_local is not None else None,
+        w_local.data_ptr() if w_local is not None else None,
+        w_global.data_ptr() if w_global is not None else None,
+        o.data_ptr(), ctypes.byref(_strides(o)),
+        _lse_arg(lse_out, (B, Hh, N), "lse_out") if lse_out is not None else None,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return (o, lse_out) if (return_lse or lse_out is not None) else o
 
 
 def kv_avgpool_fwd(x, grid, pool_hw, out=None, stream=None):

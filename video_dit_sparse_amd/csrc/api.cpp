@@ -245,6 +245,132 @@ vdsa::PoolParams pool_params(const vdsa_problem* p, const int32_t* pool, const v
   return pp;
 }
 
+// [batch, heads, N] fp32 contiguous LSE array: required (or nullable) pointer
+// checks and its byte range.
+vdsa_status check_lse_in(const vdsa_problem* p, const float* lse, const char* name, uintptr_t& lo, uintptr_t& hi) {
+  if (!lse) return fail(VDSA_ERR_NULL, "%s is NULL", name);
+  return check_lse(p, const_cast<float*>(lse), lo, hi) == VDSA_OK ? VDSA_OK
+                                                                   : fail(VDSA_ERR_ALIGN, "%s is not 4-byte aligned", name);
+}
+
+bool same_view(const void* a, const vdsa_strides* sa, const void* b, const vdsa_strides* sb) {
+  return a == b && sa->b == sb->b && sa->h == sb->h && sa->n == sb->n;
+}
+
+// The other branch's output and how it merges into the global branch (the
+// fused form); mode < 0 means no merge.
+struct FusedMerge {
+  int mode = -1;
+  const void* o_local = nullptr;
+  const vdsa_strides* local_strides = nullptr;
+  const float* lse_local = nullptr;
+  const float* w_local = nullptr;
+  const float* w_global = nullptr;
+};
+
+vdsa_status global_attn_impl(const vdsa_problem* prob, const int32_t pool_hw[2], const void* q,
+                             const vdsa_strides* q_strides, const void* k, const vdsa_strides* k_strides,
+                             const void* v, const vdsa_strides* v_strides, void* o, const vdsa_strides* o_strides,
+                             float* lse, void* workspace, size_t workspace_bytes, const FusedMerge& fm,
+                             void* stream) {
+  vdsa_status s;
+  if ((s = check_problem(prob)) != VDSA_OK) return s;
+  if ((s = check_pool(prob, pool_hw)) != VDSA_OK) return s;
+  const int64_t N = n_tokens(prob);
+  const int64_t M = pooled_tokens(prob, pool_hw);
+  View vq{"q", q, q_strides, N}, vk{"k", k, k_strides, N}, vv{"v", v, v_strides, N},
+      vo{fm.mode < 0 ? "o" : "out", o, o_strides, N};
+  if ((s = check_view(prob, vq, false)) != VDSA_OK) return s;
+  if ((s = check_view(prob, vk, false)) != VDSA_OK) return s;
+  if ((s = check_view(prob, vv, false)) != VDSA_OK) return s;
+  if ((s = check_view(prob, vo, true)) != VDSA_OK) return s;
+  uintptr_t l0, l1;
+  if ((s = check_lse(prob, lse, l0, l1)) != VDSA_OK) return s;
+  const size_t need = 2 * pooled_bytes(prob, pool_hw);
+  if (!workspace) return fail(VDSA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (workspace_bytes < need)
+    return fail(VDSA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  if ((uintptr_t)workspace % 16 != 0) return fail(VDSA_ERR_ALIGN, "workspace is not 16-byte aligned");
+  const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + need;
+  for (const View* in : {&vq, &vk, &vv})
+    if (overlaps(vo.lo, vo.hi, in->lo, in->hi)) return fail(VDSA_ERR_ALIAS, "%s overlaps %s", vo.name, in->name);
+  for (const View* in : {&vq, &vk, &vv, &vo})
+    if (overlaps(w0, w1, in->lo, in->hi)) return fail(VDSA_ERR_ALIAS, "workspace overlaps %s", in->name);
+  if (lse) {
+    for (const View* in : {&vq, &vk, &vv, &vo})
+      if (overlaps(l0, l1, in->lo, in->hi)) return fail(VDSA_ERR_ALIAS, "lse overlaps %s", in->name);
+    if (overlaps(l0, l1, w0, w1)) return fail(VDSA_ERR_ALIAS, "lse overlaps workspace");
+  }
+
+  vdsa::BoxAttnParams bp{};
+  if (fm.mode >= 0) {
+    if (fm.mode != VDSA_MERGE_GATED && fm.mode != VDSA_MERGE_LSE)
+      return fail(VDSA_ERR_UNSUPPORTED, "unknown merge mode %d", fm.mode);
+    View vl{"o_local", fm.o_local, fm.local_strides, N};
+    if ((s = check_view(prob, vl, false)) != VDSA_OK) return s;
+    if (!same_view(o, o_strides, fm.o_local, fm.local_strides) && overlaps(vo.lo, vo.hi, vl.lo, vl.hi))
+      return fail(VDSA_ERR_ALIAS, "out overlaps o_local");
+    if (overlaps(w0, w1, vl.lo, vl.hi)) return fail(VDSA_ERR_ALIAS, "workspace overlaps o_local");
+    if (lse && overlaps(l0, l1, vl.lo, vl.hi)) return fail(VDSA_ERR_ALIAS, "lse_out overlaps o_local");
+    if (fm.mode == VDSA_MERGE_LSE) {
+      uintptr_t a0, a1;
+      if ((s = check_lse_in(prob, fm.lse_local, "lse_local", a0, a1)) != VDSA_OK) return s;
+      if (overlaps(vo.lo, vo.hi, a0, a1)) return fail(VDSA_ERR_ALIAS, "out overlaps lse_local");
+      if (overlaps(w0, w1, a0, a1)) return fail(VDSA_ERR_ALIAS, "workspace overlaps lse_local");
+      if (lse && lse != fm.lse_local && overlaps(l0, l1, a0, a1))
+        return fail(VDSA_ERR_ALIAS, "lse_out overlaps lse_local");
+      bp.merge = vdsa::MERGE_LSE;
+      bp.lse_l = fm.lse_local;
+    } else {
+      if (!fm.w_global) return fail(VDSA_ERR_NULL, "w_global is NULL");
+      if ((uintptr_t)fm.w_global % 4 != 0 || (fm.w_local && (uintptr_t)fm.w_local % 4 != 0))
+        return fail(VDSA_ERR_ALIGN, "gate pointers must be 4-byte aligned");
+      for (const float* w : {fm.w_global, fm.w_local}) {
+        if (!w) continue;
+        const uintptr_t a0 = (uintptr_t)w, a1 = a0 + 4 * (uintptr_t)prob->heads;
+        if (overlaps(vo.lo, vo.hi, a0, a1) || overlaps(w0, w1, a0, a1) || (lse && overlaps(l0, l1, a0, a1)))
+          return fail(VDSA_ERR_ALIAS, "a gate array overlaps an output or the workspace");
+      }
+      bp.merge = vdsa::MERGE_GATED;
+      bp.w_l = fm.w_local;
+      bp.w_g = fm.w_global;
+    }
+    bp.ol = fm.o_local;
+    bp.ol_sb = fm.local_strides->b;
+    bp.ol_sh = fm.local_strides->h;
+    bp.ol_sn = fm.local_strides->n;
+  }
+
+  // pooled K then pooled V, each [batch, heads, M, head_dim] contiguous
+  const size_t half = pooled_bytes(prob, pool_hw);
+  void* kp = workspace;
+  void* vp = (char*)workspace + half;
+  vdsa_strides ps{(int64_t)prob->heads * M * prob->head_dim, M * prob->head_dim, prob->head_dim};
+  hipError_t e = vdsa::launch_avgpool(pool_params(prob, pool_hw, k, k_strides, kp, &ps), prob->dtype == VDSA_BF16,
+                                      (hipStream_t)stream);
+  if (e == hipSuccess)
+    e = vdsa::launch_avgpool(pool_params(prob, pool_hw, v, v_strides, vp, &ps), prob->dtype == VDSA_BF16,
+                             (hipStream_t)stream);
+  if (e != hipSuccess) return fail(VDSA_ERR_HIP, "pooling launch failed: %s", hipGetErrorString(e));
+
+  View vkp{"k_pooled", kp, &ps, M}, vvp{"v_pooled", vp, &ps, M};
+  set_qkvo(bp, vq, vkp, vvp, vo);
+  bp.lse = lse;
+  bp.batch = prob->batch;
+  bp.heads = prob->heads;
+  bp.qT = prob->grid_t; bp.qH = prob->grid_h; bp.qW = prob->grid_w;
+  // one query tile covering the whole grid; every query sees every pooled key
+  bp.bT = bp.qT; bp.bH = bp.qH; bp.bW = bp.qW;
+  bp.sT = bp.sH = bp.sW = 0;
+  bp.nT = bp.nH = bp.nW = 1;
+  bp.rT = bp.rH = bp.rW = 0;
+  bp.kT = prob->grid_t;
+  bp.kH = (prob->grid_h + pool_hw[0] - 1) / pool_hw[0];
+  bp.kW = (prob->grid_w + pool_hw[1] - 1) / pool_hw[1];
+  bp.dense_keys = 1;
+  return launch_attn(prob, bp, (hipStream_t)stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -338,63 +464,27 @@ vdsa_status global_pooled_attn_fwd(const vdsa_problem* prob, const int32_t pool_
                                    const void* v, const vdsa_strides* v_strides, void* o,
                                    const vdsa_strides* o_strides, float* lse, void* workspace,
                                    size_t workspace_bytes, void* stream) {
-  vdsa_status s;
-  if ((s = check_problem(prob)) != VDSA_OK) return s;
-  if ((s = check_pool(prob, pool_hw)) != VDSA_OK) return s;
-  const int64_t N = n_tokens(prob);
-  const int64_t M = pooled_tokens(prob, pool_hw);
-  View vq{"q", q, q_strides, N}, vk{"k", k, k_strides, N}, vv{"v", v, v_strides, N}, vo{"o", o, o_strides, N};
-  if ((s = check_view(prob, vq, false)) != VDSA_OK) return s;
-  if ((s = check_view(prob, vk, false)) != VDSA_OK) return s;
-  if ((s = check_view(prob, vv, false)) != VDSA_OK) return s;
-  if ((s = check_view(prob, vo, true)) != VDSA_OK) return s;
-  uintptr_t l0, l1;
-  if ((s = check_lse(prob, lse, l0, l1)) != VDSA_OK) return s;
-  const size_t need = 2 * pooled_bytes(prob, pool_hw);
-  if (!workspace) return fail(VDSA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
-  if (workspace_bytes < need)
-    return fail(VDSA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
-  if ((uintptr_t)workspace % 16 != 0) return fail(VDSA_ERR_ALIGN, "workspace is not 16-byte aligned");
-  const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + need;
-  for (const View* in : {&vq, &vk, &vv})
-    if (overlaps(vo.lo, vo.hi, in->lo, in->hi)) return fail(VDSA_ERR_ALIAS, "o overlaps %s", in->name);
-  for (const View* in : {&vq, &vk, &vv, &vo})
-    if (overlaps(w0, w1, in->lo, in->hi)) return fail(VDSA_ERR_ALIAS, "workspace overlaps %s", in->name);
-  if (lse) {
-    for (const View* in : {&vq, &vk, &vv, &vo})
-      if (overlaps(l0, l1, in->lo, in->hi)) return fail(VDSA_ERR_ALIAS, "lse overlaps %s", in->name);
-    if (overlaps(l0, l1, w0, w1)) return fail(VDSA_ERR_ALIAS, "lse overlaps workspace");
-  }
+  return global_attn_impl(prob, pool_hw, q, q_strides, k, k_strides, v, v_strides, o, o_strides, lse, workspace,
+                          workspace_bytes, FusedMerge{}, stream);
+}
 
-  // pooled K then pooled V, each [batch, heads, M, head_dim] contiguous
-  const size_t half = pooled_bytes(prob, pool_hw);
-  void* kp = workspace;
-  void* vp = (char*)workspace + half;
-  vdsa_strides ps{(int64_t)prob->heads * M * prob->head_dim, M * prob->head_dim, prob->head_dim};
-  hipError_t e = vdsa::launch_avgpool(pool_params(prob, pool_hw, k, k_strides, kp, &ps), prob->dtype == VDSA_BF16,
-                                      (hipStream_t)stream);
-  if (e == hipSuccess)
-    e = vdsa::launch_avgpool(pool_params(prob, pool_hw, v, v_strides, vp, &ps), prob->dtype == VDSA_BF16,
-                             (hipStream_t)stream);
-  if (e != hipSuccess) return fail(VDSA_ERR_HIP, "pooling launch failed: %s", hipGetErrorString(e));
-
-  vdsa::BoxAttnParams bp{};
-  View vkp{"k_pooled", kp, &ps, M}, vvp{"v_pooled", vp, &ps, M};
-  set_qkvo(bp, vq, vkp, vvp, vo);
-  bp.lse = lse;
-  bp.batch = prob->batch;
-  bp.heads = prob->heads;
-  bp.qT = prob->grid_t; bp.qH = prob->grid_h; bp.qW = prob->grid_w;
-  // one query tile covering the whole grid; every query sees every pooled key
-  bp.bT = bp.qT; bp.bH = bp.qH; bp.bW = bp.qW;
-  bp.sT = bp.sH = bp.sW = 0;
-  bp.nT = bp.nH = bp.nW = 1;
-  bp.rT = bp.rH = bp.rW = 0;
-  bp.kT = prob->grid_t;
-  bp.kH = (prob->grid_h + pool_hw[0] - 1) / pool_hw[0];
-  bp.kW = (prob->grid_w + pool_hw[1] - 1) / pool_hw[1];
-  bp.dense_keys = 1;
-  return launch_attn(prob, bp, (hipStream_t)stream);
+vdsa_status global_pooled_attn_merge_fwd(const vdsa_problem* prob, const int32_t pool_hw[2], const void* q,
+                                         const vdsa_strides* q_strides, const void* k, const vdsa_strides* k_strides,
+                                         const void* v, const vdsa_strides* v_strides, vdsa_merge_mode mode,
+                                         const void* o_local, const vdsa_strides* local_strides,
+                                         const float* lse_local, const float* w_local, const float* w_global,
+                                         void* out, const vdsa_strides* out_strides, float* lse_out,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  FusedMerge fm;
+  fm.mode = (int)mode;
+  fm.o_local = o_local;
+  fm.local_strides = local_strides;
+  fm.lse_local = lse_local;
+  fm.w_local = w_local;
+  fm.w_global = w_global;
+  if (fm.mode < 0) return fail(VDSA_ERR_UNSUPPORTED, "unknown merge mode %d", fm.mode);
+  return global_attn_impl(prob, pool_hw, q, q_strides, k, k_strides, v, v_strides, out, out_strides, lse_out,
+                          workspace, workspace_bytes, fm, stream);
 }
 
 vdsa_status dual_branch_merge(const vdsa_problem* prob, const void* o_local, const vdsa_strides* local_strides,
@@ -426,6 +516,54 @@ vdsa_status dual_branch_merge(const vdsa_problem* prob, const void* o_local, con
   mp.g = o_global;
   mp.w_a = w_local;
   mp.w_g = w_global;
+  mp.out = out;
+  mp.a_sb = local_strides->b; mp.a_sh = local_strides->h; mp.a_sn = local_strides->n;
+  mp.g_sb = global_strides->b; mp.g_sh = global_strides->h; mp.g_sn = global_strides->n;
+  mp.o_sb = out_strides->b; mp.o_sh = out_strides->h; mp.o_sn = out_strides->n;
+  mp.batch = prob->batch;
+  mp.heads = prob->heads;
+  mp.head_dim = prob->head_dim;
+  mp.n_tokens = N;
+  hipError_t e = vdsa::launch_merge(mp, prob->dtype == VDSA_BF16, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(VDSA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+vdsa_status dual_branch_merge_lse(const vdsa_problem* prob, const void* o_local, const vdsa_strides* local_strides,
+                                  const float* lse_local, const void* o_global, const vdsa_strides* global_strides,
+                                  const float* lse_global, void* out, const vdsa_strides* out_strides, float* lse_out,
+                                  void* stream) {
+  vdsa_status s;
+  if ((s = check_problem(prob)) != VDSA_OK) return s;
+  const int64_t N = n_tokens(prob);
+  View va{"o_local", o_local, local_strides, N}, vg{"o_global", o_global, global_strides, N},
+      vo{"out", out, out_strides, N};
+  if ((s = check_view(prob, va, false)) != VDSA_OK) return s;
+  if ((s = check_view(prob, vg, false)) != VDSA_OK) return s;
+  if ((s = check_view(prob, vo, true)) != VDSA_OK) return s;
+  uintptr_t la0, la1, lg0, lg1, lo0, lo1;
+  if ((s = check_lse_in(prob, lse_local, "lse_local", la0, la1)) != VDSA_OK) return s;
+  if ((s = check_lse_in(prob, lse_global, "lse_global", lg0, lg1)) != VDSA_OK) return s;
+  if ((s = check_lse(prob, lse_out, lo0, lo1)) != VDSA_OK) return s;
+  if (!same_view(out, out_strides, o_local, local_strides) && overlaps(vo.lo, vo.hi, va.lo, va.hi))
+    return fail(VDSA_ERR_ALIAS, "out overlaps o_local");
+  if (!same_view(out, out_strides, o_global, global_strides) && overlaps(vo.lo, vo.hi, vg.lo, vg.hi))
+    return fail(VDSA_ERR_ALIAS, "out overlaps o_global");
+  if (overlaps(vo.lo, vo.hi, la0, la1)) return fail(VDSA_ERR_ALIAS, "out overlaps lse_local");
+  if (overlaps(vo.lo, vo.hi, lg0, lg1)) return fail(VDSA_ERR_ALIAS, "out overlaps lse_global");
+  if (lse_out) {
+    if (lse_out != lse_local && overlaps(lo0, lo1, la0, la1)) return fail(VDSA_ERR_ALIAS, "lse_out overlaps lse_local");
+    if (lse_out != lse_global && overlaps(lo0, lo1, lg0, lg1))
+      return fail(VDSA_ERR_ALIAS, "lse_out overlaps lse_global");
+    for (const View* in : {&va, &vg, &vo})
+      if (overlaps(lo0, lo1, in->lo, in->hi)) return fail(VDSA_ERR_ALIAS, "lse_out overlaps %s", in->name);
+  }
+  vdsa::MergeParams mp{};
+  mp.a = o_local;
+  mp.g = o_global;
+  mp.lse_a = lse_local;
+  mp.lse_g = lse_global;
+  mp.lse_out = lse_out;
   mp.out = out;
   mp.a_sb = local_strides->b; mp.a_sh = local_strides->h; mp.a_sn = local_strides->n;
   mp.g_sb = global_strides->b; mp.g_sh = global_strides->h; mp.g_sn = global_strides->n;

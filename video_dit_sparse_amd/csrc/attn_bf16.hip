@@ -111,7 +111,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
   const uint32_t vrange = ((uint32_t)(p.kT * p.kH * p.kW) - 1u) * 2u * (uint32_t)p.v_sn + 2u * HD;
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, (int)krange, BUF_FLAGS);
   const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vp, 0, (int)vrange, BUF_FLAGS);
-  char* __restrict__ op = (char*)p.o + 2 * (b * p.o_sb + h * p.o_sh);
+  char* op = (char*)p.o + 2 * (b * p.o_sb + h * p.o_sh);
   const uint32_t q_row = 2u * (uint32_t)p.q_sn, k_row = 2u * (uint32_t)p.k_sn;
   const uint32_t v_row = 2u * (uint32_t)p.v_sn, o_row = 2u * (uint32_t)p.o_sn;
 
@@ -308,23 +308,45 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
   if (last_partial) process(nkb - 1, std::true_type{});
 
   // ---- epilogue: normalise and store (lane owns query l32; register v of
-  // block nb holds head_dim index 32*nb + 8*(v/4) + 4*g + v%4)
+  // block nb holds head_dim index 32*nb + 8*(v/4) + 4*g + v%4); with a merge,
+  // the row combines with the other branch's row read at the same positions
   const float l_tot = xhalf_sum(l_run);
   const float inv = 1.f / l_tot;
   if (q_valid) {
+    float lse_row = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+    float wa = 0.f, sc = inv;
+    if (p.merge != MERGE_NONE) {
+      const RowMerge rm = row_merge(p, b, h, qtok, lse_row);
+      wa = rm.wa;
+      sc = rm.wb * inv;
+      lse_row = rm.lse;
+    }
     char* dst = op + qtok * o_row + 8 * g;
+    const char* src = p.merge != MERGE_NONE
+                          ? (const char*)p.ol + 2 * (b * p.ol_sb + h * p.ol_sh) + qtok * (2u * (uint32_t)p.ol_sn) + 8 * g
+                          : nullptr;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
+        float f[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = oacc[nb][4 * r4 + e] * sc;
+        if (p.merge != MERGE_NONE) {
+          const u32x2 raw = *(const u32x2*)(src + 64 * nb + 16 * r4);
+          float a[4];
+          bf16x4_to_f32(raw[0], raw[1], a);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) f[e] = fmaf(wa, a[e], f[e]);
+        }
         bf16x4 ov;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(oacc[nb][4 * r4 + e] * inv);
+        for (int e = 0; e < 4; ++e) ov[e] = (__bf16)f[e];
         *(u32x2*)(dst + 64 * nb + 16 * r4) = __builtin_bit_cast(u32x2, ov);
       }
     if (p.lse != nullptr && g == 0) {
       const int64_t N = (int64_t)p.qT * p.qH * p.qW;
-      p.lse[((int64_t)b * p.heads + h) * N + qtok] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+      p.lse[((int64_t)b * p.heads + h) * N + qtok] = lse_row;
     }
   }
 }

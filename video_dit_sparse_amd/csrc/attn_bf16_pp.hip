@@ -161,7 +161,7 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
   const uint32_t vrange = (nkeys - 1u) * 2u * (uint32_t)p.v_sn + 2u * HD;
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, (int)krange, BUF_FLAGS);
   const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vp, 0, (int)vrange, BUF_FLAGS);
-  char* __restrict__ op = (char*)p.o + 2 * (b * p.o_sb + h * p.o_sh);
+  char* op = (char*)p.o + 2 * (b * p.o_sb + h * p.o_sh);
   const uint32_t q_row = 2u * (uint32_t)p.q_sn, k_row = 2u * (uint32_t)p.k_sn;
   const uint32_t v_row = 2u * (uint32_t)p.v_sn, o_row = 2u * (uint32_t)p.o_sn;
 
@@ -415,24 +415,45 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
   __builtin_amdgcn_s_setprio(0);
   if (!grp_b) phase_barrier();
 
-  // ---- epilogue: O^T register v of tile (dt, qt) is head_dim 16dt + 4G + v
+  // ---- epilogue: O^T register v of tile (dt, qt) is head_dim 16dt + 4G + v;
+  // with a merge, each row combines with the other branch's row (read at the
+  // positions this lane writes, so out may be that tensor itself).
+  const char* olp = p.merge != MERGE_NONE ? (const char*)p.ol + 2 * (b * p.ol_sb + h * p.ol_sh) : nullptr;
+  const uint32_t ol_row = 2u * (uint32_t)p.ol_sn;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const float l_tot = lacc[qt][0];
     const float inv = 1.f / l_tot;
     if (q_valid[qt]) {
+      float lse_row = (m_run[qt] + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+      float wa = 0.f, sc = inv;
+      if (p.merge != MERGE_NONE) {
+        const RowMerge rm = row_merge(p, b, h, qtok[qt], lse_row);
+        wa = rm.wa;
+        sc = rm.wb * inv;
+        lse_row = rm.lse;
+      }
       char* dst = op + qtok[qt] * o_row + 8 * G;
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) {
+        float f[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) f[v] = oacc[dt][qt][v] * sc;
+        if (p.merge != MERGE_NONE) {
+          const u32x2 raw = *(const u32x2*)(olp + qtok[qt] * ol_row + 8 * G + 32 * dt);
+          float a[4];
+          bf16x4_to_f32(raw[0], raw[1], a);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) f[v] = fmaf(wa, a[v], f[v]);
+        }
         bf16x4 ov;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) ov[v] = (__bf16)(oacc[dt][qt][v] * inv);
+        for (int v = 0; v < 4; ++v) ov[v] = (__bf16)f[v];
         *(u32x2*)(dst + 32 * dt) = __builtin_bit_cast(u32x2, ov);
       }
       if (p.lse != nullptr && G == 0) {
         const int64_t N = (int64_t)p.qT * p.qH * p.qW;
-        p.lse[((int64_t)b * p.heads + h) * N + qtok[qt]] =
-            (m_run[qt] + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+        p.lse[((int64_t)b * p.heads + h) * N + qtok[qt]] = lse_row;
       }
     }
   }

@@ -5,7 +5,7 @@
 // simpler inner loop: 64 queries per workgroup, four lanes per query each
 // owning a quarter of head_dim, keys staged through LDS 32 at a time, and an
 // fp32 online softmax.  This path exists for fp32 inputs; it is not tuned.
-#include "internal.h"
+#include "box_common.h"
 
 namespace vdsa {
 namespace {
@@ -125,11 +125,22 @@ __global__ __launch_bounds__(NTHREADS) void box_attn_f32_kernel(const BoxAttnPar
 
   if (q_valid) {
     const float inv = 1.f / l_run;
+    float lse_row = (m_run + log2f(l_run)) * 0.69314718055994531f;
+    if (p.merge != MERGE_NONE) {
+      // combine with the other branch's row, read at the positions written
+      const RowMerge rm = row_merge(p, b, h, (uint32_t)qtok, lse_row);
+      const float* olp = (const float*)p.ol + b * p.ol_sb + h * p.ol_sh + (int64_t)qtok * p.ol_sn + part * DPL;
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) op[(int64_t)qtok * p.o_sn + part * DPL + i] = o[i] * inv;
+      for (int i = 0; i < DPL; ++i)
+        op[(int64_t)qtok * p.o_sn + part * DPL + i] = fmaf(rm.wa, olp[i], rm.wb * (o[i] * inv));
+      lse_row = rm.lse;
+    } else {
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) op[(int64_t)qtok * p.o_sn + part * DPL + i] = o[i] * inv;
+    }
     if (p.lse != nullptr && part == 0) {
       const int64_t N = (int64_t)p.qT * p.qH * p.qW;
-      p.lse[((int64_t)b * p.heads + h) * N + qtok] = (m_run + log2f(l_run)) * 0.69314718055994531f;
+      p.lse[((int64_t)b * p.heads + h) * N + qtok] = lse_row;
     }
   }
 }

@@ -29,6 +29,41 @@ __device__ __forceinline__ float xrow4_sum(float x) {
   return xhalf_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
 }
 
+// Weights of the epilogue merge for one query row: out = wa * o_other +
+// wb * o_this, where o_this is the kernel's normalised output row and
+// lse_this its log-sum-exp (natural log).  lse is the row's merged LSE (LSE
+// mode) or lse_this (gated mode).
+struct RowMerge {
+  float wa, wb, lse;
+};
+__device__ __forceinline__ RowMerge row_merge(const BoxAttnParams& p, int b, int h, uint32_t tok, float lse_this) {
+  RowMerge r{0.f, 1.f, lse_this};
+  if (p.merge == MERGE_GATED) {
+    r.wa = p.w_l != nullptr ? p.w_l[h] : 1.f;
+    r.wb = p.w_g[h];
+  } else if (p.merge == MERGE_LSE) {
+    constexpr float LOG2E = 1.4426950408889634f, LN2 = 0.69314718055994531f;
+    const int64_t N = (int64_t)p.qT * p.qH * p.qW;
+    const float la = p.lse_l[((int64_t)b * p.heads + h) * N + tok];
+    const float m = fmaxf(la, lse_this);
+    const float ea = __builtin_amdgcn_exp2f((la - m) * LOG2E);
+    const float eb = __builtin_amdgcn_exp2f((lse_this - m) * LOG2E);
+    const float z = ea + eb;
+    r.wa = ea / z;
+    r.wb = eb / z;
+    r.lse = m + __builtin_amdgcn_logf(z) * LN2;
+  }
+  return r;
+}
+
+// Four bf16 (packed in two dwords) to fp32.
+__device__ __forceinline__ void bf16x4_to_f32(uint32_t lo, uint32_t hi, float (&f)[4]) {
+  f[0] = __uint_as_float(lo << 16);
+  f[1] = __uint_as_float(lo & 0xFFFF0000u);
+  f[2] = __uint_as_float(hi << 16);
+  f[3] = __uint_as_float(hi & 0xFFFF0000u);
+}
+
 __device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv& f) {
   return (__umulhi(n, f.m) + n) >> f.s;
 }

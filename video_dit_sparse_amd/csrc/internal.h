@@ -51,7 +51,16 @@ struct BoxAttnParams {
   int32_t variant;            // which kernel shape the launcher runs (set by the host)
   int32_t total_wg;           // batch * heads * tiles * qblocks
   float scale_log2e;          // scale * log2(e)
+  // Optional merge with another branch's output in the epilogue (merge !=
+  // MERGE_NONE): out row = wa * ol row + wb * this kernel's normalised row.
+  int32_t merge;              // MERGE_NONE / MERGE_GATED / MERGE_LSE
+  const void* ol;             // other branch output, same dtype, [batch, heads, N, D]
+  int64_t ol_sb, ol_sh, ol_sn;
+  const float* lse_l;         // MERGE_LSE: other branch LSE, [batch, heads, N] contiguous
+  const float* w_l;           // MERGE_GATED: weight of ol per head (nullable => 1)
+  const float* w_g;           // MERGE_GATED: weight of this kernel's output per head
 };
+enum { MERGE_NONE = 0, MERGE_GATED = 1, MERGE_LSE = 2 };
 
 struct PoolParams {
   const void* x;
@@ -69,6 +78,9 @@ struct MergeParams {
   const void* g;
   const float* w_a;   // nullable => 1
   const float* w_g;
+  const float* lse_a; // lse_a and lse_g set: LSE merge (weights from them, w_* unused)
+  const float* lse_g;
+  float* lse_out;     // LSE merge only, nullable
   void* out;
   int64_t a_sb, a_sh, a_sn;
   int64_t g_sb, g_sh, g_sn;

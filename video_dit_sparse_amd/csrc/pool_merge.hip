@@ -106,8 +106,22 @@ __global__ __launch_bounds__(NTHREADS) void merge_kernel(const MergeParams p) {
     const int64_t n = row % p.n_tokens;
     const int bh = (int)(row / p.n_tokens);
     const int h = bh % p.heads, b = bh / p.heads;
-    const float wa = p.w_a ? p.w_a[h] : 1.f;
-    const float wg = p.w_g[h];
+    float wa, wg;
+    if (p.lse_a != nullptr) {
+      // one softmax over the union of both key sets: weights from the two
+      // log-sum-exps (natural log) of the row
+      constexpr float LOG2E = 1.4426950408889634f, LN2 = 0.69314718055994531f;
+      const float la = p.lse_a[row], lg = p.lse_g[row];
+      const float m = fmaxf(la, lg);
+      const float ea = __builtin_amdgcn_exp2f((la - m) * LOG2E), eg = __builtin_amdgcn_exp2f((lg - m) * LOG2E);
+      const float z = ea + eg;
+      wa = ea / z;
+      wg = eg / z;
+      if (p.lse_out != nullptr && ch == 0) p.lse_out[row] = m + __builtin_amdgcn_logf(z) * LN2;
+    } else {
+      wa = p.w_a ? p.w_a[h] : 1.f;
+      wg = p.w_g[h];
+    }
     float fa[C::E], fg[C::E];
     C::unpack(*(const u32x4*)((const char*)p.a + (b * p.a_sb + h * p.a_sh + n * p.a_sn) * esz + ch * 16), fa);
     C::unpack(*(const u32x4*)((const char*)p.g + (b * p.g_sb + h * p.g_sh + n * p.g_sn) * esz + ch * 16), fg);
