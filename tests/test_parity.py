@@ -196,8 +196,18 @@ def _check_workload(name, heads_to_check, n_random_tiles=4, rows_per_tile=24):
     gate = WL.make_gate(w, DEV)
     buf = P.Buffers(w, q)
     say(f"[workload] {name}: running")
-    out = P.run(w, q, k, v, gate, buf, with_lse=True)
+    out = P.run(w, q, k, v, gate, buf, with_lse=True, fused=False)
     torch.cuda.synchronize()
+    merged_fused = None
+    if w.pool_hw is not None:
+        # the fused global + merge call must give the same merged output
+        merged_unfused = out["merged"].clone()
+        out_f = P.run(w, q, k, v, gate, buf, with_lse=True, fused=True)
+        torch.cuda.synchronize()
+        merged_fused = out_f["merged"]
+        d = (merged_fused.float() - merged_unfused.float()).abs()
+        say(f"[workload] {name}: fused vs unfused merge max diff {d.max().item():.3e}")
+        assert d.max().item() <= 2e-2 and d.mean().item() <= 2e-3
     for i, shift in enumerate(w.shifts):
         rows = sample_rows(w.grid, w.tile, shift, n_random_tiles, rows_per_tile, seed=i)
         for h in heads_to_check:
@@ -220,6 +230,7 @@ def _check_workload(name, heads_to_check, n_random_tiles=4, rows_per_tile=24):
                 g = float(gate[h])
                 mr = R.merge_ref(ro[None], go[None], None, np.array([g]))[0]
                 compare(out["merged"][0, h, rows].cpu(), mr, w.dtype, f"{name} merged h{h}")
+                compare(merged_fused[0, h, rows].cpu(), mr, w.dtype, f"{name} merged (fused) h{h}")
     # properties over every output element
     for t in out["local"]:
         assert torch.isfinite(t.float()).all()

@@ -3,8 +3,10 @@
 Local branch: one ``sta_attn_fwd`` per lattice shift (two for the
 cross-window pair: the plain tile lattice, then the half-tile-shifted one, as
 in UltraGen's alternating window partitions, summary section 4.3).  Global
-branch, where the workload has one: ``global_pooled_attn_fwd`` over K/V pooled
-k_h x k_w, then ``dual_branch_merge`` with the per-head gate (w_local = 1).
+branch, where the workload has one: attention over K/V pooled k_h x k_w and
+the gated merge with the per-head gate (w_local = 1), either as one call with
+the merge fused into the attention epilogue (``global_pooled_attn_merge_fwd``,
+the default) or as ``global_pooled_attn_fwd`` then ``dual_branch_merge``.
 Every step runs in libvdsa.so's kernels on the current torch stream.
 """
 from __future__ import annotations
@@ -33,18 +35,26 @@ class Buffers:
             self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
 
 
-def run(w: Workload, q, k, v, gate: Optional[torch.Tensor], buf: Buffers, with_lse: bool = False) -> Dict:
-    """One pass of the workload's hot path; returns the output tensors."""
+def run(w: Workload, q, k, v, gate: Optional[torch.Tensor], buf: Buffers, with_lse: bool = False,
+        fused: bool = True) -> Dict:
+    """One pass of the workload's hot path; returns the output tensors.  With
+    ``fused`` the global branch's own output is never materialised
+    (``glob`` is None; ``glob_lse`` still holds its LSE when requested)."""
     for i, shift in enumerate(w.shifts):
         L.sta_attn_fwd(q, k, v, w.grid, w.tile, w.window, shift, scale=w.softmax_scale,
                        out=buf.local[i], lse=buf.lse[i] if with_lse else None)
     out = {"local": buf.local, "lse": buf.lse if with_lse else None}
     if w.pool_hw is not None:
-        L.global_pooled_attn_fwd(q, k, v, w.grid, w.pool_hw, scale=w.softmax_scale, out=buf.glob,
-                                 lse=buf.glob_lse if with_lse else None, workspace=buf.workspace)
-        L.dual_branch_merge(buf.local[0], buf.glob, gate, out=buf.merged)
-        out.update(glob=buf.glob, glob_lse=buf.glob_lse if with_lse else None, merged=buf.merged,
-                   workspace=buf.workspace)
+        glse = buf.glob_lse if with_lse else None
+        if fused:
+            L.global_pooled_attn_merge_fwd(q, k, v, w.grid, w.pool_hw, buf.local[0], mode="gated", w_global=gate,
+                                           scale=w.softmax_scale, out=buf.merged, lse_out=glse,
+                                           workspace=buf.workspace)
+        else:
+            L.global_pooled_attn_fwd(q, k, v, w.grid, w.pool_hw, scale=w.softmax_scale, out=buf.glob, lse=glse,
+                                     workspace=buf.workspace)
+            L.dual_branch_merge(buf.local[0], buf.glob, gate, out=buf.merged)
+        out.update(glob=None if fused else buf.glob, glob_lse=glse, merged=buf.merged, workspace=buf.workspace)
     return out
 
 
