@@ -176,6 +176,39 @@ def main():
                 "flop_per_launch": launch_flops}
 
     extra = {}
+    if w.pool_hw is not None and args.steps > 0:
+        # global branch: fused global + merge call against the two separate
+        # calls, and the standalone exact (LSE) merge, each timed with events
+        def timed(fn, n):
+            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            fn()
+            a.record(stream)
+            for _ in range(n):
+                fn()
+            z.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(z) / n
+        lse_l = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        V.sta_attn_fwd(q, k, v, w.grid, w.tile, w.window, w.shifts[0], scale=w.softmax_scale,
+                       out=buf.local[0], lse=lse_l)
+        n = max(1, min(args.steps, 10))
+        fused_ms = timed(lambda: P.run_global(w, q, k, v, gate, buf, fused=True), n)
+        unfused_ms = timed(lambda: P.run_global(w, q, k, v, gate, buf, fused=False), n)
+        lse_g = torch.empty_like(lse_l)
+        V.global_pooled_attn_fwd(q, k, v, w.grid, w.pool_hw, scale=w.softmax_scale, out=buf.glob, lse=lse_g,
+                                 workspace=buf.workspace)
+        merge_lse_ms = timed(lambda: V.dual_branch_merge_lse(buf.local[0], lse_l, buf.glob, lse_g,
+                                                             out=buf.merged), n)
+        tensor_bytes = q.numel() * q.element_size()
+        lse_bytes = lse_l.numel() * 4
+        merge_lse_bytes = 3 * tensor_bytes + 2 * lse_bytes   # read two rows and two LSEs, write one row
+        extra["global_branch"] = {
+            "fused_global_merge_ms": round(fused_ms, 3), "global_then_merge_ms": round(unfused_ms, 3),
+            "merge_lse_ms": round(merge_lse_ms, 4),
+            "merge_lse_GBps": round(merge_lse_bytes / (merge_lse_ms * 1e-3) / 1e9, 1),
+            "merge_lse_hbm_frac": round(merge_lse_bytes / (merge_lse_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        log(f"[bench] global branch: fused {fused_ms:.3f} ms, global then merge {unfused_ms:.3f} ms; "
+            f"LSE merge {merge_lse_ms:.3f} ms ({merge_lse_bytes / (merge_lse_ms * 1e-3) / 1e9:.0f} GB/s)")
     if args.dense_steps > 0 and w.pool_hw is None:
         # the same kernel with a window covering the whole tile lattice = dense attention
         n_tiles = [-(-(L + s) // b) for L, b, s in zip(w.grid, w.tile, w.shifts[0])]

@@ -45,17 +45,22 @@ def run(w: Workload, q, k, v, gate: Optional[torch.Tensor], buf: Buffers, with_l
                        out=buf.local[i], lse=buf.lse[i] if with_lse else None)
     out = {"local": buf.local, "lse": buf.lse if with_lse else None}
     if w.pool_hw is not None:
-        glse = buf.glob_lse if with_lse else None
-        if fused:
-            L.global_pooled_attn_merge_fwd(q, k, v, w.grid, w.pool_hw, buf.local[0], mode="gated", w_global=gate,
-                                           scale=w.softmax_scale, out=buf.merged, lse_out=glse,
-                                           workspace=buf.workspace)
-        else:
-            L.global_pooled_attn_fwd(q, k, v, w.grid, w.pool_hw, scale=w.softmax_scale, out=buf.glob, lse=glse,
-                                     workspace=buf.workspace)
-            L.dual_branch_merge(buf.local[0], buf.glob, gate, out=buf.merged)
-        out.update(glob=None if fused else buf.glob, glob_lse=glse, merged=buf.merged, workspace=buf.workspace)
+        out.update(run_global(w, q, k, v, gate, buf, with_lse, fused))
     return out
+
+
+def run_global(w: Workload, q, k, v, gate, buf: Buffers, with_lse: bool = False, fused: bool = True) -> Dict:
+    """The global branch and the merge with the local output in ``buf.local[0]``."""
+    glse = buf.glob_lse if with_lse else None
+    if fused:
+        L.global_pooled_attn_merge_fwd(q, k, v, w.grid, w.pool_hw, buf.local[0], mode="gated", w_global=gate,
+                                       scale=w.softmax_scale, out=buf.merged, lse_out=glse,
+                                       workspace=buf.workspace)
+    else:
+        L.global_pooled_attn_fwd(q, k, v, w.grid, w.pool_hw, scale=w.softmax_scale, out=buf.glob, lse=glse,
+                                 workspace=buf.workspace)
+        L.dual_branch_merge(buf.local[0], buf.glob, gate, out=buf.merged)
+    return {"glob": None if fused else buf.glob, "glob_lse": glse, "merged": buf.merged, "workspace": buf.workspace}
 
 
 def flops(w: Workload) -> Dict[str, float]:
