@@ -22,6 +22,9 @@ from .ref import (  # noqa: F401
     merge_ref,
     merge_lse_ref,
     union_attention_ref,
+    attention_bwd_ref,
+    sta_bwd_ref,
+    global_bwd_ref,
     sta_pair_count_ref,
     sta_flops_ref,
     global_flops_ref,

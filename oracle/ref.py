@@ -47,7 +47,8 @@ __all__ = [
     "to_f64", "token_coords", "tile_index", "tile_counts", "tile_extent",
     "window_radius", "sta_mask_row", "sta_ref", "dense_ref",
     "attention_weights_ref", "pooled_grid", "pool_ref", "global_ref",
-    "merge_ref", "merge_lse_ref", "union_attention_ref", "sta_pair_count_ref",
+    "merge_ref", "merge_lse_ref", "union_attention_ref", "attention_bwd_ref", "sta_bwd_ref",
+    "global_bwd_ref", "sta_pair_count_ref",
     "sta_flops_ref", "global_flops_ref", "dense_flops_ref",
 ]
 
@@ -301,6 +302,82 @@ def union_attention_ref(q, k, v, grid, tile, window, shift, k_pooled, v_pooled, 
         oj, lj = _softmax_attend(q[n:n + 1], kk, vv, scale)
         o[j], lse[j] = oj[0], lj[0]
     return o, lse
+
+
+# --------------------------------------------------------------------------
+# backward (gradients of the forward definitions above)
+# --------------------------------------------------------------------------
+def attention_bwd_ref(q, k, v, do, scale):
+    """Gradients of O = softmax(scale * q k^T) v over the given keys.
+
+    With P the softmax, dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dO * O))
+    (the softmax Jacobian applied row by row), dQ = scale dS K and
+    dK = scale dS^T Q.  Returns (dQ, dK, dV) for these rows and keys.
+    """
+    s = scale * (q @ k.T)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    o = p @ v
+    dv = p.T @ do
+    dp = do @ v.T
+    ds = p * (dp - (do * o).sum(axis=1, keepdims=True))
+    return scale * (ds @ k), scale * (ds.T @ q), dv
+
+
+def sta_bwd_ref(q, k, v, do, grid, tile, window, shift=(0, 0, 0), scale=None):
+    """Gradients of ``sta_ref`` for one head: every query tile's rows
+    contribute through its own selected keys (the explicit mask of
+    ``sta_mask_row``); key gradients are summed over all query tiles that
+    select the key.  Returns (dQ, dK, dV), each [N, D].
+    """
+    q, k, v, do = to_f64(q), to_f64(k), to_f64(v), to_f64(do)
+    N, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    radius = window_radius(window)
+    ti = tile_index(token_coords(grid), tile, shift)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    uniq, inv = np.unique(ti, axis=0, return_inverse=True)
+    inv = np.asarray(inv).reshape(-1)
+    for g in range(len(uniq)):
+        rows = np.nonzero(inv == g)[0]
+        keys = np.nonzero(sta_mask_row(ti, uniq[g], radius))[0]
+        gq, gk, gv = attention_bwd_ref(q[rows], k[keys], v[keys], do[rows], scale)
+        dq[rows] += gq
+        dk[keys] += gk
+        dv[keys] += gv
+    return dq, dk, dv
+
+
+def global_bwd_ref(q, k, v, do, grid, pool_hw, scale=None):
+    """Gradients of the global branch for one head, through the pooling:
+    dQ, dKp, dVp of dense attention over the pooled keys, then every token of
+    a cell receives its cell's gradient divided by the cell's token count
+    (the derivative of the cell mean).  Returns (dQ, dK, dV), each [N, D].
+    """
+    q, k, v, do = to_f64(q), to_f64(k), to_f64(v), to_f64(do)
+    N, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    kp, vp = pool_ref(k, grid, pool_hw), pool_ref(v, grid, pool_hw)
+    dq, dkp, dvp = attention_bwd_ref(q, kp, vp, do, scale)
+    T, H, W = grid
+    kh, kw = pool_hw
+    _, Hp, Wp = pooled_grid(grid, pool_hw)
+    dk, dv = np.empty_like(k), np.empty_like(v)
+    for t in range(T):
+        for i in range(Hp):
+            for j in range(Wp):
+                hs = range(i * kh, min(H, (i + 1) * kh))
+                ws = range(j * kw, min(W, (j + 1) * kw))
+                cnt = len(hs) * len(ws)
+                m = (t * Hp + i) * Wp + j
+                for h in hs:
+                    for w in ws:
+                        n = (t * H + h) * W + w
+                        dk[n] = dkp[m] / cnt
+                        dv[n] = dvp[m] / cnt
+    return dq, dk, dv
 
 
 # --------------------------------------------------------------------------

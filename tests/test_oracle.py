@@ -407,3 +407,120 @@ def test_cost_estimate_page_fact():
     assert round(speedup) == f["approx_speedup"]
     # asymmetric global (full-resolution Q against K x K pooled K/V) is 1/K^2
     assert R.global_flops_ref(grid, (K, K)) * K ** 2 == dense
+
+
+# ---------------------------------------------------------------- backward
+def _autograd_masked_attention(q, k, v, do, mask, scale):
+    """Gradients by torch autograd (fp64, CPU) of softmax(scale q k^T + mask) v."""
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    s = scale * tq @ tk.T
+    if mask is not None:
+        s = s.masked_fill(~torch.from_numpy(mask), float("-inf"))
+    o = torch.softmax(s, dim=1) @ tv
+    o.backward(torch.from_numpy(do))
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+def _sta_mask_by_coords(grid, tile, window, shift):
+    """Token-level window mask built independently of the oracle: tile
+    indices from numpy's own index decomposition, then the window test."""
+    c = coords_lib(grid)
+    ti = (c + np.asarray(shift)) // np.asarray(tile)
+    r = (np.asarray(window) - 1) // 2
+    return np.all(np.abs(ti[:, None, :] - ti[None, :, :]) <= r[None, None, :], axis=2)
+
+
+def test_attention_bwd_matches_autograd():
+    q, k, v, do = randn(200, 7, 16), randn(201, 11, 16), randn(202, 11, 16), randn(203, 7, 16)
+    got = R.attention_bwd_ref(q, k, v, do, 0.3)
+    ref = _autograd_masked_attention(q, k, v, do, None, 0.3)
+    for g, r in zip(got, ref):
+        np.testing.assert_allclose(g, r, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("grid,tile,window,shift", [
+    ((4, 6, 8), (2, 3, 4), (3, 1, 1), (0, 0, 0)),
+    ((3, 7, 9), (2, 4, 4), (1, 3, 3), (1, 2, 2)),
+    ((2, 5, 6), (1, 2, 3), (3, 3, 1), (0, 1, 2)),
+])
+def test_sta_bwd_matches_autograd_of_masked_dense(grid, tile, window, shift):
+    N = int(np.prod(grid))
+    q, k, v, do = randn(210, N, 8), randn(211, N, 8), randn(212, N, 8), randn(213, N, 8)
+    mask = _sta_mask_by_coords(grid, tile, window, shift)
+    got = R.sta_bwd_ref(q, k, v, do, grid, tile, window, shift, scale=0.4)
+    ref = _autograd_masked_attention(q, k, v, do, mask, 0.4)
+    for g, r in zip(got, ref):
+        np.testing.assert_allclose(g, r, rtol=0, atol=1e-11)
+
+
+def test_sta_bwd_finite_differences():
+    grid, tile, window, shift = (2, 2, 3), (1, 2, 2), (1, 1, 3), (0, 1, 0)
+    N, D = 12, 3
+    q, k, v, g = randn(220, N, D), randn(221, N, D), randn(222, N, D), randn(223, N, D)
+    loss = lambda qq, kk, vv: float((R.sta_ref(qq, kk, vv, grid, tile, window, shift, scale=0.7)[0] * g).sum())
+    dq, dk, dv = R.sta_bwd_ref(q, k, v, g, grid, tile, window, shift, scale=0.7)
+    eps = 1e-6
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        args = [q, k, v]
+        fd = np.zeros_like(grad)
+        for n in range(N):
+            for d in range(D):
+                up = [a.copy() for a in args]
+                dn = [a.copy() for a in args]
+                up[which][n, d] += eps
+                dn[which][n, d] -= eps
+                fd[n, d] = (loss(*up) - loss(*dn)) / (2 * eps)
+        np.testing.assert_allclose(grad, fd, rtol=0, atol=1e-7)
+
+
+def test_sta_bwd_invariants():
+    # softmax rows sum to one: keys' value gradients sum to the output
+    # gradients' sum, and key gradients sum to zero
+    grid, tile, window, shift = (3, 6, 8), (2, 3, 4), (1, 3, 1), (1, 1, 2)
+    N = int(np.prod(grid))
+    q, k, v, do = randn(230, N, 8), randn(231, N, 8), randn(232, N, 8), randn(233, N, 8)
+    dq, dk, dv = R.sta_bwd_ref(q, k, v, do, grid, tile, window, shift)
+    np.testing.assert_allclose(dv.sum(axis=0), do.sum(axis=0), atol=1e-11)
+    np.testing.assert_allclose(dk.sum(axis=0), 0.0, atol=1e-11)
+    # a full window is dense attention's backward
+    full = tuple(2 * c - 1 for c in R.tile_counts(grid, tile, shift))
+    dense = R.attention_bwd_ref(q, k, v, do, 1.0 / math.sqrt(8))
+    for g, r in zip(R.sta_bwd_ref(q, k, v, do, grid, tile, full, shift), dense):
+        np.testing.assert_allclose(g, r, atol=1e-12)
+
+
+@pytest.mark.parametrize("grid,pool", [((2, 4, 6), (2, 3)), ((3, 6, 4), (3, 2)), ((1, 4, 4), (1, 1))])
+def test_global_bwd_matches_autograd_through_avg_pool(grid, pool):
+    T, H, W = grid
+    N = T * H * W
+    q, k, v, do = randn(240, N, 5), randn(241, N, 5), randn(242, N, 5), randn(243, N, 5)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    pool2d = lambda x: torch.nn.functional.avg_pool2d(x.reshape(T, H, W, 5).permute(0, 3, 1, 2), pool,
+                                                      stride=pool).permute(0, 2, 3, 1).reshape(-1, 5)
+    o = torch.softmax(0.5 * tq @ pool2d(tk).T, dim=1) @ pool2d(tv)
+    o.backward(torch.from_numpy(do))
+    got = R.global_bwd_ref(q, k, v, do, grid, pool, scale=0.5)
+    for g, r in zip(got, (tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy())):
+        np.testing.assert_allclose(g, r, rtol=0, atol=1e-12)
+
+
+def test_global_bwd_ragged_cells_finite_differences():
+    grid, pool = (1, 3, 5), (2, 2)   # cells of 4, 2 and 1 tokens
+    N, D = 15, 2
+    q, k, v, g = randn(250, N, D), randn(251, N, D), randn(252, N, D), randn(253, N, D)
+
+    def loss(qq, kk, vv):
+        o, _ = R.global_ref(qq, R.pool_ref(kk, grid, pool), R.pool_ref(vv, grid, pool), scale=0.8)
+        return float((o * g).sum())
+    grads = R.global_bwd_ref(q, k, v, g, grid, pool, scale=0.8)
+    eps = 1e-6
+    for which in range(3):
+        fd = np.zeros((N, D))
+        for n in range(N):
+            for d in range(D):
+                up = [q.copy(), k.copy(), v.copy()]
+                dn = [q.copy(), k.copy(), v.copy()]
+                up[which][n, d] += eps
+                dn[which][n, d] -= eps
+                fd[n, d] = (loss(*up) - loss(*dn)) / (2 * eps)
+        np.testing.assert_allclose(grads[which], fd, rtol=0, atol=1e-7)
