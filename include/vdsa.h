@@ -240,6 +240,54 @@ vdsa_status global_pooled_attn_merge_fwd(const vdsa_problem* prob, const int32_t
                                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Backward passes.  Gradients of a forward call's output O given dO, from the
+ * forward's inputs, its output O and its LSE (natural log, as written by the
+ * forward's `lse` argument).  With P the attention weights of a query row:
+ *   delta = rowsum(dO * O),  dS = P * (dO.V^T - delta),
+ *   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO,
+ * summed over every query whose keys include the key (the softmax Jacobian
+ * of the definitions above).  Gradients are written (not accumulated) in the
+ * problem dtype with fp32 accumulation.  bf16 supports head_dim 128; fp32
+ * supports 64 and 128 (VDSA_ERR_UNSUPPORTED otherwise).
+ *
+ *   workspace : device, at least *_bwd_workspace_size() bytes, 16-byte
+ *               aligned, not overlapping any argument.
+ *   dq, dk, dv: must not overlap each other, any input, lse or the workspace.
+ * Errors: as the forward call, plus VDSA_ERR_WORKSPACE.
+ */
+vdsa_status sta_attn_bwd_workspace_size(const vdsa_problem* prob, size_t* bytes);
+vdsa_status sta_attn_bwd(const vdsa_problem* prob, const vdsa_sta_cfg* cfg,
+                         const void* q, const vdsa_strides* q_strides,
+                         const void* k, const vdsa_strides* k_strides,
+                         const void* v, const vdsa_strides* v_strides,
+                         const void* o, const vdsa_strides* o_strides,
+                         const void* d_o, const vdsa_strides* do_strides,
+                         const float* lse,
+                         void* dq, const vdsa_strides* dq_strides,
+                         void* dk, const vdsa_strides* dk_strides,
+                         void* dv, const vdsa_strides* dv_strides,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* The global branch's backward, through the pooling: the pooled K and V get
+ * their gradients as above (every query attends every pooled token), then
+ * every token of a pooling cell receives its cell's gradient divided by the
+ * cell's token count (the derivative of the cell mean).  o and lse are the
+ * outputs of global_pooled_attn_fwd (not of a fused merge call). */
+vdsa_status global_pooled_attn_bwd_workspace_size(const vdsa_problem* prob, const int32_t pool_hw[2],
+                                                  size_t* bytes);
+vdsa_status global_pooled_attn_bwd(const vdsa_problem* prob, const int32_t pool_hw[2],
+                                   const void* q, const vdsa_strides* q_strides,
+                                   const void* k, const vdsa_strides* k_strides,
+                                   const void* v, const vdsa_strides* v_strides,
+                                   const void* o, const vdsa_strides* o_strides,
+                                   const void* d_o, const vdsa_strides* do_strides,
+                                   const float* lse,
+                                   void* dq, const vdsa_strides* dq_strides,
+                                   void* dk, const vdsa_strides* dk_strides,
+                                   void* dv, const vdsa_strides* dv_strides,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * kv_avgpool_fwd - the pooling step of global_pooled_attn_fwd on one tensor,
  * exported so it can be checked and timed alone.  x_pooled is
  * [batch, heads, M, head_dim] with its own strides; must not overlap x.

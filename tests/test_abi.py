@@ -198,6 +198,44 @@ def test_fused_global_merge_checks():
     assert f(L.VDSA_MERGE_GATED, wsb=n.value - 1) == L.STATUS["VDSA_ERR_WORKSPACE"]
 
 
+def test_backward_checks():
+    p = prob()
+    d = st(p)
+    c = cfg()
+    n = ctypes.c_size_t()
+    assert L.lib().sta_attn_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    assert n.value >= 1 * 2 * 256 * 4   # delta: [batch, heads, N] fp32
+    DO, DQ, DK, DV = 0x80000000, 0x90000000, 0xA0000000, 0xB0000000
+
+    def b(pp=p, lse=LSE, dq=DQ, dk=DK, dv=DV, ws=WS, wsb=None, o=O):
+        return L.lib().sta_attn_bwd(ctypes.byref(pp), ctypes.byref(c), Q, ctypes.byref(d), K, ctypes.byref(d),
+                                    V, ctypes.byref(d), o, ctypes.byref(d), DO, ctypes.byref(d), lse,
+                                    dq, ctypes.byref(d), dk, ctypes.byref(d), dv, ctypes.byref(d), ws,
+                                    n.value if wsb is None else wsb, None)
+    assert b(lse=None) == L.STATUS["VDSA_ERR_NULL"]
+    assert b(dq=None) == L.STATUS["VDSA_ERR_NULL"]
+    assert b(dk=Q + 512) == L.STATUS["VDSA_ERR_ALIAS"]        # dk over q
+    assert b(dv=DK + 256) == L.STATUS["VDSA_ERR_ALIAS"]       # dv straddles dk
+    assert b(dq=LSE) == L.STATUS["VDSA_ERR_ALIAS"]            # dq over lse
+    assert b(ws=None) == L.STATUS["VDSA_ERR_WORKSPACE"]
+    assert b(wsb=n.value - 1) == L.STATUS["VDSA_ERR_WORKSPACE"]
+    assert b(ws=DV + 256) == L.STATUS["VDSA_ERR_ALIAS"]       # workspace inside dv
+    assert b(pp=prob(head_dim=64)) == L.STATUS["VDSA_ERR_UNSUPPORTED"]   # bf16 backward: head_dim 128
+    pool = (ctypes.c_int32 * 2)(4, 4)
+    gn = ctypes.c_size_t()
+    assert L.lib().global_pooled_attn_bwd_workspace_size(ctypes.byref(p), pool, ctypes.byref(gn)) == 0
+    assert gn.value > n.value
+
+    def gb(lse=LSE, wsb=None, pl=pool):
+        return L.lib().global_pooled_attn_bwd(ctypes.byref(p), pl, Q, ctypes.byref(d), K, ctypes.byref(d),
+                                              V, ctypes.byref(d), O, ctypes.byref(d), DO, ctypes.byref(d), lse,
+                                              DQ, ctypes.byref(d), DK, ctypes.byref(d), DV, ctypes.byref(d), WS,
+                                              gn.value if wsb is None else wsb, None)
+    assert gb(lse=None) == L.STATUS["VDSA_ERR_NULL"]
+    assert gb(wsb=gn.value - 1) == L.STATUS["VDSA_ERR_WORKSPACE"]
+    assert gb(pl=(ctypes.c_int32 * 2)(0, 4)) == L.STATUS["VDSA_ERR_WINDOW"]
+
+
 FLOP_CASES = [
     ((4, 8, 8), (2, 4, 4), (3, 3, 3), (0, 0, 0)),
     ((30, 48, 80), (6, 8, 8), (3, 3, 5), (0, 0, 0)),

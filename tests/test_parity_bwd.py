@@ -1,0 +1,117 @@
+"""GPU parity of the backward passes (``sta_attn_bwd``,
+``global_pooled_attn_bwd``) through the C ABI against the CPU fp64 oracle,
+on every gradient element.
+
+Tolerance (bf16): the kernels round P and dS to bf16 for the matrix-core
+products (relative rounding 2^-9) and take delta = rowsum(dO * O) from the
+bf16 forward output; the global branch also rounds the pooled K and V to
+bf16.  Each gradient element sums many such terms in fp32, so its typical
+error is 2^-9 to sqrt(3) 2^-9 of the gradient's RMS (measured 1.7e-3 to
+2.7e-3).  Elements whose terms share a sign accumulate their rounding
+linearly instead of as a random walk, giving a tail about ten times the mean;
+and key gradients through the pooling are the cell gradient divided by the
+cell's token count, so tokens of small ragged cells carry gradients many
+times the RMS.  The bar: mean abs error <= 5e-3 * RMS (a dropped or wrong
+term shows at the scale of the RMS itself) and, element by element,
+abs error <= 6e-2 * (RMS + |reference|).  fp32: 1e-5 * RMS and
+1e-4 * (RMS + |reference|).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as R
+import video_dit_sparse_amd as V
+from video_dit_sparse_amd import workloads as WL
+from _parity import head_f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TDT = {"bf16": torch.bfloat16, "f32": torch.float32}
+TOL_BWD = {"bf16": (6e-2, 5e-3), "f32": (1e-4, 1e-5)}
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    V.lib()  # fail loudly if the library is missing
+
+
+def tensors(shape, dtype, seed, n=4):
+    return [WL.make_tensor(shape, dtype, DEV, seed=seed + i) for i in range(n)]
+
+
+def rel_compare(got, ref, dt, what):
+    g = R.to_f64(got)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    assert np.isfinite(g).all(), f"{what}: non-finite values"
+    rms = float(np.sqrt(np.mean(r * r)))
+    err = np.abs(g - r)
+    tmax, tmean = TOL_BWD[dt]
+    worst = float((err / (rms + np.abs(r))).max())
+    mean = float(err.mean()) / rms
+    say(f"  {what}: max err {worst:.2e} (rms + |ref|), mean {mean:.2e} rms (rms {rms:.3e})")
+    assert worst <= tmax and mean <= tmean, \
+        f"{what}: max err {worst:.3e} x (rms + |ref|) (<= {tmax}), mean {mean:.3e} rms (<= {tmean})"
+
+
+STA_BWD = [
+    # name, batch, grid, tile, window, shift, heads, head_dim, dtype
+    ("tile32_bf16", 1, (4, 8, 12), (2, 4, 4), (1, 3, 3), (0, 0, 0), 2, 128, "bf16"),
+    ("shift_partial_bf16", 2, (3, 10, 13), (2, 4, 4), (3, 1, 3), (1, 2, 2), 1, 128, "bf16"),
+    ("tile384_bf16", 1, (6, 16, 16), (6, 8, 8), (1, 3, 1), (0, 0, 0), 1, 128, "bf16"),
+    ("f32_d64", 1, (3, 6, 8), (3, 3, 4), (1, 3, 1), (0, 1, 2), 2, 64, "f32"),
+    ("f32_d128", 1, (2, 6, 8), (1, 3, 4), (1, 1, 3), (0, 0, 0), 1, 128, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", STA_BWD, ids=[c[0] for c in STA_BWD])
+def test_sta_bwd_small(case):
+    name, B, grid, tile, window, shift, heads, D, dt = case
+    say(f"[sta bwd] {name}")
+    N = int(np.prod(grid))
+    q, k, v, do = tensors((B, heads, N, D), TDT[dt], seed=800)
+    o, lse = V.sta_attn_fwd(q, k, v, grid, tile, window, shift, return_lse=True)
+    dq, dk, dv = V.sta_attn_bwd(q, k, v, o, do, lse, grid, tile, window, shift)
+    dq2, dk2, dv2 = V.sta_attn_bwd(q, k, v, o, do, lse, grid, tile, window, shift)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)   # deterministic
+    for b in range(B):
+        for h in range(heads):
+            ref = R.sta_bwd_ref(head_f64(q, b, h), head_f64(k, b, h), head_f64(v, b, h), head_f64(do, b, h),
+                                grid, tile, window, shift, scale=D ** -0.5)
+            for nm, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+                rel_compare(got[b, h].cpu(), r, dt, f"{name} {nm} b{b} h{h}")
+
+
+GLOBAL_BWD = [
+    # name, batch, grid, pool, heads, head_dim, dtype
+    ("pool2x4_bf16", 1, (3, 8, 12), (2, 4), 2, 128, "bf16"),
+    ("pool_ragged_bf16", 2, (2, 9, 10), (4, 3), 1, 128, "bf16"),
+    ("pool_f32_d64", 1, (3, 9, 10), (2, 3), 2, 64, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", GLOBAL_BWD, ids=[c[0] for c in GLOBAL_BWD])
+def test_global_bwd_small(case):
+    name, B, grid, pool, heads, D, dt = case
+    say(f"[global bwd] {name}")
+    N = int(np.prod(grid))
+    q, k, v, do = tensors((B, heads, N, D), TDT[dt], seed=820)
+    o, lse = V.global_pooled_attn_fwd(q, k, v, grid, pool, return_lse=True)
+    dq, dk, dv = V.global_pooled_attn_bwd(q, k, v, o, do, lse, grid, pool)
+    torch.cuda.synchronize()
+    for b in range(B):
+        for h in range(heads):
+            ref = R.global_bwd_ref(head_f64(q, b, h), head_f64(k, b, h), head_f64(v, b, h), head_f64(do, b, h),
+                                   grid, pool, scale=D ** -0.5)
+            for nm, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+                rel_compare(got[b, h].cpu(), r, dt, f"{name} {nm} b{b} h{h}")

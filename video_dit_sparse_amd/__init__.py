@@ -4,7 +4,8 @@ Python face of libvdsa.so: the three calls of the hot path
 (``sta_attn_fwd``, ``global_pooled_attn_fwd``, ``dual_branch_merge``), the
 exact log-sum-exp merge (``dual_branch_merge_lse``), the global branch with
 either merge fused into it (``global_pooled_attn_merge_fwd``), the pooling
-step alone (``kv_avgpool_fwd``) and the effective-work counters.
+step alone (``kv_avgpool_fwd``), the backward passes (``sta_attn_bwd``,
+``global_pooled_attn_bwd``) and the effective-work counters.
 """
 from ._lib import (  # noqa: F401
     VdsaError,
@@ -14,9 +15,11 @@ from ._lib import (  # noqa: F401
     global_flops,
     global_pooled_attn_fwd,
     global_pooled_attn_merge_fwd,
+    global_pooled_attn_bwd,
     global_pooled_attn_workspace_size,
     kv_avgpool_fwd,
     lib,
     sta_attn_fwd,
+    sta_attn_bwd,
     sta_flops,
 )

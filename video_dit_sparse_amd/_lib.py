@@ -28,6 +28,8 @@ STATUS = {v: k for k, v in STATUS_NAMES.items()}
 EXPORTED = [
     "sta_attn_fwd", "global_pooled_attn_workspace_size", "global_pooled_attn_fwd",
     "dual_branch_merge", "dual_branch_merge_lse", "global_pooled_attn_merge_fwd",
+    "sta_attn_bwd_workspace_size", "sta_attn_bwd", "global_pooled_attn_bwd_workspace_size",
+    "global_pooled_attn_bwd",
     "kv_avgpool_fwd", "vdsa_sta_flops", "vdsa_global_flops",
     "vdsa_status_string", "vdsa_last_error", "vdsa_abi_version",
 ]
@@ -78,6 +80,12 @@ def lib() -> ctypes.CDLL:
     L.global_pooled_attn_merge_fwd.argtypes = [P, i32p, vp, S, vp, S, vp, S, ctypes.c_int, vp, S, fp, fp, fp,
                                                vp, S, fp, vp, ctypes.c_size_t, vp]
     L.kv_avgpool_fwd.argtypes = [P, i32p, vp, S, vp, S, vp]
+    L.sta_attn_bwd_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    L.sta_attn_bwd.argtypes = [P, C, vp, S, vp, S, vp, S, vp, S, vp, S, fp, vp, S, vp, S, vp, S,
+                               vp, ctypes.c_size_t, vp]
+    L.global_pooled_attn_bwd_workspace_size.argtypes = [P, i32p, ctypes.POINTER(ctypes.c_size_t)]
+    L.global_pooled_attn_bwd.argtypes = [P, i32p, vp, S, vp, S, vp, S, vp, S, vp, S, fp, vp, S, vp, S, vp, S,
+                                         vp, ctypes.c_size_t, vp]
     L.vdsa_sta_flops.argtypes = [P, C, ctypes.POINTER(ctypes.c_double)]
     L.vdsa_global_flops.argtypes = [P, i32p, ctypes.POINTER(ctypes.c_double)]
     L.vdsa_status_string.argtypes = [ctypes.c_int]
@@ -289,6 +297,58 @@ def global_pooled_attn_merge_fwd(q, k, v, grid, pool_hw, o_local, mode="gated", 
         _lse_arg(lse_out, (B, Hh, N), "lse_out") if lse_out is not None else None,
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
     return (o, lse_out) if (return_lse or lse_out is not None) else o
+
+
+def _bwd_outputs(q, dq, dk, dv):
+    torch = _torch()
+    return tuple(torch.empty_like(q, memory_format=torch.contiguous_format) if t is None else t for t in (dq, dk, dv))
+
+
+def sta_attn_bwd(q, k, v, o, do, lse, grid, tile, window, shift=(0, 0, 0), scale=None, dq=None, dk=None, dv=None,
+                 workspace=None, stream=None):
+    """Gradients of ``sta_attn_fwd`` (``sta_attn_bwd`` in include/vdsa.h), from
+    the forward's inputs, output ``o`` and ``lse``.  Returns (dQ, dK, dV)."""
+    torch = _torch()
+    _same(q, k, v, o, do)
+    B, Hh, N, D = q.shape
+    prob = _problem_for(q, grid, scale)
+    cfg = make_cfg(tile, window, shift)
+    need = ctypes.c_size_t()
+    check(lib().sta_attn_bwd_workspace_size(ctypes.byref(prob), ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+    dq, dk, dv = _bwd_outputs(q, dq, dk, dv)
+    check(lib().sta_attn_bwd(
+        ctypes.byref(prob), ctypes.byref(cfg), q.data_ptr(), ctypes.byref(_strides(q)),
+        k.data_ptr(), ctypes.byref(_strides(k)), v.data_ptr(), ctypes.byref(_strides(v)),
+        o.data_ptr(), ctypes.byref(_strides(o)), do.data_ptr(), ctypes.byref(_strides(do)),
+        _lse_arg(lse, (B, Hh, N), "lse"), dq.data_ptr(), ctypes.byref(_strides(dq)),
+        dk.data_ptr(), ctypes.byref(_strides(dk)), dv.data_ptr(), ctypes.byref(_strides(dv)),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return dq, dk, dv
+
+
+def global_pooled_attn_bwd(q, k, v, o, do, lse, grid, pool_hw, scale=None, dq=None, dk=None, dv=None,
+                           workspace=None, stream=None):
+    """Gradients of ``global_pooled_attn_fwd`` through the pooling
+    (``global_pooled_attn_bwd``).  Returns (dQ, dK, dV)."""
+    torch = _torch()
+    _same(q, k, v, o, do)
+    B, Hh, N, D = q.shape
+    prob = _problem_for(q, grid, scale)
+    need = ctypes.c_size_t()
+    check(lib().global_pooled_attn_bwd_workspace_size(ctypes.byref(prob), _pool(pool_hw), ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+    dq, dk, dv = _bwd_outputs(q, dq, dk, dv)
+    check(lib().global_pooled_attn_bwd(
+        ctypes.byref(prob), _pool(pool_hw), q.data_ptr(), ctypes.byref(_strides(q)),
+        k.data_ptr(), ctypes.byref(_strides(k)), v.data_ptr(), ctypes.byref(_strides(v)),
+        o.data_ptr(), ctypes.byref(_strides(o)), do.data_ptr(), ctypes.byref(_strides(do)),
+        _lse_arg(lse, (B, Hh, N), "lse"), dq.data_ptr(), ctypes.byref(_strides(dq)),
+        dk.data_ptr(), ctypes.byref(_strides(dk)), dv.data_ptr(), ctypes.byref(_strides(dv)),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return dq, dk, dv
 
 
 def kv_avgpool_fwd(x, grid, pool_hw, out=None, stream=None):

@@ -26,7 +26,7 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-f
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function"]
 
-SOURCES = ["attn_bf16.hip", "attn_bf16_m16.hip", "attn_bf16_pp.hip", "attn_f32.hip", "pool_merge.hip", "api.cpp"]
+SOURCES = ["attn_bf16.hip", "attn_bf16_m16.hip", "attn_bf16_pp.hip", "attn_bwd_bf16.hip", "attn_bwd.hip", "attn_f32.hip", "pool_merge.hip", "api.cpp"]
 
 
 def hipcc() -> str:

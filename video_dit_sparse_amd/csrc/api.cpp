@@ -371,6 +371,109 @@ vdsa_status global_attn_impl(const vdsa_problem* prob, const int32_t pool_hw[2],
   return launch_attn(prob, bp, (hipStream_t)stream);
 }
 
+
+// ---- backward
+struct BwdViews {
+  View q, k, v, o, dout, dq, dk, dv;
+};
+
+vdsa_status check_bwd(const vdsa_problem* prob, BwdViews& bv, const float* lse, uintptr_t& l0, uintptr_t& l1) {
+  vdsa_status s;
+  if (prob->dtype == VDSA_BF16 && prob->head_dim != 128)
+    return fail(VDSA_ERR_UNSUPPORTED, "the bf16 backward supports head_dim 128 (got %d)", prob->head_dim);
+  for (View* in : {&bv.q, &bv.k, &bv.v, &bv.o, &bv.dout})
+    if ((s = check_view(prob, *in, false)) != VDSA_OK) return s;
+  for (View* out : {&bv.dq, &bv.dk, &bv.dv})
+    if ((s = check_view(prob, *out, true)) != VDSA_OK) return s;
+  if ((s = check_lse_in(prob, lse, "lse", l0, l1)) != VDSA_OK) return s;
+  const View* outs[3] = {&bv.dq, &bv.dk, &bv.dv};
+  for (int i = 0; i < 3; ++i) {
+    for (const View* in : {&bv.q, &bv.k, &bv.v, &bv.o, &bv.dout})
+      if (overlaps(outs[i]->lo, outs[i]->hi, in->lo, in->hi))
+        return fail(VDSA_ERR_ALIAS, "%s overlaps %s", outs[i]->name, in->name);
+    if (overlaps(outs[i]->lo, outs[i]->hi, l0, l1)) return fail(VDSA_ERR_ALIAS, "%s overlaps lse", outs[i]->name);
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i]->lo, outs[i]->hi, outs[j]->lo, outs[j]->hi))
+        return fail(VDSA_ERR_ALIAS, "%s overlaps %s", outs[i]->name, outs[j]->name);
+  }
+  return VDSA_OK;
+}
+
+vdsa_status check_workspace(const BwdViews& bv, uintptr_t l0, uintptr_t l1, void* workspace, size_t bytes,
+                            size_t need) {
+  if (!workspace) return fail(VDSA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (bytes < need) return fail(VDSA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", bytes, need);
+  if ((uintptr_t)workspace % 16 != 0) return fail(VDSA_ERR_ALIGN, "workspace is not 16-byte aligned");
+  const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + need;
+  for (const View* v : {&bv.q, &bv.k, &bv.v, &bv.o, &bv.dout, &bv.dq, &bv.dk, &bv.dv})
+    if (overlaps(w0, w1, v->lo, v->hi)) return fail(VDSA_ERR_ALIAS, "workspace overlaps %s", v->name);
+  if (overlaps(w0, w1, l0, l1)) return fail(VDSA_ERR_ALIAS, "workspace overlaps lse");
+  return VDSA_OK;
+}
+
+size_t delta_bytes(const vdsa_problem* p) { return align_up((size_t)p->batch * p->heads * n_tokens(p) * 4, 256); }
+
+vdsa::BoxBwdParams bwd_params(const vdsa_problem* prob, const BwdViews& bv, const float* lse, const float* delta) {
+  vdsa::BoxBwdParams P{};
+  P.q = bv.q.ptr; P.k = bv.k.ptr; P.v = bv.v.ptr; P.dout = bv.dout.ptr;
+  P.lse = lse;
+  P.delta = delta;
+  P.dq = const_cast<void*>(bv.dq.ptr); P.dk = const_cast<void*>(bv.dk.ptr); P.dv = const_cast<void*>(bv.dv.ptr);
+  P.q_sb = bv.q.st->b; P.q_sh = bv.q.st->h; P.q_sn = bv.q.st->n;
+  P.k_sb = bv.k.st->b; P.k_sh = bv.k.st->h; P.k_sn = bv.k.st->n;
+  P.v_sb = bv.v.st->b; P.v_sh = bv.v.st->h; P.v_sn = bv.v.st->n;
+  P.do_sb = bv.dout.st->b; P.do_sh = bv.dout.st->h; P.do_sn = bv.dout.st->n;
+  P.dq_sb = bv.dq.st->b; P.dq_sh = bv.dq.st->h; P.dq_sn = bv.dq.st->n;
+  P.dk_sb = bv.dk.st->b; P.dk_sh = bv.dk.st->h; P.dk_sn = bv.dk.st->n;
+  P.dv_sb = bv.dv.st->b; P.dv_sh = bv.dv.st->h; P.dv_sn = bv.dv.st->n;
+  P.n_q = n_tokens(prob);
+  P.n_k = n_tokens(prob);
+  P.head_dim = prob->head_dim;
+  P.scale = prob->scale;
+  P.g.batch = prob->batch;
+  P.g.heads = prob->heads;
+  P.g.scale_log2e = prob->scale * 1.4426950408889634f;
+  return P;
+}
+
+// Launch one backward pass over the geometry in P.g (own tiles from qT.. /
+// bT.. / sT.., iterated boxes from rT.. or dense_keys over kT..).
+vdsa_status launch_bwd_pass(const vdsa_problem* prob, vdsa::BoxBwdParams& P, bool kv, hipStream_t stream) {
+  const int bf16 = prob->dtype == VDSA_BF16;
+  const int bm = vdsa::attn_bwd_block_m(bf16);
+  vdsa::BoxAttnParams& g = P.g;
+  const int64_t mv = (int64_t)max_tile_extent(g.qT, g.bT, g.sT) * max_tile_extent(g.qH, g.bH, g.sH) *
+                     max_tile_extent(g.qW, g.bW, g.sW);
+  g.qblocks = (int32_t)((mv + bm - 1) / bm);
+  const int64_t total = (int64_t)g.batch * g.heads * g.nT * g.nH * g.nW * g.qblocks;
+  if (total >= (int64_t(1) << 31) / 512)
+    return fail(VDSA_ERR_SHAPE, "problem needs %lld workgroups, beyond the launch limit", (long long)total);
+  g.total_wg = (int32_t)total;
+  const hipError_t e = kv ? vdsa::launch_attn_bwd_dkdv(P, bf16, stream) : vdsa::launch_attn_bwd_dq(P, bf16, stream);
+  if (e != hipSuccess) return fail(VDSA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+  return VDSA_OK;
+}
+
+vdsa_status launch_delta(const vdsa_problem* prob, const BwdViews& bv, float* delta, hipStream_t stream) {
+  vdsa::RowDotParams rp{};
+  rp.a = bv.dout.ptr;
+  rp.b = bv.o.ptr;
+  rp.out = delta;
+  rp.a_sb = bv.dout.st->b; rp.a_sh = bv.dout.st->h; rp.a_sn = bv.dout.st->n;
+  rp.b_sb = bv.o.st->b; rp.b_sh = bv.o.st->h; rp.b_sn = bv.o.st->n;
+  rp.batch = prob->batch;
+  rp.heads = prob->heads;
+  rp.head_dim = prob->head_dim;
+  rp.n = n_tokens(prob);
+  const hipError_t e = vdsa::launch_rowdot(rp, prob->dtype == VDSA_BF16, stream);
+  if (e != hipSuccess) return fail(VDSA_ERR_HIP, "delta launch failed: %s", hipGetErrorString(e));
+  return VDSA_OK;
+}
+
+size_t pooled_f32_bytes(const vdsa_problem* p, const int32_t* pool) {
+  return align_up((size_t)p->batch * p->heads * pooled_tokens(p, pool) * p->head_dim * 4, 256);
+}
+
 }  // namespace
 
 extern "C" {
@@ -574,6 +677,143 @@ vdsa_status dual_branch_merge_lse(const vdsa_problem* prob, const void* o_local,
   mp.n_tokens = N;
   hipError_t e = vdsa::launch_merge(mp, prob->dtype == VDSA_BF16, (hipStream_t)stream);
   if (e != hipSuccess) return fail(VDSA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+vdsa_status sta_attn_bwd_workspace_size(const vdsa_problem* prob, size_t* bytes) {
+  vdsa_status s;
+  if ((s = check_problem(prob)) != VDSA_OK) return s;
+  if (!bytes) return fail(VDSA_ERR_NULL, "bytes is NULL");
+  *bytes = delta_bytes(prob);
+  return ok();
+}
+
+vdsa_status sta_attn_bwd(const vdsa_problem* prob, const vdsa_sta_cfg* cfg, const void* q,
+                         const vdsa_strides* q_strides, const void* k, const vdsa_strides* k_strides,
+                         const void* v, const vdsa_strides* v_strides, const void* o,
+                         const vdsa_strides* o_strides, const void* d_o, const vdsa_strides* do_strides,
+                         const float* lse, void* dq, const vdsa_strides* dq_strides, void* dk,
+                         const vdsa_strides* dk_strides, void* dv, const vdsa_strides* dv_strides,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  vdsa_status s;
+  if ((s = check_problem(prob)) != VDSA_OK) return s;
+  if ((s = check_sta_cfg(cfg)) != VDSA_OK) return s;
+  const int64_t N = n_tokens(prob);
+  BwdViews bv{{"q", q, q_strides, N},   {"k", k, k_strides, N},    {"v", v, v_strides, N},
+              {"o", o, o_strides, N},   {"d_o", d_o, do_strides, N}, {"dq", dq, dq_strides, N},
+              {"dk", dk, dk_strides, N}, {"dv", dv, dv_strides, N}};
+  uintptr_t l0, l1;
+  if ((s = check_bwd(prob, bv, lse, l0, l1)) != VDSA_OK) return s;
+  if ((s = check_workspace(bv, l0, l1, workspace, workspace_bytes, delta_bytes(prob))) != VDSA_OK) return s;
+
+  float* delta = (float*)workspace;
+  if ((s = launch_delta(prob, bv, delta, (hipStream_t)stream)) != VDSA_OK) return s;
+  vdsa::BoxBwdParams P = bwd_params(prob, bv, lse, delta);
+  vdsa::BoxAttnParams& g = P.g;
+  g.qT = prob->grid_t; g.qH = prob->grid_h; g.qW = prob->grid_w;
+  g.bT = cfg->tile[0]; g.bH = cfg->tile[1]; g.bW = cfg->tile[2];
+  g.sT = cfg->shift[0]; g.sH = cfg->shift[1]; g.sW = cfg->shift[2];
+  g.nT = tiles_along(g.qT, g.bT, g.sT);
+  g.nH = tiles_along(g.qH, g.bH, g.sH);
+  g.nW = tiles_along(g.qW, g.bW, g.sW);
+  g.rT = (cfg->window[0] - 1) / 2; g.rH = (cfg->window[1] - 1) / 2; g.rW = (cfg->window[2] - 1) / 2;
+  g.kT = g.qT; g.kH = g.qH; g.kW = g.qW;
+  g.dense_keys = 0;
+  // the window relation is symmetric: the dK/dV pass walks the same boxes
+  if ((s = launch_bwd_pass(prob, P, false, (hipStream_t)stream)) != VDSA_OK) return s;
+  if ((s = launch_bwd_pass(prob, P, true, (hipStream_t)stream)) != VDSA_OK) return s;
+  return ok();
+}
+
+vdsa_status global_pooled_attn_bwd_workspace_size(const vdsa_problem* prob, const int32_t pool_hw[2],
+                                                  size_t* bytes) {
+  vdsa_status s;
+  if ((s = check_problem(prob)) != VDSA_OK) return s;
+  if ((s = check_pool(prob, pool_hw)) != VDSA_OK) return s;
+  if (!bytes) return fail(VDSA_ERR_NULL, "bytes is NULL");
+  *bytes = delta_bytes(prob) + 2 * pooled_bytes(prob, pool_hw) + 2 * pooled_f32_bytes(prob, pool_hw);
+  return ok();
+}
+
+vdsa_status global_pooled_attn_bwd(const vdsa_problem* prob, const int32_t pool_hw[2], const void* q,
+                                   const vdsa_strides* q_strides, const void* k, const vdsa_strides* k_strides,
+                                   const void* v, const vdsa_strides* v_strides, const void* o,
+                                   const vdsa_strides* o_strides, const void* d_o, const vdsa_strides* do_strides,
+                                   const float* lse, void* dq, const vdsa_strides* dq_strides, void* dk,
+                                   const vdsa_strides* dk_strides, void* dv, const vdsa_strides* dv_strides,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  vdsa_status s;
+  if ((s = check_problem(prob)) != VDSA_OK) return s;
+  if ((s = check_pool(prob, pool_hw)) != VDSA_OK) return s;
+  const int64_t N = n_tokens(prob);
+  const int64_t M = pooled_tokens(prob, pool_hw);
+  BwdViews bv{{"q", q, q_strides, N},   {"k", k, k_strides, N},    {"v", v, v_strides, N},
+              {"o", o, o_strides, N},   {"d_o", d_o, do_strides, N}, {"dq", dq, dq_strides, N},
+              {"dk", dk, dk_strides, N}, {"dv", dv, dv_strides, N}};
+  uintptr_t l0, l1;
+  if ((s = check_bwd(prob, bv, lse, l0, l1)) != VDSA_OK) return s;
+  const size_t need = delta_bytes(prob) + 2 * pooled_bytes(prob, pool_hw) + 2 * pooled_f32_bytes(prob, pool_hw);
+  if ((s = check_workspace(bv, l0, l1, workspace, workspace_bytes, need)) != VDSA_OK) return s;
+
+  char* ws = (char*)workspace;
+  float* delta = (float*)ws;
+  void* kp = ws + delta_bytes(prob);
+  void* vp = (char*)kp + pooled_bytes(prob, pool_hw);
+  float* dkp = (float*)((char*)vp + pooled_bytes(prob, pool_hw));
+  float* dvp = (float*)((char*)dkp + pooled_f32_bytes(prob, pool_hw));
+  const hipStream_t st = (hipStream_t)stream;
+  if ((s = launch_delta(prob, bv, delta, st)) != VDSA_OK) return s;
+  vdsa_strides ps{(int64_t)prob->heads * M * prob->head_dim, M * prob->head_dim, prob->head_dim};
+  hipError_t e = vdsa::launch_avgpool(pool_params(prob, pool_hw, k, k_strides, kp, &ps), prob->dtype == VDSA_BF16, st);
+  if (e == hipSuccess)
+    e = vdsa::launch_avgpool(pool_params(prob, pool_hw, v, v_strides, vp, &ps), prob->dtype == VDSA_BF16, st);
+  if (e != hipSuccess) return fail(VDSA_ERR_HIP, "pooling launch failed: %s", hipGetErrorString(e));
+  const int Hp = (prob->grid_h + pool_hw[0] - 1) / pool_hw[0], Wp = (prob->grid_w + pool_hw[1] - 1) / pool_hw[1];
+
+  // dQ pass: the forward's geometry (one query tile over the grid, every
+  // pooled key)
+  vdsa::BoxBwdParams P = bwd_params(prob, bv, lse, delta);
+  P.k = kp; P.v = vp;
+  P.k_sb = ps.b; P.k_sh = ps.h; P.k_sn = ps.n;
+  P.v_sb = ps.b; P.v_sh = ps.h; P.v_sn = ps.n;
+  P.n_k = M;
+  vdsa::BoxAttnParams& g = P.g;
+  g.qT = prob->grid_t; g.qH = prob->grid_h; g.qW = prob->grid_w;
+  g.bT = g.qT; g.bH = g.qH; g.bW = g.qW;
+  g.nT = g.nH = g.nW = 1;
+  g.kT = prob->grid_t; g.kH = Hp; g.kW = Wp;
+  g.dense_keys = 1;
+  if ((s = launch_bwd_pass(prob, P, false, st)) != VDSA_OK) return s;
+
+  // dK/dV pass: own rows = pooled keys (one tile over the pooled grid), every
+  // query iterated; fp32 gradients of the pooled keys into the workspace
+  vdsa::BoxBwdParams Pk = P;
+  Pk.dk = dkp; Pk.dv = dvp;
+  Pk.dk_sb = ps.b; Pk.dk_sh = ps.h; Pk.dk_sn = ps.n;
+  Pk.dv_sb = ps.b; Pk.dv_sh = ps.h; Pk.dv_sn = ps.n;
+  Pk.grad_f32 = 1;
+  vdsa::BoxAttnParams& gk = Pk.g;
+  gk.qT = prob->grid_t; gk.qH = Hp; gk.qW = Wp;
+  gk.bT = gk.qT; gk.bH = gk.qH; gk.bW = gk.qW;
+  gk.nT = gk.nH = gk.nW = 1;
+  gk.kT = prob->grid_t; gk.kH = prob->grid_h; gk.kW = prob->grid_w;
+  gk.dense_keys = 1;
+  if ((s = launch_bwd_pass(prob, Pk, true, st)) != VDSA_OK) return s;
+
+  // through the pooling: every token of a cell gets the cell's gradient / count
+  for (int which = 0; which < 2; ++which) {
+    vdsa::UnpoolParams up{};
+    up.gp = which == 0 ? dkp : dvp;
+    up.g = which == 0 ? dk : dv;
+    const vdsa_strides* gs = which == 0 ? dk_strides : dv_strides;
+    up.g_sb = gs->b; up.g_sh = gs->h; up.g_sn = gs->n;
+    up.batch = prob->batch; up.heads = prob->heads; up.head_dim = prob->head_dim;
+    up.T = prob->grid_t; up.H = prob->grid_h; up.W = prob->grid_w;
+    up.kh = pool_hw[0]; up.kw = pool_hw[1];
+    up.Hp = Hp; up.Wp = Wp;
+    e = vdsa::launch_unpool_grad(up, prob->dtype == VDSA_BF16, st);
+    if (e != hipSuccess) return fail(VDSA_ERR_HIP, "pooling-gradient launch failed: %s", hipGetErrorString(e));
+  }
   return ok();
 }
 

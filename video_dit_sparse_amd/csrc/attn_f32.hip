@@ -14,14 +14,6 @@ constexpr int QPB = 64;        // queries per workgroup
 constexpr int KPB = 32;        // keys per LDS stage
 constexpr int NTHREADS = 256;  // 4 lanes per query
 
-__device__ __forceinline__ int xcd_remap(int hw, int total) {
-  constexpr int NX = 8;
-  const int per = total / NX, extra = total % NX;
-  const int xcd = hw % NX, slot = hw / NX;
-  const int base = xcd < extra ? xcd * (per + 1) : extra * (per + 1) + (xcd - extra) * per;
-  return base + slot;
-}
-
 template <int HD>
 __global__ __launch_bounds__(NTHREADS) void box_attn_f32_kernel(const BoxAttnParams p) {
   constexpr int DPL = HD / 4;  // head_dim elements per lane

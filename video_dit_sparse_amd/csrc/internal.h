@@ -89,6 +89,67 @@ struct MergeParams {
   int64_t n_tokens;
 };
 
+// Backward pass of box attention.  `g` carries the geometry: the pass's own
+// rows are cut into the tiles of g (qT.. / bT.. / sT.. / nT..), and each own
+// tile iterates the box of tokens given by g's key side (rT.. or dense_keys
+// over kT, kH, kW); g's pointers are unused.
+//   dQ pass:    own rows = queries (Q, dO in registers), iterated = their key
+//               boxes (K, V), exactly the forward's geometry.
+//   dK/dV pass: own rows = keys (K, V in registers), iterated = the queries
+//               whose windows contain the key tile.  The window relation
+//               |a - c| <= r is symmetric, so for sliding tiles this is the
+//               box around the key tile on the same lattice; for pooled keys
+//               (one tile over the pooled grid) it is every query (dense_keys
+//               over the query grid).
+struct BoxBwdParams {
+  BoxAttnParams g;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* lse;     // forward LSE (natural log), [batch, heads, n_q] contiguous
+  const float* delta;   // rowsum(dO * O), [batch, heads, n_q] contiguous
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t q_sb, q_sh, q_sn;   // element strides
+  int64_t k_sb, k_sh, k_sn;
+  int64_t v_sb, v_sh, v_sn;
+  int64_t do_sb, do_sh, do_sn;
+  int64_t dq_sb, dq_sh, dq_sn;
+  int64_t dk_sb, dk_sh, dk_sn;
+  int64_t dv_sb, dv_sh, dv_sn;
+  int64_t n_q;                // query tokens per head
+  int64_t n_k;                // key tokens per head
+  int32_t grad_f32;           // dK/dV pass: store fp32 gradients (else the I/O dtype)
+  int32_t head_dim;
+  float scale;                // softmax scale
+};
+
+// rowsum(dO * O) per row of [batch, heads, n, head_dim] tensors into
+// delta [batch, heads, n] fp32 contiguous.
+struct RowDotParams {
+  const void* a;
+  const void* b;
+  float* out;
+  int64_t a_sb, a_sh, a_sn;
+  int64_t b_sb, b_sh, b_sn;
+  int32_t batch, heads, head_dim;
+  int64_t n;
+};
+
+// Gradient of k_h x k_w frame-wise average pooling: every token of a cell
+// receives the cell's fp32 gradient divided by the cell's token count.
+struct UnpoolParams {
+  const float* gp;   // [batch, heads, M, head_dim] fp32 contiguous
+  void* g;           // [batch, heads, N, head_dim] in the I/O dtype, strided
+  int64_t g_sb, g_sh, g_sn;
+  int32_t batch, heads, head_dim;
+  int32_t T, H, W;
+  int32_t kh, kw;
+  int32_t Hp, Wp;
+};
+
 // Launchers: return hipSuccess or the launch error.  They assume the
 // parameters were validated.
 hipError_t launch_box_attn_bf16(const BoxAttnParams& p, int head_dim, hipStream_t stream);
@@ -100,5 +161,12 @@ hipError_t launch_box_attn_bf16_pp(const BoxAttnParams& p, hipStream_t stream);
 hipError_t launch_box_attn_f32(const BoxAttnParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_avgpool(const PoolParams& p, int bf16, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int bf16, hipStream_t stream);
+// backward: bf16 head_dim 128 on the matrix cores, fp32 (head_dim 64, 128)
+// on the vector ALU; grad_f32 applies to the fp32 kernel trivially
+hipError_t launch_attn_bwd_dq(const BoxBwdParams& p, int bf16, hipStream_t stream);
+hipError_t launch_attn_bwd_dkdv(const BoxBwdParams& p, int bf16, hipStream_t stream);
+int attn_bwd_block_m(int bf16);   // own rows per workgroup
+hipError_t launch_rowdot(const RowDotParams& p, int bf16, hipStream_t stream);
+hipError_t launch_unpool_grad(const UnpoolParams& p, int bf16, hipStream_t stream);
 
 }  // namespace vdsa
