@@ -102,6 +102,8 @@ def main():
     ap.add_argument("--workload", default="sta_720p")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget (0 = skip)")
     ap.add_argument("--dense-steps", type=int, default=3, help="full-window comparison calls (0 = skip)")
+    ap.add_argument("--bwd-steps", type=int, default=3,
+                    help="backward-pass calls of the local branch to time (0 = skip)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc runs)")
     args = ap.parse_args()
@@ -209,6 +211,35 @@ def main():
             "merge_lse_hbm_frac": round(merge_lse_bytes / (merge_lse_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         log(f"[bench] global branch: fused {fused_ms:.3f} ms, global then merge {unfused_ms:.3f} ms; "
             f"LSE merge {merge_lse_ms:.3f} ms ({merge_lse_bytes / (merge_lse_ms * 1e-3) / 1e9:.0f} GB/s)")
+    if args.bwd_steps > 0:
+        # backward of the local branch (first lattice shift): dQ, dK, dV from
+        # the forward's output and LSE; effective work 10 * head_dim FLOP per
+        # attended pair (S, dP, dV, dQ, dK), 2.5x the forward's
+        lse_f = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        o_f = V.sta_attn_fwd(q, k, v, w.grid, w.tile, w.window, w.shifts[0], scale=w.softmax_scale, lse=lse_f)[0]
+        do = WL.make_tensor(q.shape, q.dtype, dev, seed=99)
+        grads = [torch.empty_like(q) for _ in range(3)]
+        ws = torch.empty(V.sta_attn_bwd_workspace_size(w.batch, w.heads, w.head_dim, w.grid,
+                                                       1 if w.dtype == "bf16" else 0),
+                         dtype=torch.uint8, device=dev)
+        def bwd():
+            V.sta_attn_bwd(q, k, v, o_f, do, lse_f, w.grid, w.tile, w.window, w.shifts[0],
+                           scale=w.softmax_scale, dq=grads[0], dk=grads[1], dv=grads[2], workspace=ws)
+        bwd()
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record(stream)
+        for _ in range(args.bwd_steps):
+            bwd()
+        b1.record(stream)
+        torch.cuda.synchronize()
+        bwd_ms = b0.elapsed_time(b1) / args.bwd_steps
+        bwd_flops = 2.5 * fl["local"] / len(w.shifts)
+        extra["backward"] = {"call": "sta_attn_bwd", "ms_per_call": round(bwd_ms, 3),
+                             "effective_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 1),
+                             "effective_flop_per_call": bwd_flops,
+                             "frac_of_peak": round(bwd_flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        log(f"[bench] backward: {bwd_ms:.2f} ms per call, {bwd_flops / (bwd_ms * 1e-3) / 1e12:.1f} effective TFLOP/s")
+        del grads, do, o_f, lse_f
     if args.dense_steps > 0 and w.pool_hw is None:
         # the same kernel with a window covering the whole tile lattice = dense attention
         n_tiles = [-(-(L + s) // b) for L, b, s in zip(w.grid, w.tile, w.shifts[0])]

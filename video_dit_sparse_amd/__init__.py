@@ -21,5 +21,6 @@ from ._lib import (  # noqa: F401
     lib,
     sta_attn_fwd,
     sta_attn_bwd,
+    sta_attn_bwd_workspace_size,
     sta_flops,
 )

@@ -304,6 +304,13 @@ def _bwd_outputs(q, dq, dk, dv):
     return tuple(torch.empty_like(q, memory_format=torch.contiguous_format) if t is None else t for t in (dq, dk, dv))
 
 
+def sta_attn_bwd_workspace_size(batch, heads, head_dim, grid, dtype_code=VDSA_BF16) -> int:
+    prob = make_problem(batch, heads, head_dim, grid, dtype_code, 1.0)
+    n = ctypes.c_size_t()
+    check(lib().sta_attn_bwd_workspace_size(ctypes.byref(prob), ctypes.byref(n)))
+    return n.value
+
+
 def sta_attn_bwd(q, k, v, o, do, lse, grid, tile, window, shift=(0, 0, 0), scale=None, dq=None, dk=None, dv=None,
                  workspace=None, stream=None):
     """Gradients of ``sta_attn_fwd`` (``sta_attn_bwd`` in include/vdsa.h), from
