@@ -22,6 +22,9 @@ from .ref import (  # noqa: F401
     merge_ref,
     merge_lse_ref,
     union_attention_ref,
+    upsample_bilinear_ref,
+    compressed_global_ref,
+    hier_pooled_ref,
     attention_bwd_ref,
     sta_bwd_ref,
     global_bwd_ref,

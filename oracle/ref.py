@@ -47,7 +47,8 @@ __all__ = [
     "to_f64", "token_coords", "tile_index", "tile_counts", "tile_extent",
     "window_radius", "sta_mask_row", "sta_ref", "dense_ref",
     "attention_weights_ref", "pooled_grid", "pool_ref", "global_ref",
-    "merge_ref", "merge_lse_ref", "union_attention_ref", "attention_bwd_ref", "sta_bwd_ref",
+    "merge_ref", "merge_lse_ref", "union_attention_ref", "upsample_bilinear_ref",
+    "compressed_global_ref", "hier_pooled_ref", "attention_bwd_ref", "sta_bwd_ref",
     "global_bwd_ref", "sta_pair_count_ref",
     "sta_flops_ref", "global_flops_ref", "dense_flops_ref",
 ]
@@ -300,6 +301,78 @@ def union_attention_ref(q, k, v, grid, tile, window, shift, k_pooled, v_pooled, 
         kk = np.concatenate([k[keys], kp], axis=0)
         vv = np.concatenate([v[keys], vp], axis=0)
         oj, lj = _softmax_attend(q[n:n + 1], kk, vv, scale)
+        o[j], lse[j] = oj[0], lj[0]
+    return o, lse
+
+
+def upsample_bilinear_ref(xp, grid, pool_hw):
+    """Frame-wise bilinear upsampling of a pooled [T*Hp*Wp, D] tensor back to
+    the grid's H x W (UltraGen §4.2: bilinear upsampling restores the latent
+    resolution; here without the learned 3D convolution that follows it).
+    Half-pixel sample positions: output row y samples pooled row
+    max((y + 1/2) Hp/H - 1/2, 0), interpolating the two nearest rows (the
+    last row repeats at the far edge); the same along W.
+    """
+    xp = to_f64(xp)
+    T, H, W = grid
+    _, Hp, Wp = pooled_grid(grid, pool_hw)
+    x = xp.reshape(T, Hp, Wp, -1)
+
+    def taps(n_out, n_in):
+        i0 = np.empty(n_out, dtype=np.int64)
+        i1 = np.empty(n_out, dtype=np.int64)
+        lam = np.empty(n_out)
+        for y in range(n_out):
+            src = max((y + 0.5) * n_in / n_out - 0.5, 0.0)
+            a = int(math.floor(src))
+            i0[y], i1[y], lam[y] = a, min(a + 1, n_in - 1), src - a
+        return i0, i1, lam
+    y0, y1, ly = taps(H, Hp)
+    x0, x1, lx = taps(W, Wp)
+    out = np.empty((T, H, W, x.shape[-1]))
+    for y in range(H):
+        for xx in range(W):
+            out[:, y, xx] = ((1 - ly[y]) * (1 - lx[xx]) * x[:, y0[y], x0[xx]] + (1 - ly[y]) * lx[xx] * x[:, y0[y], x1[xx]]
+                             + ly[y] * (1 - lx[xx]) * x[:, y1[y], x0[xx]] + ly[y] * lx[xx] * x[:, y1[y], x1[xx]])
+    return out.reshape(T * H * W, -1)
+
+
+def compressed_global_ref(q, k, v, grid, pool_hw, scale=None):
+    """UltraGen's compressed global attention (§4.2, App. B's (THW)^2 D / K^4
+    term): Q, K and V pooled k_h x k_w within each frame, full attention among
+    the pooled tokens, bilinear upsampling of the pooled output to the grid."""
+    qp, kp, vp = (pool_ref(x, grid, pool_hw) for x in (q, k, v))
+    if scale is None:
+        scale = 1.0 / math.sqrt(qp.shape[1])
+    op, _ = dense_ref(qp, kp, vp, scale=scale)
+    return upsample_bilinear_ref(op, grid, pool_hw)
+
+
+def hier_pooled_ref(q, k, v, grid, tile, window, shift, pool_hw, scale=None, rows=None):
+    """Intermediate-scale attention (UltraGen §4.3 hierarchical local
+    attention; App. B's (THW)^2 D / (4 K^2) term for 2 x 2 pooling): each
+    full-resolution query attends the k_h x k_w pooled keys and values of its
+    sliding-tile window, i.e. every pooling cell that holds a token of the
+    window (``sta_mask_row``'s keys mapped to their cells).  Returns (O, LSE).
+    """
+    q = to_f64(q)
+    N, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    kp, vp = pool_ref(k, grid, pool_hw), pool_ref(v, grid, pool_hw)
+    T, H, W = grid
+    kh, kw = pool_hw
+    _, Hp, Wp = pooled_grid(grid, pool_hw)
+    coords = token_coords(grid)
+    cell = (coords[:, 0] * Hp + coords[:, 1] // kh) * Wp + coords[:, 2] // kw
+    radius = window_radius(window)
+    ti = tile_index(coords, tile, shift)
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.empty((len(rows), D))
+    lse = np.empty(len(rows))
+    for j, n in enumerate(rows):
+        cells = np.unique(cell[sta_mask_row(ti, ti[n], radius)])
+        oj, lj = _softmax_attend(q[n:n + 1], kp[cells], vp[cells], scale)
         o[j], lse[j] = oj[0], lj[0]
     return o, lse
 

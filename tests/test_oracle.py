@@ -524,3 +524,69 @@ def test_global_bwd_ragged_cells_finite_differences():
                 dn[which][n, d] -= eps
                 fd[n, d] = (loss(*up) - loss(*dn)) / (2 * eps)
         np.testing.assert_allclose(grads[which], fd, rtol=0, atol=1e-7)
+
+
+# ---------------------------------------------------------------- compressed global, hierarchical windows
+@pytest.mark.parametrize("grid,pool", [((2, 8, 12), (4, 4)), ((3, 9, 10), (4, 3)), ((1, 6, 5), (2, 2)),
+                                       ((2, 4, 4), (1, 1))])
+def test_upsample_matches_torch_bilinear(grid, pool):
+    T, H, W = grid
+    _, Hp, Wp = R.pooled_grid(grid, pool)
+    xp = randn(300, T * Hp * Wp, 3)
+    ref = torch.nn.functional.interpolate(torch.from_numpy(xp.reshape(T, Hp, Wp, 3)).permute(0, 3, 1, 2),
+                                          size=(H, W), mode="bilinear", align_corners=False)
+    ref = ref.permute(0, 2, 3, 1).reshape(-1, 3).numpy()
+    np.testing.assert_allclose(R.upsample_bilinear_ref(xp, grid, pool), ref, rtol=0, atol=1e-12)
+
+
+def test_upsample_constant_and_identity():
+    grid = (2, 6, 9)
+    c = np.full((2 * 2 * 3, 4), 1.25)
+    np.testing.assert_allclose(R.upsample_bilinear_ref(c, grid, (3, 3)), 1.25, atol=1e-15)
+    x = randn(301, 2 * 6 * 9, 4)
+    np.testing.assert_allclose(R.upsample_bilinear_ref(x, grid, (1, 1)), x, atol=1e-15)
+
+
+def test_compressed_global_special_cases():
+    grid = (2, 4, 6)
+    N = 48
+    q, k, v = randn(310, N, 8), randn(311, N, 8), randn(312, N, 8)
+    # no pooling: plain dense attention
+    np.testing.assert_allclose(R.compressed_global_ref(q, k, v, grid, (1, 1)), R.dense_ref(q, k, v)[0], atol=1e-13)
+    # one cell per frame: every output row of a frame is that frame's pooled
+    # value (one key; the upsampling of a 1x1 frame is constant)
+    o = R.compressed_global_ref(q, k, v, grid, (4, 6))
+    vbar = v.reshape(2, 24, 8).mean(axis=1)
+    frame_of = np.arange(N) // 24
+    np.testing.assert_allclose(o, R.dense_ref(R.pool_ref(q, grid, (4, 6)), R.pool_ref(k, grid, (4, 6)),
+                                              R.pool_ref(v, grid, (4, 6)))[0][frame_of], atol=1e-13)
+    np.testing.assert_allclose(R.dense_ref(np.zeros((1, 8)), R.pool_ref(k, grid, (4, 6)), vbar)[0][0],
+                               vbar.mean(axis=0), atol=1e-14)
+
+
+@pytest.mark.parametrize("grid,tile,window,shift,pool", [
+    ((3, 8, 12), (1, 4, 4), (1, 1, 3), (0, 0, 0), (2, 2)),
+    ((2, 9, 10), (2, 3, 4), (1, 3, 1), (1, 1, 2), (2, 2)),
+])
+def test_hier_pooled_by_explicit_cells(grid, tile, window, shift, pool):
+    # pooled keys of a query = the cells holding a token of its window,
+    # found here through a dense token -> cell assignment built with numpy
+    T, H, W = grid
+    N = T * H * W
+    q, k, v = randn(320, N, 6), randn(321, N, 6), randn(322, N, 6)
+    o, lse = R.hier_pooled_ref(q, k, v, grid, tile, window, shift, pool, scale=0.5)
+    mask = _sta_mask_by_coords(grid, tile, window, shift)
+    c = coords_lib(grid)
+    Hp, Wp = -(-H // pool[0]), -(-W // pool[1])
+    cell = (c[:, 0] * Hp + c[:, 1] // pool[0]) * Wp + c[:, 2] // pool[1]
+    kp, vp = R.pool_ref(k, grid, pool), R.pool_ref(v, grid, pool)
+    for n in range(0, N, 7):
+        cells = sorted(set(cell[mask[n]].tolist()))
+        ref_o, ref_l = R.dense_ref(q[n:n + 1], kp[cells], vp[cells], scale=0.5)
+        np.testing.assert_allclose(o[n], ref_o[0], atol=1e-13)
+        np.testing.assert_allclose(lse[n], ref_l[0], atol=1e-13)
+    # unit pooling: plain sliding-tile attention
+    o1, l1 = R.hier_pooled_ref(q, k, v, grid, tile, window, shift, (1, 1), scale=0.5)
+    so, sl = R.sta_ref(q, k, v, grid, tile, window, shift, scale=0.5)
+    np.testing.assert_allclose(o1, so, atol=1e-13)
+    np.testing.assert_allclose(l1, sl, atol=1e-13)
