@@ -240,6 +240,52 @@ vdsa_status global_pooled_attn_merge_fwd(const vdsa_problem* prob, const int32_t
                                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * hier_pooled_attn_fwd - intermediate-scale windowed attention (UltraGen
+ * section 4.3 "Cross-window Hierarchical Local Attention": attention over
+ * coarse windows; its cost term in App. B "Efficiency Analysis" is that of
+ * full-resolution queries against 2x2-pooled keys within each window).  Each
+ * query attends the pooled K/V (pool_hw = [ph, pw] cell means within each
+ * frame, as global_pooled_attn_fwd) of every pooling cell that holds a token
+ * of its sliding-tile window (cfg as in sta_attn_fwd, on the full grid):
+ *   O[n] = sum_c softmax_c(scale * Q[n].Kp[c]) Vp[c],  c over those cells.
+ * With tiles and shifts that are multiples of the pooling these are exactly
+ * the pooled tokens of the window.
+ *
+ *   workspace : at least hier_pooled_attn_workspace_size() bytes (pooled K
+ *               then pooled V, as in global_pooled_attn_fwd).
+ * Errors: as sta_attn_fwd and global_pooled_attn_fwd.
+ */
+vdsa_status hier_pooled_attn_workspace_size(const vdsa_problem* prob, const int32_t pool_hw[2], size_t* bytes);
+vdsa_status hier_pooled_attn_fwd(const vdsa_problem* prob, const vdsa_sta_cfg* cfg, const int32_t pool_hw[2],
+                                 const void* q, const vdsa_strides* q_strides,
+                                 const void* k, const vdsa_strides* k_strides,
+                                 const void* v, const vdsa_strides* v_strides,
+                                 void* o, const vdsa_strides* o_strides, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * compressed_global_attn_fwd - UltraGen's own compressed global attention
+ * (section 4.2 "Spatially-Compressed Global Attention"; App. B's
+ * (THW)^2 D / K^4 term): Q, K and V pooled pool_hw within each frame, full
+ * attention among the pooled tokens, then frame-wise bilinear upsampling of
+ * the pooled output back to the grid (half-pixel sample positions, edge rows
+ * and columns repeated; the pages' learned 3D convolution after it is not
+ * part of this call).
+ *
+ *   workspace : at least compressed_global_attn_workspace_size() bytes
+ *               (pooled Q, K, V and the pooled output).
+ * Errors: as global_pooled_attn_fwd.
+ */
+vdsa_status compressed_global_attn_workspace_size(const vdsa_problem* prob, const int32_t pool_hw[2],
+                                                  size_t* bytes);
+vdsa_status compressed_global_attn_fwd(const vdsa_problem* prob, const int32_t pool_hw[2],
+                                       const void* q, const vdsa_strides* q_strides,
+                                       const void* k, const vdsa_strides* k_strides,
+                                       const void* v, const vdsa_strides* v_strides,
+                                       void* o, const vdsa_strides* o_strides,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Backward passes.  Gradients of a forward call's output O given dO, from the
  * forward's inputs, its output O and its LSE (natural log, as written by the
  * forward's `lse` argument).  With P the attention weights of a query row:

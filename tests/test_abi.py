@@ -236,6 +236,29 @@ def test_backward_checks():
     assert gb(pl=(ctypes.c_int32 * 2)(0, 4)) == L.STATUS["VDSA_ERR_WINDOW"]
 
 
+def test_variant_checks():
+    p = prob()
+    d = st(p)
+    c = cfg()
+    pool = (ctypes.c_int32 * 2)(2, 2)
+    n = ctypes.c_size_t()
+    assert L.lib().hier_pooled_attn_workspace_size(ctypes.byref(p), pool, ctypes.byref(n)) == 0
+    h = lambda wsb, pl=pool, cc=c: L.lib().hier_pooled_attn_fwd(
+        ctypes.byref(p), ctypes.byref(cc), pl, Q, ctypes.byref(d), K, ctypes.byref(d), V, ctypes.byref(d),
+        O, ctypes.byref(d), None, WS, wsb, None)
+    assert h(n.value - 1) == L.STATUS["VDSA_ERR_WORKSPACE"]
+    assert h(n.value, (ctypes.c_int32 * 2)(2, 0)) == L.STATUS["VDSA_ERR_WINDOW"]
+    assert h(n.value, pool, cfg(window=(2, 3, 3))) == L.STATUS["VDSA_ERR_WINDOW"]
+    m = ctypes.c_size_t()
+    assert L.lib().compressed_global_attn_workspace_size(ctypes.byref(p), pool, ctypes.byref(m)) == 0
+    assert m.value == 2 * n.value
+    g = lambda wsb, o=O: L.lib().compressed_global_attn_fwd(
+        ctypes.byref(p), pool, Q, ctypes.byref(d), K, ctypes.byref(d), V, ctypes.byref(d), o, ctypes.byref(d),
+        WS, wsb, None)
+    assert g(m.value - 1) == L.STATUS["VDSA_ERR_WORKSPACE"]
+    assert g(m.value, Q + 256) == L.STATUS["VDSA_ERR_ALIAS"]
+
+
 FLOP_CASES = [
     ((4, 8, 8), (2, 4, 4), (3, 3, 3), (0, 0, 0)),
     ((30, 48, 80), (6, 8, 8), (3, 3, 5), (0, 0, 0)),

@@ -4,12 +4,15 @@ Python face of libvdsa.so: the three calls of the hot path
 (``sta_attn_fwd``, ``global_pooled_attn_fwd``, ``dual_branch_merge``), the
 exact log-sum-exp merge (``dual_branch_merge_lse``), the global branch with
 either merge fused into it (``global_pooled_attn_merge_fwd``), the pooling
-step alone (``kv_avgpool_fwd``), the backward passes (``sta_attn_bwd``,
+step alone (``kv_avgpool_fwd``), UltraGen's hierarchical and compressed
+global variants (``hier_pooled_attn_fwd``, ``compressed_global_attn_fwd``),
+the backward passes (``sta_attn_bwd``,
 ``global_pooled_attn_bwd``) and the effective-work counters.
 """
 from ._lib import (  # noqa: F401
     VdsaError,
     abi_version,
+    compressed_global_attn_fwd,
     dual_branch_merge,
     dual_branch_merge_lse,
     global_flops,
@@ -17,6 +20,7 @@ from ._lib import (  # noqa: F401
     global_pooled_attn_merge_fwd,
     global_pooled_attn_bwd,
     global_pooled_attn_workspace_size,
+    hier_pooled_attn_fwd,
     kv_avgpool_fwd,
     lib,
     sta_attn_fwd,

@@ -28,6 +28,8 @@ STATUS = {v: k for k, v in STATUS_NAMES.items()}
 EXPORTED = [
     "sta_attn_fwd", "global_pooled_attn_workspace_size", "global_pooled_attn_fwd",
     "dual_branch_merge", "dual_branch_merge_lse", "global_pooled_attn_merge_fwd",
+    "hier_pooled_attn_workspace_size", "hier_pooled_attn_fwd", "compressed_global_attn_workspace_size",
+    "compressed_global_attn_fwd",
     "sta_attn_bwd_workspace_size", "sta_attn_bwd", "global_pooled_attn_bwd_workspace_size",
     "global_pooled_attn_bwd",
     "kv_avgpool_fwd", "vdsa_sta_flops", "vdsa_global_flops",
@@ -80,6 +82,10 @@ def lib() -> ctypes.CDLL:
     L.global_pooled_attn_merge_fwd.argtypes = [P, i32p, vp, S, vp, S, vp, S, ctypes.c_int, vp, S, fp, fp, fp,
                                                vp, S, fp, vp, ctypes.c_size_t, vp]
     L.kv_avgpool_fwd.argtypes = [P, i32p, vp, S, vp, S, vp]
+    L.hier_pooled_attn_workspace_size.argtypes = [P, i32p, ctypes.POINTER(ctypes.c_size_t)]
+    L.hier_pooled_attn_fwd.argtypes = [P, C, i32p, vp, S, vp, S, vp, S, vp, S, fp, vp, ctypes.c_size_t, vp]
+    L.compressed_global_attn_workspace_size.argtypes = [P, i32p, ctypes.POINTER(ctypes.c_size_t)]
+    L.compressed_global_attn_fwd.argtypes = [P, i32p, vp, S, vp, S, vp, S, vp, S, vp, ctypes.c_size_t, vp]
     L.sta_attn_bwd_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     L.sta_attn_bwd.argtypes = [P, C, vp, S, vp, S, vp, S, vp, S, vp, S, fp, vp, S, vp, S, vp, S,
                                vp, ctypes.c_size_t, vp]
@@ -297,6 +303,48 @@ def global_pooled_attn_merge_fwd(q, k, v, grid, pool_hw, o_local, mode="gated", 
         _lse_arg(lse_out, (B, Hh, N), "lse_out") if lse_out is not None else None,
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
     return (o, lse_out) if (return_lse or lse_out is not None) else o
+
+
+def hier_pooled_attn_fwd(q, k, v, grid, tile, window, pool_hw, shift=(0, 0, 0), scale=None, out=None, lse=None,
+                         return_lse=False, workspace=None, stream=None):
+    """Full-resolution queries against the pooled K/V of their sliding-tile
+    window (``hier_pooled_attn_fwd``).  Returns O (and LSE)."""
+    torch = _torch()
+    _same(q, k, v)
+    prob = _problem_for(q, grid, scale)
+    cfg = make_cfg(tile, window, shift)
+    need = ctypes.c_size_t()
+    check(lib().hier_pooled_attn_workspace_size(ctypes.byref(prob), _pool(pool_hw), ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    if lse is None and return_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    check(lib().hier_pooled_attn_fwd(
+        ctypes.byref(prob), ctypes.byref(cfg), _pool(pool_hw), q.data_ptr(), ctypes.byref(_strides(q)),
+        k.data_ptr(), ctypes.byref(_strides(k)), v.data_ptr(), ctypes.byref(_strides(v)),
+        o.data_ptr(), ctypes.byref(_strides(o)), lse.data_ptr() if lse is not None else None,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return (o, lse) if (return_lse or lse is not None) else o
+
+
+def compressed_global_attn_fwd(q, k, v, grid, pool_hw, scale=None, out=None, workspace=None, stream=None):
+    """Pooled Q, K, V, full attention among pooled tokens, bilinear upsampling
+    (``compressed_global_attn_fwd``).  Returns O."""
+    torch = _torch()
+    _same(q, k, v)
+    prob = _problem_for(q, grid, scale)
+    need = ctypes.c_size_t()
+    check(lib().compressed_global_attn_workspace_size(ctypes.byref(prob), _pool(pool_hw), ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    check(lib().compressed_global_attn_fwd(
+        ctypes.byref(prob), _pool(pool_hw), q.data_ptr(), ctypes.byref(_strides(q)),
+        k.data_ptr(), ctypes.byref(_strides(k)), v.data_ptr(), ctypes.byref(_strides(v)),
+        o.data_ptr(), ctypes.byref(_strides(o)),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o
 
 
 def _bwd_outputs(q, dq, dk, dv):

@@ -474,6 +474,35 @@ size_t pooled_f32_bytes(const vdsa_problem* p, const int32_t* pool) {
   return align_up((size_t)p->batch * p->heads * pooled_tokens(p, pool) * p->head_dim * 4, 256);
 }
 
+
+// Pooled K then pooled V (and, for the compressed global branch, pooled Q and
+// the pooled output) at the start of the workspace.
+vdsa_status check_pooled_call(const vdsa_problem* prob, const int32_t* pool_hw, View& vq, View& vk, View& vv,
+                              View& vo, float* lse, void* workspace, size_t workspace_bytes, size_t need) {
+  vdsa_status s;
+  if ((s = check_pool(prob, pool_hw)) != VDSA_OK) return s;
+  if ((s = check_view(prob, vq, false)) != VDSA_OK) return s;
+  if ((s = check_view(prob, vk, false)) != VDSA_OK) return s;
+  if ((s = check_view(prob, vv, false)) != VDSA_OK) return s;
+  if ((s = check_view(prob, vo, true)) != VDSA_OK) return s;
+  uintptr_t l0, l1;
+  if ((s = check_lse(prob, lse, l0, l1)) != VDSA_OK) return s;
+  if (!workspace) return fail(VDSA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (workspace_bytes < need) return fail(VDSA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  if ((uintptr_t)workspace % 16 != 0) return fail(VDSA_ERR_ALIGN, "workspace is not 16-byte aligned");
+  const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + need;
+  for (const View* in : {&vq, &vk, &vv})
+    if (overlaps(vo.lo, vo.hi, in->lo, in->hi)) return fail(VDSA_ERR_ALIAS, "o overlaps %s", in->name);
+  for (const View* in : {&vq, &vk, &vv, &vo})
+    if (overlaps(w0, w1, in->lo, in->hi)) return fail(VDSA_ERR_ALIAS, "workspace overlaps %s", in->name);
+  if (lse) {
+    for (const View* in : {&vq, &vk, &vv, &vo})
+      if (overlaps(l0, l1, in->lo, in->hi)) return fail(VDSA_ERR_ALIAS, "lse overlaps %s", in->name);
+    if (overlaps(l0, l1, w0, w1)) return fail(VDSA_ERR_ALIAS, "lse overlaps workspace");
+  }
+  return VDSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -677,6 +706,123 @@ vdsa_status dual_branch_merge_lse(const vdsa_problem* prob, const void* o_local,
   mp.n_tokens = N;
   hipError_t e = vdsa::launch_merge(mp, prob->dtype == VDSA_BF16, (hipStream_t)stream);
   if (e != hipSuccess) return fail(VDSA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+vdsa_status hier_pooled_attn_workspace_size(const vdsa_problem* prob, const int32_t pool_hw[2], size_t* bytes) {
+  vdsa_status s;
+  if ((s = check_problem(prob)) != VDSA_OK) return s;
+  if ((s = check_pool(prob, pool_hw)) != VDSA_OK) return s;
+  if (!bytes) return fail(VDSA_ERR_NULL, "bytes is NULL");
+  *bytes = 2 * pooled_bytes(prob, pool_hw);
+  return ok();
+}
+
+vdsa_status hier_pooled_attn_fwd(const vdsa_problem* prob, const vdsa_sta_cfg* cfg, const int32_t pool_hw[2],
+                                 const void* q, const vdsa_strides* q_strides, const void* k,
+                                 const vdsa_strides* k_strides, const void* v, const vdsa_strides* v_strides,
+                                 void* o, const vdsa_strides* o_strides, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  vdsa_status s;
+  if ((s = check_problem(prob)) != VDSA_OK) return s;
+  if ((s = check_sta_cfg(cfg)) != VDSA_OK) return s;
+  const int64_t N = n_tokens(prob);
+  View vq{"q", q, q_strides, N}, vk{"k", k, k_strides, N}, vv{"v", v, v_strides, N}, vo{"o", o, o_strides, N};
+  if ((s = check_pool(prob, pool_hw)) != VDSA_OK) return s;
+  const size_t half = pooled_bytes(prob, pool_hw);
+  if ((s = check_pooled_call(prob, pool_hw, vq, vk, vv, vo, lse, workspace, workspace_bytes, 2 * half)) != VDSA_OK)
+    return s;
+  const int64_t M = pooled_tokens(prob, pool_hw);
+  void* kp = workspace;
+  void* vp = (char*)workspace + half;
+  vdsa_strides ps{(int64_t)prob->heads * M * prob->head_dim, M * prob->head_dim, prob->head_dim};
+  const hipStream_t st = (hipStream_t)stream;
+  hipError_t e = vdsa::launch_avgpool(pool_params(prob, pool_hw, k, k_strides, kp, &ps), prob->dtype == VDSA_BF16, st);
+  if (e == hipSuccess)
+    e = vdsa::launch_avgpool(pool_params(prob, pool_hw, v, v_strides, vp, &ps), prob->dtype == VDSA_BF16, st);
+  if (e != hipSuccess) return fail(VDSA_ERR_HIP, "pooling launch failed: %s", hipGetErrorString(e));
+
+  vdsa::BoxAttnParams bp{};
+  View vkp{"k_pooled", kp, &ps, M}, vvp{"v_pooled", vp, &ps, M};
+  set_qkvo(bp, vq, vkp, vvp, vo);
+  bp.lse = lse;
+  bp.batch = prob->batch;
+  bp.heads = prob->heads;
+  bp.qT = prob->grid_t; bp.qH = prob->grid_h; bp.qW = prob->grid_w;
+  bp.bT = cfg->tile[0]; bp.bH = cfg->tile[1]; bp.bW = cfg->tile[2];
+  bp.sT = cfg->shift[0]; bp.sH = cfg->shift[1]; bp.sW = cfg->shift[2];
+  bp.nT = tiles_along(bp.qT, bp.bT, bp.sT);
+  bp.nH = tiles_along(bp.qH, bp.bH, bp.sH);
+  bp.nW = tiles_along(bp.qW, bp.bW, bp.sW);
+  bp.rT = (cfg->window[0] - 1) / 2; bp.rH = (cfg->window[1] - 1) / 2; bp.rW = (cfg->window[2] - 1) / 2;
+  bp.kT = prob->grid_t;
+  bp.kH = (prob->grid_h + pool_hw[0] - 1) / pool_hw[0];
+  bp.kW = (prob->grid_w + pool_hw[1] - 1) / pool_hw[1];
+  bp.kpT = 1; bp.kpH = pool_hw[0]; bp.kpW = pool_hw[1];
+  bp.dense_keys = 0;
+  return launch_attn(prob, bp, st);
+}
+
+vdsa_status compressed_global_attn_workspace_size(const vdsa_problem* prob, const int32_t pool_hw[2],
+                                                  size_t* bytes) {
+  vdsa_status s;
+  if ((s = check_problem(prob)) != VDSA_OK) return s;
+  if ((s = check_pool(prob, pool_hw)) != VDSA_OK) return s;
+  if (!bytes) return fail(VDSA_ERR_NULL, "bytes is NULL");
+  *bytes = 4 * pooled_bytes(prob, pool_hw);
+  return ok();
+}
+
+vdsa_status compressed_global_attn_fwd(const vdsa_problem* prob, const int32_t pool_hw[2], const void* q,
+                                       const vdsa_strides* q_strides, const void* k, const vdsa_strides* k_strides,
+                                       const void* v, const vdsa_strides* v_strides, void* o,
+                                       const vdsa_strides* o_strides, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  vdsa_status s;
+  if ((s = check_problem(prob)) != VDSA_OK) return s;
+  const int64_t N = n_tokens(prob);
+  View vq{"q", q, q_strides, N}, vk{"k", k, k_strides, N}, vv{"v", v, v_strides, N}, vo{"o", o, o_strides, N};
+  if ((s = check_pool(prob, pool_hw)) != VDSA_OK) return s;
+  const size_t part = pooled_bytes(prob, pool_hw);
+  if ((s = check_pooled_call(prob, pool_hw, vq, vk, vv, vo, nullptr, workspace, workspace_bytes, 4 * part)) !=
+      VDSA_OK)
+    return s;
+  const int64_t M = pooled_tokens(prob, pool_hw);
+  const int Hp = (prob->grid_h + pool_hw[0] - 1) / pool_hw[0], Wp = (prob->grid_w + pool_hw[1] - 1) / pool_hw[1];
+  void* qp = workspace;
+  void* kp = (char*)workspace + part;
+  void* vp = (char*)workspace + 2 * part;
+  void* op = (char*)workspace + 3 * part;
+  vdsa_strides ps{(int64_t)prob->heads * M * prob->head_dim, M * prob->head_dim, prob->head_dim};
+  const hipStream_t st = (hipStream_t)stream;
+  const int bf16 = prob->dtype == VDSA_BF16;
+  hipError_t e = vdsa::launch_avgpool(pool_params(prob, pool_hw, q, q_strides, qp, &ps), bf16, st);
+  if (e == hipSuccess) e = vdsa::launch_avgpool(pool_params(prob, pool_hw, k, k_strides, kp, &ps), bf16, st);
+  if (e == hipSuccess) e = vdsa::launch_avgpool(pool_params(prob, pool_hw, v, v_strides, vp, &ps), bf16, st);
+  if (e != hipSuccess) return fail(VDSA_ERR_HIP, "pooling launch failed: %s", hipGetErrorString(e));
+
+  // full attention among the pooled tokens: one query tile over the pooled grid
+  vdsa::BoxAttnParams bp{};
+  View vqp{"q_pooled", qp, &ps, M}, vkp{"k_pooled", kp, &ps, M}, vvp{"v_pooled", vp, &ps, M},
+      vop{"o_pooled", op, &ps, M};
+  set_qkvo(bp, vqp, vkp, vvp, vop);
+  bp.batch = prob->batch;
+  bp.heads = prob->heads;
+  bp.qT = prob->grid_t; bp.qH = Hp; bp.qW = Wp;
+  bp.bT = bp.qT; bp.bH = bp.qH; bp.bW = bp.qW;
+  bp.nT = bp.nH = bp.nW = 1;
+  bp.kT = prob->grid_t; bp.kH = Hp; bp.kW = Wp;
+  bp.dense_keys = 1;
+  if ((s = launch_attn(prob, bp, st)) != VDSA_OK) return s;
+
+  vdsa::UpsampleParams up{};
+  up.xp = op;
+  up.out = o;
+  up.o_sb = o_strides->b; up.o_sh = o_strides->h; up.o_sn = o_strides->n;
+  up.batch = prob->batch; up.heads = prob->heads; up.head_dim = prob->head_dim;
+  up.T = prob->grid_t; up.H = prob->grid_h; up.W = prob->grid_w; up.Hp = Hp; up.Wp = Wp;
+  e = vdsa::launch_upsample(up, bf16, st);
+  if (e != hipSuccess) return fail(VDSA_ERR_HIP, "upsampling launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -32,23 +32,10 @@ __global__ __launch_bounds__(NTHREADS) void box_attn_f32_kernel(const BoxAttnPar
   const int bh = rest / ntiles;
   const int h = bh % p.heads;
   const int b = bh / p.heads;
-  const int aw = tile % p.nW, ah = (tile / p.nW) % p.nH, at = tile / (p.nW * p.nH);
-
-  int qt0 = max(0, at * p.bT - p.sT), qet = min(p.qT, (at + 1) * p.bT - p.sT) - qt0;
-  int qh0 = max(0, ah * p.bH - p.sH), qeh = min(p.qH, (ah + 1) * p.bH - p.sH) - qh0;
-  int qw0 = max(0, aw * p.bW - p.sW), qew = min(p.qW, (aw + 1) * p.bW - p.sW) - qw0;
-  int kt0, ket, kh0, keh, kw0, kew;
-  if (p.dense_keys) {
-    kt0 = kh0 = kw0 = 0;
-    ket = p.kT; keh = p.kH; kew = p.kW;
-  } else {
-    int c0 = max(0, at - p.rT), c1 = min(p.nT - 1, at + p.rT);
-    kt0 = max(0, c0 * p.bT - p.sT); ket = min(p.qT, (c1 + 1) * p.bT - p.sT) - kt0;
-    c0 = max(0, ah - p.rH); c1 = min(p.nH - 1, ah + p.rH);
-    kh0 = max(0, c0 * p.bH - p.sH); keh = min(p.qH, (c1 + 1) * p.bH - p.sH) - kh0;
-    c0 = max(0, aw - p.rW); c1 = min(p.nW - 1, aw + p.rW);
-    kw0 = max(0, c0 * p.bW - p.sW); kew = min(p.qW, (c1 + 1) * p.bW - p.sW) - kw0;
-  }
+  Box qbx, kbx;
+  tile_boxes(p, tile, qbx, kbx);
+  const int qt0 = qbx.t0, qet = qbx.et, qh0 = qbx.h0, qeh = qbx.eh, qw0 = qbx.w0, qew = qbx.ew;
+  const int kt0 = kbx.t0, ket = kbx.et, kh0 = kbx.h0, keh = kbx.eh, kw0 = kbx.w0, kew = kbx.ew;
   const int qvol = qet * qeh * qew;
   const int q0 = qblk * QPB;
   if (q0 >= qvol) return;

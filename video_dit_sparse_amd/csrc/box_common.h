@@ -105,6 +105,18 @@ __device__ __forceinline__ void tile_boxes(const BoxAttnParams& p, int tile, Box
     wspan(at, p.rT, p.nT, p.bT, p.sT, p.qT, kb.t0, kb.et);
     wspan(ah, p.rH, p.nH, p.bH, p.sH, p.qH, kb.h0, kb.eh);
     wspan(aw, p.rW, p.nW, p.bW, p.sW, p.qW, kb.w0, kb.ew);
+    if (p.kpT > 1 || p.kpH > 1 || p.kpW > 1) {
+      // keys pooled k x k: the cells holding a token of the window box
+      auto cells = [](int k, int& lo, int& ext) {
+        if (k <= 1) return;
+        const int hi = lo + ext;
+        lo /= k;
+        ext = (hi + k - 1) / k - lo;
+      };
+      cells(p.kpT, kb.t0, kb.et);
+      cells(p.kpH, kb.h0, kb.eh);
+      cells(p.kpW, kb.w0, kb.ew);
+    }
   }
 }
 

@@ -47,6 +47,8 @@ struct BoxAttnParams {
   int32_t rT, rH, rW;
   int32_t kT, kH, kW;
   int32_t dense_keys;
+  int32_t kpT, kpH, kpW;      // pooled keys (> 1): the key box is every k-grid cell holding
+                              // a token of the window box; the k grid is the pooled grid
   int32_t qblocks;            // query blocks per tile
   int32_t variant;            // which kernel shape the launcher runs (set by the host)
   int32_t total_wg;           // batch * heads * tiles * qblocks
@@ -150,6 +152,16 @@ struct UnpoolParams {
   int32_t Hp, Wp;
 };
 
+// Frame-wise bilinear upsampling of a pooled tensor back to the grid
+// (half-pixel sample positions, edge rows / columns repeated).
+struct UpsampleParams {
+  const void* xp;    // [batch, heads, T*Hp*Wp, head_dim] contiguous, I/O dtype
+  void* out;         // [batch, heads, T*H*W, head_dim], strided
+  int64_t o_sb, o_sh, o_sn;
+  int32_t batch, heads, head_dim;
+  int32_t T, H, W, Hp, Wp;
+};
+
 // Launchers: return hipSuccess or the launch error.  They assume the
 // parameters were validated.
 hipError_t launch_box_attn_bf16(const BoxAttnParams& p, int head_dim, hipStream_t stream);
@@ -161,6 +173,7 @@ hipError_t launch_box_attn_bf16_pp(const BoxAttnParams& p, hipStream_t stream);
 hipError_t launch_box_attn_f32(const BoxAttnParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_avgpool(const PoolParams& p, int bf16, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int bf16, hipStream_t stream);
+hipError_t launch_upsample(const UpsampleParams& p, int bf16, hipStream_t stream);
 // backward: bf16 head_dim 128 on the matrix cores, fp32 (head_dim 64, 128)
 // on the vector ALU; grad_f32 applies to the fp32 kernel trivially
 hipError_t launch_attn_bwd_dq(const BoxBwdParams& p, int bf16, hipStream_t stream);

@@ -131,6 +131,47 @@ __global__ __launch_bounds__(NTHREADS) void merge_kernel(const MergeParams p) {
   }
 }
 
+// One thread per 16-byte chunk of an output row: the four pooled taps of the
+// row's position, fp32 weights.
+template <bool BF16>
+__global__ __launch_bounds__(NTHREADS) void upsample_kernel(const UpsampleParams p) {
+  using C = Chunk<BF16>;
+  const int cpr = p.head_dim / C::E;
+  const int64_t N = (int64_t)p.T * p.H * p.W;
+  const int64_t M = (int64_t)p.T * p.Hp * p.Wp;
+  const int64_t total = (int64_t)p.batch * p.heads * N * cpr;
+  const size_t esz = BF16 ? 2 : 4;
+  const float sy = (float)p.Hp / (float)p.H, sx = (float)p.Wp / (float)p.W;
+  for (int64_t idx = (int64_t)blockIdx.x * NTHREADS + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * NTHREADS) {
+    const int ch = (int)(idx % cpr);
+    const int64_t row = idx / cpr;
+    const int64_t n = row % N;
+    const int bh = (int)(row / N);
+    const int h = bh % p.heads, b = bh / p.heads;
+    const int t = (int)(n / ((int64_t)p.H * p.W)), rem = (int)(n % ((int64_t)p.H * p.W));
+    const int y = rem / p.W, x = rem % p.W;
+    const float fy = fmaxf(((float)y + 0.5f) * sy - 0.5f, 0.f), fx = fmaxf(((float)x + 0.5f) * sx - 0.5f, 0.f);
+    const int y0 = min((int)fy, p.Hp - 1), x0 = min((int)fx, p.Wp - 1);
+    const int y1 = min(y0 + 1, p.Hp - 1), x1 = min(x0 + 1, p.Wp - 1);
+    const float ly = fy - (float)y0, lx = fx - (float)x0;
+    const char* base = (const char*)p.xp + ((int64_t)bh * M + (int64_t)t * p.Hp * p.Wp) * p.head_dim * esz + ch * 16;
+    auto tap = [&](int yy, int xx, float (&f)[C::E]) {
+      C::unpack(*(const u32x4*)(base + ((int64_t)yy * p.Wp + xx) * p.head_dim * esz), f);
+    };
+    float a[C::E], c[C::E], acc[C::E];
+    tap(y0, x0, a);
+    tap(y0, x1, c);
+#pragma unroll
+    for (int e = 0; e < C::E; ++e) acc[e] = (1.f - ly) * ((1.f - lx) * a[e] + lx * c[e]);
+    tap(y1, x0, a);
+    tap(y1, x1, c);
+#pragma unroll
+    for (int e = 0; e < C::E; ++e) acc[e] += ly * ((1.f - lx) * a[e] + lx * c[e]);
+    *(u32x4*)((char*)p.out + (b * p.o_sb + h * p.o_sh + n * p.o_sn) * esz + ch * 16) = C::pack(acc);
+  }
+}
+
 int grid_for(int64_t work) {
   int64_t blocks = (work + NTHREADS - 1) / NTHREADS;
   const int64_t cap = 256 * 8 * 16;  // enough waves to saturate HBM; the loop strides the rest
@@ -156,6 +197,16 @@ hipError_t launch_merge(const MergeParams& p, int bf16, hipStream_t stream) {
     hipLaunchKernelGGL(merge_kernel<true>, dim3(grid_for(work)), dim3(NTHREADS), 0, stream, p);
   else
     hipLaunchKernelGGL(merge_kernel<false>, dim3(grid_for(work)), dim3(NTHREADS), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_upsample(const UpsampleParams& p, int bf16, hipStream_t stream) {
+  const int cpr = p.head_dim / (bf16 ? 8 : 4);
+  const int64_t work = (int64_t)p.batch * p.heads * p.T * p.H * p.W * cpr;
+  if (bf16)
+    hipLaunchKernelGGL(upsample_kernel<true>, dim3(grid_for(work)), dim3(NTHREADS), 0, stream, p);
+  else
+    hipLaunchKernelGGL(upsample_kernel<false>, dim3(grid_for(work)), dim3(NTHREADS), 0, stream, p);
   return hipGetLastError();
 }
 
