@@ -115,6 +115,7 @@ def main():
 
     import torch
     import video_dit_sparse_amd as V
+    from video_dit_sparse_amd import _lib as L
     from video_dit_sparse_amd import pipeline as P
     from video_dit_sparse_amd import workloads as WL
 
@@ -211,6 +212,27 @@ def main():
             "merge_lse_hbm_frac": round(merge_lse_bytes / (merge_lse_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         log(f"[bench] global branch: fused {fused_ms:.3f} ms, global then merge {unfused_ms:.3f} ms; "
             f"LSE merge {merge_lse_ms:.3f} ms ({merge_lse_bytes / (merge_lse_ms * 1e-3) / 1e9:.0f} GB/s)")
+        # UltraGen's variants on the same inputs: hierarchical windows over
+        # 2x2-pooled keys (the local tiling), compressed global attention
+        # (Q pooled too, bilinear upsampling; the workload's pooling)
+        sh0 = w.shifts[0]
+        ws_h = torch.empty(L.global_pooled_attn_workspace_size(w.batch, w.heads, w.head_dim, w.grid, (2, 2),
+                                                               1 if w.dtype == "bf16" else 0),
+                           dtype=torch.uint8, device=dev)
+        ws_c = torch.empty(2 * buf.workspace.numel(), dtype=torch.uint8, device=dev)
+        hier_ms = timed(lambda: V.hier_pooled_attn_fwd(q, k, v, w.grid, w.tile, w.window, (2, 2), sh0,
+                                                       scale=w.softmax_scale, out=buf.glob, workspace=ws_h), n)
+        comp_ms = timed(lambda: V.compressed_global_attn_fwd(q, k, v, w.grid, w.pool_hw, scale=w.softmax_scale,
+                                                             out=buf.glob, workspace=ws_c), n)
+        hier_fl = V.hier_flops(w.batch, w.heads, w.head_dim, w.grid, w.tile, w.window, (2, 2), sh0)
+        comp_fl = V.compressed_global_flops(w.batch, w.heads, w.head_dim, w.grid, w.pool_hw)
+        extra["ultragen_variants"] = {
+            "hier_pool2x2_ms": round(hier_ms, 3), "hier_effective_flop": hier_fl,
+            "hier_tflops": round(hier_fl / (hier_ms * 1e-3) / 1e12, 1),
+            "compressed_global_ms": round(comp_ms, 3), "compressed_global_effective_flop": comp_fl,
+            "compressed_global_tflops": round(comp_fl / (comp_ms * 1e-3) / 1e12, 1)}
+        log(f"[bench] hierarchical (2x2-pooled keys): {hier_ms:.3f} ms ({hier_fl / (hier_ms * 1e-3) / 1e12:.0f} TFLOP/s); "
+            f"compressed global: {comp_ms:.3f} ms ({comp_fl / (comp_ms * 1e-3) / 1e12:.0f} TFLOP/s)")
     if args.bwd_steps > 0:
         # backward of the local branch (first lattice shift): dQ, dK, dV from
         # the forward's output and LSE; effective work 10 * head_dim FLOP per

@@ -347,6 +347,11 @@ vdsa_status kv_avgpool_fwd(const vdsa_problem* prob, const int32_t pool_hw[2],
  * partial tiles count their real tokens only.  Host only. */
 vdsa_status vdsa_sta_flops(const vdsa_problem* prob, const vdsa_sta_cfg* cfg, double* flops);
 vdsa_status vdsa_global_flops(const vdsa_problem* prob, const int32_t pool_hw[2], double* flops);
+/* hier_pooled_attn_fwd: 4 * head_dim per (query, pooled cell of its window);
+ * compressed_global_attn_fwd: 4 * head_dim per (pooled query, pooled key). */
+vdsa_status vdsa_hier_flops(const vdsa_problem* prob, const vdsa_sta_cfg* cfg, const int32_t pool_hw[2],
+                            double* flops);
+vdsa_status vdsa_compressed_global_flops(const vdsa_problem* prob, const int32_t pool_hw[2], double* flops);
 
 const char* vdsa_status_string(vdsa_status s);
 const char* vdsa_last_error(void);   /* thread-local detail of the last failed call */

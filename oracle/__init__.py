@@ -32,5 +32,6 @@ from .ref import (  # noqa: F401
     sta_flops_ref,
     global_flops_ref,
     dense_flops_ref,
+    hier_pair_count_ref,
     to_f64,
 )

@@ -50,7 +50,7 @@ __all__ = [
     "merge_ref", "merge_lse_ref", "union_attention_ref", "upsample_bilinear_ref",
     "compressed_global_ref", "hier_pooled_ref", "attention_bwd_ref", "sta_bwd_ref",
     "global_bwd_ref", "sta_pair_count_ref",
-    "sta_flops_ref", "global_flops_ref", "dense_flops_ref",
+    "sta_flops_ref", "global_flops_ref", "dense_flops_ref", "hier_pair_count_ref",
 ]
 
 
@@ -488,3 +488,21 @@ def global_flops_ref(grid, pool_hw, head_dim=128, heads=1, batch=1) -> float:
 def dense_flops_ref(grid, head_dim=128, heads=1, batch=1) -> float:
     N = int(np.prod(grid))
     return 4.0 * head_dim * heads * batch * N * N
+
+
+def hier_pair_count_ref(grid, tile, window, shift, pool_hw) -> int:
+    """(query, pooled cell) pairs of ``hier_pooled_ref`` for one head, counted
+    query by query through the explicit token -> cell map."""
+    T, H, W = grid
+    kh, kw = pool_hw
+    _, Hp, Wp = pooled_grid(grid, pool_hw)
+    coords = token_coords(grid)
+    cell = (coords[:, 0] * Hp + coords[:, 1] // kh) * Wp + coords[:, 2] // kw
+    ti = tile_index(coords, tile, shift)
+    radius = window_radius(window)
+    uniq, inv, cnt = np.unique(ti, axis=0, return_inverse=True, return_counts=True)
+    total = 0
+    for g in range(len(uniq)):
+        total += int(cnt[g]) * len(np.unique(cell[sta_mask_row(ti, uniq[g], radius)]))
+    return total
+

@@ -279,3 +279,21 @@ def test_flop_counter_matches_oracle(grid, tile, window, shift):
 def test_global_flop_counter_matches_oracle():
     for grid, pool in [((21, 68, 120), (4, 4)), ((21, 136, 240), (8, 8)), ((3, 9, 10), (4, 3))]:
         assert L.global_flops(1, 24, 128, grid, pool) == R.global_flops_ref(grid, pool, head_dim=128, heads=24)
+
+
+@pytest.mark.parametrize("grid,tile,window,shift,pool", [
+    ((3, 8, 16), (1, 4, 4), (1, 3, 3), (0, 0, 0), (2, 2)),
+    ((2, 9, 11), (1, 3, 4), (1, 3, 3), (0, 1, 1), (2, 2)),
+    ((21, 68, 120), (21, 17, 30), (1, 1, 1), (0, 0, 0), (2, 2)),
+    ((4, 10, 14), (2, 4, 6), (3, 1, 3), (1, 2, 3), (4, 3)),
+])
+def test_hier_flop_counter_matches_oracle(grid, tile, window, shift, pool):
+    got = L.hier_flops(1, 2, 128, grid, tile, window, pool, shift)
+    assert got == 4.0 * 128 * 2 * R.hier_pair_count_ref(grid, tile, window, shift, pool)
+
+
+def test_compressed_global_flop_counter():
+    T, H, W = 21, 68, 120
+    M = T * 17 * 30
+    assert L.compressed_global_flops(1, 24, 128, (T, H, W), (4, 4)) == 4.0 * 128 * 24 * M * M
+

@@ -15,7 +15,9 @@ from ._lib import (  # noqa: F401
     compressed_global_attn_fwd,
     dual_branch_merge,
     dual_branch_merge_lse,
+    compressed_global_flops,
     global_flops,
+    hier_flops,
     global_pooled_attn_fwd,
     global_pooled_attn_merge_fwd,
     global_pooled_attn_bwd,

@@ -32,7 +32,7 @@ EXPORTED = [
     "compressed_global_attn_fwd",
     "sta_attn_bwd_workspace_size", "sta_attn_bwd", "global_pooled_attn_bwd_workspace_size",
     "global_pooled_attn_bwd",
-    "kv_avgpool_fwd", "vdsa_sta_flops", "vdsa_global_flops",
+    "kv_avgpool_fwd", "vdsa_sta_flops", "vdsa_global_flops", "vdsa_hier_flops", "vdsa_compressed_global_flops",
     "vdsa_status_string", "vdsa_last_error", "vdsa_abi_version",
 ]
 VDSA_MERGE_GATED, VDSA_MERGE_LSE = 0, 1
@@ -94,6 +94,8 @@ def lib() -> ctypes.CDLL:
                                          vp, ctypes.c_size_t, vp]
     L.vdsa_sta_flops.argtypes = [P, C, ctypes.POINTER(ctypes.c_double)]
     L.vdsa_global_flops.argtypes = [P, i32p, ctypes.POINTER(ctypes.c_double)]
+    L.vdsa_hier_flops.argtypes = [P, C, i32p, ctypes.POINTER(ctypes.c_double)]
+    L.vdsa_compressed_global_flops.argtypes = [P, i32p, ctypes.POINTER(ctypes.c_double)]
     L.vdsa_status_string.argtypes = [ctypes.c_int]
     L.vdsa_status_string.restype = ctypes.c_char_p
     L.vdsa_last_error.argtypes = []
@@ -432,6 +434,21 @@ def global_flops(batch, heads, head_dim, grid, pool_hw) -> float:
     prob = make_problem(batch, heads, head_dim, grid, VDSA_BF16, 1.0)
     f = ctypes.c_double()
     check(lib().vdsa_global_flops(ctypes.byref(prob), _pool(pool_hw), ctypes.byref(f)))
+    return f.value
+
+
+def hier_flops(batch, heads, head_dim, grid, tile, window, pool_hw, shift=(0, 0, 0)) -> float:
+    prob = make_problem(batch, heads, head_dim, grid, VDSA_BF16, 1.0)
+    cfg = make_cfg(tile, window, shift)
+    f = ctypes.c_double()
+    check(lib().vdsa_hier_flops(ctypes.byref(prob), ctypes.byref(cfg), _pool(pool_hw), ctypes.byref(f)))
+    return f.value
+
+
+def compressed_global_flops(batch, heads, head_dim, grid, pool_hw) -> float:
+    prob = make_problem(batch, heads, head_dim, grid, VDSA_BF16, 1.0)
+    f = ctypes.c_double()
+    check(lib().vdsa_compressed_global_flops(ctypes.byref(prob), _pool(pool_hw), ctypes.byref(f)))
     return f.value
 
 

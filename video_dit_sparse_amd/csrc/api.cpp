@@ -989,6 +989,45 @@ vdsa_status vdsa_sta_flops(const vdsa_problem* prob, const vdsa_sta_cfg* cfg, do
   return ok();
 }
 
+vdsa_status vdsa_hier_flops(const vdsa_problem* prob, const vdsa_sta_cfg* cfg, const int32_t pool_hw[2],
+                            double* flops) {
+  vdsa_status s;
+  if ((s = check_problem(prob)) != VDSA_OK) return s;
+  if ((s = check_sta_cfg(cfg)) != VDSA_OK) return s;
+  if ((s = check_pool(prob, pool_hw)) != VDSA_OK) return s;
+  if (!flops) return fail(VDSA_ERR_NULL, "flops is NULL");
+  // per dim: sum over query tiles of size(a) * cells intersecting the window
+  // box of a (the key set is a product of per-dim intervals)
+  const int L[3] = {prob->grid_t, prob->grid_h, prob->grid_w};
+  const int pk[3] = {1, pool_hw[0], pool_hw[1]};
+  double pairs = 1.0;
+  for (int d = 0; d < 3; ++d) {
+    const int b = cfg->tile[d], sh = cfg->shift[d], r = (cfg->window[d] - 1) / 2;
+    const int n = tiles_along(L[d], b, sh);
+    double acc = 0.0;
+    for (int a = 0; a < n; ++a) {
+      const int size = std::min(L[d], (a + 1) * b - sh) - std::max(0, a * b - sh);
+      const int c0 = std::max(0, a - r), c1 = std::min(n - 1, a + r);
+      const int lo = std::max(0, c0 * b - sh), hi = std::min(L[d], (c1 + 1) * b - sh);
+      const int cells = (hi + pk[d] - 1) / pk[d] - lo / pk[d];
+      acc += (double)size * cells;
+    }
+    pairs *= acc;
+  }
+  *flops = 4.0 * prob->head_dim * prob->batch * prob->heads * pairs;
+  return ok();
+}
+
+vdsa_status vdsa_compressed_global_flops(const vdsa_problem* prob, const int32_t pool_hw[2], double* flops) {
+  vdsa_status s;
+  if ((s = check_problem(prob)) != VDSA_OK) return s;
+  if ((s = check_pool(prob, pool_hw)) != VDSA_OK) return s;
+  if (!flops) return fail(VDSA_ERR_NULL, "flops is NULL");
+  const double M = (double)pooled_tokens(prob, pool_hw);
+  *flops = 4.0 * prob->head_dim * prob->batch * prob->heads * M * M;
+  return ok();
+}
+
 vdsa_status vdsa_global_flops(const vdsa_problem* prob, const int32_t pool_hw[2], double* flops) {
   vdsa_status s;
   if ((s = check_problem(prob)) != VDSA_OK) return s;
