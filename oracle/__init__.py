@@ -13,6 +13,11 @@ from .ref import (  # noqa: F401
     tile_extent,
     window_radius,
     sta_mask_row,
+    WINDOW_MODES,
+    mode_tile_index,
+    mode_tile_counts,
+    window_tiles,
+    mode_mask_row,
     sta_ref,
     dense_ref,
     attention_weights_ref,

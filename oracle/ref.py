@@ -45,7 +45,8 @@ import numpy as np
 
 __all__ = [
     "to_f64", "token_coords", "tile_index", "tile_counts", "tile_extent",
-    "window_radius", "sta_mask_row", "sta_ref", "dense_ref",
+    "window_radius", "sta_mask_row", "WINDOW_MODES", "mode_tile_index", "mode_tile_counts",
+    "window_tiles", "mode_mask_row", "sta_ref", "dense_ref",
     "attention_weights_ref", "pooled_grid", "pool_ref", "global_ref",
     "merge_ref", "merge_lse_ref", "union_attention_ref", "upsample_bilinear_ref",
     "compressed_global_ref", "hier_pooled_ref", "attention_bwd_ref", "sta_bwd_ref",
@@ -117,6 +118,52 @@ def window_radius(window) -> tuple:
     return tuple((int(w) - 1) // 2 for w in window)
 
 
+WINDOW_MODES = ("clip", "inward", "cyclic")
+
+
+def mode_tile_index(grid, tile, shift=(0, 0, 0), window_mode="clip") -> np.ndarray:
+    """Tile coordinate of every token under a window mode.
+
+    ``clip`` and ``inward``: the shifted lattice of ``tile_index``.
+    ``cyclic``: the token grid is first rolled by the shift, x' = (x + s) mod L
+    (a Swin-style cyclic shift, here without a seam mask), then tiled from 0:
+    i = x' // b, so the tiles at the seam hold tokens of both grid edges.
+    """
+    coords = token_coords(grid)
+    if window_mode == "cyclic":
+        rolled = (coords + np.asarray(shift, dtype=np.int64)) % np.asarray(grid, dtype=np.int64)
+        return rolled // np.asarray(tile, dtype=np.int64)
+    return tile_index(coords, tile, shift)
+
+
+def mode_tile_counts(grid, tile, shift=(0, 0, 0), window_mode="clip") -> tuple:
+    return tile_counts(grid, tile, (0, 0, 0) if window_mode == "cyclic" else shift)
+
+
+def window_tiles(query_tile, radius, counts, window_mode="clip"):
+    """Per dim, the inclusive range [lo, hi] of key tiles in the window of
+    ``query_tile``.  ``clip`` / ``cyclic``: the tiles within ``radius``,
+    clipped at the lattice edge.  ``inward``: the same number of tiles, 2r+1,
+    moved inward at the edges (all tiles when the lattice has fewer)."""
+    lo, hi = [], []
+    for a, r, n in zip(query_tile, radius, counts):
+        a, r, n = int(a), int(r), int(n)
+        if window_mode == "inward":
+            c0 = max(0, min(a - r, n - (2 * r + 1)))
+            lo.append(c0)
+            hi.append(min(n - 1, c0 + 2 * r))
+        else:
+            lo.append(max(0, a - r))
+            hi.append(min(n - 1, a + r))
+    return np.asarray(lo), np.asarray(hi)
+
+
+def mode_mask_row(tiles_of_keys, query_tile, radius, counts, window_mode="clip") -> np.ndarray:
+    """Boolean mask over all keys for one query under a window mode."""
+    lo, hi = window_tiles(query_tile, radius, counts, window_mode)
+    return np.all((tiles_of_keys >= lo[None, :]) & (tiles_of_keys <= hi[None, :]), axis=1)
+
+
 def sta_mask_row(tiles_of_keys: np.ndarray, query_tile, radius) -> np.ndarray:
     """Boolean mask over all keys for one query: key m is attended iff its
     tile is within ``radius`` tiles of the query's tile in every dim.
@@ -141,7 +188,7 @@ def _softmax_attend(qb, kb, vb, scale):
     return o, mx[:, 0] + np.log(l[:, 0])
 
 
-def sta_ref(q, k, v, grid, tile, window, shift=(0, 0, 0), scale=None, rows=None):
+def sta_ref(q, k, v, grid, tile, window, shift=(0, 0, 0), scale=None, rows=None, window_mode="clip"):
     """Sliding-tile attention for one head.
 
     For query token n: O_n = sum_m softmax_m(scale * q_n . k_m) v_m with m over
@@ -162,7 +209,8 @@ def sta_ref(q, k, v, grid, tile, window, shift=(0, 0, 0), scale=None, rows=None)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     radius = window_radius(window)
-    ti = tile_index(token_coords(grid), tile, shift)
+    ti = mode_tile_index(grid, tile, shift, window_mode)
+    counts = mode_tile_counts(grid, tile, shift, window_mode)
     rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
     o = np.empty((len(rows), v.shape[1]))
     lse = np.empty(len(rows))
@@ -172,7 +220,7 @@ def sta_ref(q, k, v, grid, tile, window, shift=(0, 0, 0), scale=None, rows=None)
         pos = np.nonzero(inv == g)[0]
         block = np.empty((len(pos), N), dtype=bool)
         for j, n in enumerate(rows[pos]):
-            block[j] = sta_mask_row(ti, ti[n], radius)
+            block[j] = mode_mask_row(ti, ti[n], radius, counts, window_mode)
         assert block[0].any(), "a query row with no key"
         assert (block == block[0][None, :]).all(), "rows of one query tile differ"
         keys = np.nonzero(block[0])[0]
@@ -397,7 +445,7 @@ def attention_bwd_ref(q, k, v, do, scale):
     return scale * (ds @ k), scale * (ds.T @ q), dv
 
 
-def sta_bwd_ref(q, k, v, do, grid, tile, window, shift=(0, 0, 0), scale=None):
+def sta_bwd_ref(q, k, v, do, grid, tile, window, shift=(0, 0, 0), scale=None, window_mode="clip"):
     """Gradients of ``sta_ref`` for one head: every query tile's rows
     contribute through its own selected keys (the explicit mask of
     ``sta_mask_row``); key gradients are summed over all query tiles that
@@ -408,13 +456,14 @@ def sta_bwd_ref(q, k, v, do, grid, tile, window, shift=(0, 0, 0), scale=None):
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     radius = window_radius(window)
-    ti = tile_index(token_coords(grid), tile, shift)
+    ti = mode_tile_index(grid, tile, shift, window_mode)
+    counts = mode_tile_counts(grid, tile, shift, window_mode)
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     uniq, inv = np.unique(ti, axis=0, return_inverse=True)
     inv = np.asarray(inv).reshape(-1)
     for g in range(len(uniq)):
         rows = np.nonzero(inv == g)[0]
-        keys = np.nonzero(sta_mask_row(ti, uniq[g], radius))[0]
+        keys = np.nonzero(mode_mask_row(ti, uniq[g], radius, counts, window_mode))[0]
         gq, gk, gv = attention_bwd_ref(q[rows], k[keys], v[keys], do[rows], scale)
         dq[rows] += gq
         dk[keys] += gk
@@ -456,27 +505,28 @@ def global_bwd_ref(q, k, v, do, grid, pool_hw, scale=None):
 # --------------------------------------------------------------------------
 # effective work
 # --------------------------------------------------------------------------
-def sta_pair_count_ref(grid, tile, window, shift=(0, 0, 0)) -> int:
+def sta_pair_count_ref(grid, tile, window, shift=(0, 0, 0), window_mode="clip") -> int:
     """Attended (query, key) token pairs of one head: sum over tile pairs
-    (a, c) inside each other's window of tokens(a) * tokens(c).
+    (a, c) with c in a's window of tokens(a) * tokens(c).
 
     Built from the explicit tile-level mask, so partial tiles count only
     their real tokens.
     """
-    radius = np.asarray(window_radius(window), dtype=np.int64)
-    counts = tile_counts(grid, tile, shift)
+    radius = window_radius(window)
+    sh = (0, 0, 0) if window_mode == "cyclic" else shift
+    counts = tile_counts(grid, tile, sh)
     sizes = [np.array([tile_extent(i, int(L), int(b), int(s))[1] - tile_extent(i, int(L), int(b), int(s))[0]
                        for i in range(n)], dtype=np.int64)
-             for L, b, s, n in zip(grid, tile, shift, counts)]
+             for L, b, s, n in zip(grid, tile, sh, counts)]
     idx = np.stack(np.meshgrid(*[np.arange(n) for n in counts], indexing="ij"), axis=-1).reshape(-1, 3)
     tok = sizes[0][idx[:, 0]] * sizes[1][idx[:, 1]] * sizes[2][idx[:, 2]]
-    A = np.all(np.abs(idx[:, None, :] - idx[None, :, :]) <= radius[None, None, :], axis=2)
+    A = np.stack([mode_mask_row(idx, a, radius, counts, window_mode) for a in idx])
     return int(tok @ A.astype(np.int64) @ tok)
 
 
-def sta_flops_ref(grid, tile, window, shift=(0, 0, 0), head_dim=128, heads=1, batch=1) -> float:
+def sta_flops_ref(grid, tile, window, shift=(0, 0, 0), head_dim=128, heads=1, batch=1, window_mode="clip") -> float:
     """4 * D FLOP per attended pair (2D for q.k, 2D for the p*v update)."""
-    return 4.0 * head_dim * heads * batch * sta_pair_count_ref(grid, tile, window, shift)
+    return 4.0 * head_dim * heads * batch * sta_pair_count_ref(grid, tile, window, shift, window_mode)
 
 
 def global_flops_ref(grid, pool_hw, head_dim=128, heads=1, batch=1) -> float:

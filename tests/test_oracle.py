@@ -590,3 +590,87 @@ def test_hier_pooled_by_explicit_cells(grid, tile, window, shift, pool):
     so, sl = R.sta_ref(q, k, v, grid, tile, window, shift, scale=0.5)
     np.testing.assert_allclose(o1, so, atol=1e-13)
     np.testing.assert_allclose(l1, sl, atol=1e-13)
+
+
+# ---------------------------------------------------------------- window modes
+def _mode_mask_by_coords(grid, tile, window, shift, mode):
+    """Token-level mask of a window mode, built independently of the oracle."""
+    c = coords_lib(grid)
+    L = np.asarray(grid)
+    b = np.asarray(tile)
+    if mode == "cyclic":
+        ti = ((c + np.asarray(shift)) % L) // b
+        n = -(-L // b)
+    else:
+        ti = (c + np.asarray(shift)) // b
+        n = -(-(L + np.asarray(shift)) // b)
+    r = (np.asarray(window) - 1) // 2
+    w = 2 * r + 1
+    if mode == "inward":
+        start = np.empty_like(ti)
+        for d in range(3):
+            for i in range(ti.shape[0]):
+                s0 = ti[i, d] - r[d]
+                if s0 + w[d] > n[d]:
+                    s0 = n[d] - w[d]
+                if s0 < 0:
+                    s0 = 0
+                start[i, d] = s0
+        return np.all((ti[None, :, :] >= start[:, None, :]) & (ti[None, :, :] < start[:, None, :] + w[None, None, :]),
+                      axis=2)
+    return np.all(np.abs(ti[:, None, :] - ti[None, :, :]) <= r[None, None, :], axis=2)
+
+
+def _masked_dense(q, k, v, mask, scale):
+    s = scale * q @ k.T
+    s = np.where(mask, s, -np.inf)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    return (p / p.sum(axis=1, keepdims=True)) @ v
+
+
+def test_cyclic_mode_is_clip_on_rolled_grid():
+    grid, tile, window, shift = (3, 8, 10), (1, 4, 4), (1, 1, 3), (1, 2, 3)
+    T, H, W = grid
+    N = T * H * W
+    q, k, v = randn(400, N, 6), randn(401, N, 6), randn(402, N, 6)
+    o, lse = R.sta_ref(q, k, v, grid, tile, window, shift, scale=0.5, window_mode="cyclic")
+    roll = lambda x, s: np.roll(x.reshape(T, H, W, -1), s, axis=(0, 1, 2)).reshape(N, -1)
+    ro, rl = R.sta_ref(roll(q, shift), roll(k, shift), roll(v, shift), grid, tile, window, (0, 0, 0), scale=0.5)
+    neg = tuple(-s for s in shift)
+    np.testing.assert_allclose(o, roll(ro, neg), atol=1e-13)
+    np.testing.assert_allclose(lse, roll(rl[:, None], neg)[:, 0], atol=1e-13)
+
+
+@pytest.mark.parametrize("grid,tile,window,shift,mode", [
+    ((4, 9, 12), (2, 3, 4), (3, 1, 3), (0, 0, 0), "inward"),
+    ((3, 10, 13), (2, 4, 4), (1, 3, 3), (1, 2, 2), "inward"),
+    ((5, 8, 8), (2, 4, 4), (5, 3, 1), (1, 0, 2), "inward"),   # window wider than the T lattice
+    ((3, 8, 10), (2, 4, 4), (1, 3, 3), (1, 2, 3), "cyclic"),
+])
+def test_window_mode_by_independent_mask(grid, tile, window, shift, mode):
+    N = int(np.prod(grid))
+    q, k, v = randn(410, N, 6), randn(411, N, 6), randn(412, N, 6)
+    mask = _mode_mask_by_coords(grid, tile, window, shift, mode)
+    o, _ = R.sta_ref(q, k, v, grid, tile, window, shift, scale=0.5, window_mode=mode)
+    np.testing.assert_allclose(o, _masked_dense(q, k, v, mask, 0.5), atol=1e-13)
+    assert R.sta_pair_count_ref(grid, tile, window, shift, mode) == int(mask.sum())
+    if mode == "inward":
+        # every window spans min(w, n) tiles per dim
+        ti = R.mode_tile_index(grid, tile, shift, mode)
+        counts = R.mode_tile_counts(grid, tile, shift, mode)
+        r = R.window_radius(window)
+        for a in np.unique(ti, axis=0):
+            lo, hi = R.window_tiles(a, r, counts, mode)
+            np.testing.assert_array_equal(hi - lo + 1, np.minimum(2 * np.asarray(r) + 1, counts))
+
+
+@pytest.mark.parametrize("mode,shift", [("inward", (1, 2, 0)), ("cyclic", (1, 2, 3))])
+def test_window_mode_bwd_matches_autograd(mode, shift):
+    grid, tile, window = (3, 8, 10), (2, 4, 4), (1, 3, 3)
+    N = int(np.prod(grid))
+    q, k, v, do = randn(420, N, 6), randn(421, N, 6), randn(422, N, 6), randn(423, N, 6)
+    mask = _mode_mask_by_coords(grid, tile, window, shift, mode)
+    got = R.sta_bwd_ref(q, k, v, do, grid, tile, window, shift, scale=0.5, window_mode=mode)
+    ref = _autograd_masked_attention(q, k, v, do, mask, 0.5)
+    for g, r in zip(got, ref):
+        np.testing.assert_allclose(g, r, rtol=0, atol=1e-11)
