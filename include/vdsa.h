@@ -44,13 +44,14 @@
 extern "C" {
 #endif
 
-#define VDSA_ABI_VERSION 2
+#define VDSA_ABI_VERSION 3
 
 typedef enum {
   VDSA_OK = 0,
   VDSA_ERR_NULL = 1,        /* a required pointer is NULL */
   VDSA_ERR_SHAPE = 2,       /* a dimension <= 0, or an offset beyond the size limit */
-  VDSA_ERR_WINDOW = 3,      /* tile < 1, window even or < 1, shift outside [0, tile), pool < 1 */
+  VDSA_ERR_WINDOW = 3,      /* tile < 1, window even or < 1, shift outside [0, tile), pool < 1,
+                               unknown window_mode */
   VDSA_ERR_UNSUPPORTED = 4, /* head_dim not in {64, 128}, unknown dtype, non-finite scale */
   VDSA_ERR_ALIGN = 5,       /* pointer or stride breaks the 16-byte rule */
   VDSA_ERR_ALIAS = 6,       /* an output overlaps an input it must not overlap */
@@ -86,11 +87,31 @@ typedef struct {
  *             lattice that makes edge tiles partial (the shifted partition of
  *             UltraGen section 4.3, "Cross-window Hierarchical Local
  *             Attention").  Partial tiles hold only real tokens.
+ *   window_mode (vdsa_window_mode) how windows meet the grid edge; 0 (the
+ *             value of a zero-initialised struct) is VDSA_WINDOW_CLIP.
  */
+typedef enum {
+  /* windows clipped at the lattice edge (the definition above) */
+  VDSA_WINDOW_CLIP = 0,
+  /* every window spans min(window[d], tiles[d]) tiles: a window that would
+   * cross the lattice edge is moved inward, so its first tile along d is
+   * max(0, min(a - r, tiles[d] - window[d])) for query tile a, r =
+   * (window[d]-1)/2 (the other reading of the edge rule, which the Sliding
+   * Tile Attention abstract leaves open) */
+  VDSA_WINDOW_INWARD = 1,
+  /* the token grid is rolled cyclically before tiling: the token at x lands
+   * at (x + shift[d]) mod L_d, the rolled grid is tiled from 0 and windows
+   * are clipped there (the cyclic shift of Swin windows, the local module
+   * UltraGen's ablation swaps in, section 5.3 and appendix F; no seam mask,
+   * so tiles at the seam mix tokens of both grid edges) */
+  VDSA_WINDOW_CYCLIC = 2
+} vdsa_window_mode;
+
 typedef struct {
   int32_t tile[3];
   int32_t window[3];
   int32_t shift[3];
+  int32_t window_mode;
 } vdsa_sta_cfg;
 
 /*
@@ -98,8 +119,10 @@ typedef struct {
  *
  * For every (b, h, query token n):
  *   O[n] = sum_m softmax_m(scale * Q[n].K[m]) V[m]
- * over the keys m whose tile is inside the window of n's tile.  The window
- * map is computed in-kernel; no mask is materialised.
+ * over the keys m whose tile is inside the window of n's tile, under
+ * cfg->window_mode (tiles and windows of the rolled grid for
+ * VDSA_WINDOW_CYCLIC; O and LSE stay in the caller's token order).  The
+ * window map is computed in-kernel; no mask is materialised.
  *
  *   q, k, v : device, [batch, heads, N, head_dim] with the given strides.
  *   o       : device output, same shape; must not overlap q, k, v or lse.
@@ -249,7 +272,8 @@ vdsa_status global_pooled_attn_merge_fwd(const vdsa_problem* prob, const int32_t
  * of its sliding-tile window (cfg as in sta_attn_fwd, on the full grid):
  *   O[n] = sum_c softmax_c(scale * Q[n].Kp[c]) Vp[c],  c over those cells.
  * With tiles and shifts that are multiples of the pooling these are exactly
- * the pooled tokens of the window.
+ * the pooled tokens of the window.  cfg->window_mode must be
+ * VDSA_WINDOW_CLIP (VDSA_ERR_WINDOW otherwise).
  *
  *   workspace : at least hier_pooled_attn_workspace_size() bytes (pooled K
  *               then pooled V, as in global_pooled_attn_fwd).
@@ -344,7 +368,8 @@ vdsa_status kv_avgpool_fwd(const vdsa_problem* prob, const int32_t pool_hw[2],
 
 /* Effective work: 4 * head_dim FLOP per attended (query, key) token pair
  * (2*head_dim for q.k, 2*head_dim for p*v), summed over batch and heads;
- * partial tiles count their real tokens only.  Host only. */
+ * partial tiles count their real tokens only; vdsa_sta_flops follows
+ * cfg->window_mode.  Host only. */
 vdsa_status vdsa_sta_flops(const vdsa_problem* prob, const vdsa_sta_cfg* cfg, double* flops);
 vdsa_status vdsa_global_flops(const vdsa_problem* prob, const int32_t pool_hw[2], double* flops);
 /* hier_pooled_attn_fwd: 4 * head_dim per (query, pooled cell of its window);

@@ -1,5 +1,7 @@
 """Shared helpers of the GPU parity tests: tolerances, comparison and row
 sampling.  Test infrastructure only."""
+import sys
+
 import numpy as np
 
 import oracle as R
@@ -7,6 +9,10 @@ import oracle as R
 # bf16 inputs: max abs error <= 2e-2 and mean abs error <= 2e-3 against the
 # fp64 oracle; fp32 path: max abs error <= 1e-4.
 TOL = {"bf16": (2e-2, 2e-3), "f32": (1e-4, 1e-4)}
+# gradients, relative to the reference gradient's RMS (derivation in the
+# backward parity tests' docstring): (elementwise bound on
+# |err| / (RMS + |ref|), bound on mean |err| / RMS)
+TOL_BWD = {"bf16": (6e-2, 5e-3), "f32": (1e-4, 1e-5)}
 
 
 def compare(got, ref, dtype, what=""):
@@ -54,3 +60,21 @@ def sample_rows(grid, tile, shift, n_random_tiles=6, rows_per_tile=48, seed=0):
 def head_f64(x, b, h):
     """One (batch, head) slice of a [B, heads, N, D] tensor as fp64 NumPy."""
     return R.to_f64(x[b, h])
+
+
+def rel_compare(got, ref, dt, what):
+    """Gradient comparison against the oracle at the TOL_BWD bar; prints the
+    measured errors."""
+    g = R.to_f64(got)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    assert np.isfinite(g).all(), f"{what}: non-finite values"
+    rms = float(np.sqrt(np.mean(r * r)))
+    err = np.abs(g - r)
+    tmax, tmean = TOL_BWD[dt]
+    worst = float((err / (rms + np.abs(r))).max())
+    mean = float(err.mean()) / rms
+    print(f"  {what}: max err {worst:.2e} (rms + |ref|), mean {mean:.2e} rms (rms {rms:.3e})",
+          file=sys.stderr, flush=True)
+    assert worst <= tmax and mean <= tmean, \
+        f"{what}: max err {worst:.3e} x (rms + |ref|) (<= {tmax}), mean {mean:.3e} rms (<= {tmean})"

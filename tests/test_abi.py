@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert L.abi_version() == 2
+    assert L.abi_version() == 3
     for code in L.STATUS_NAMES:
         assert L.lib().vdsa_status_string(code)
 
@@ -66,7 +66,10 @@ GOOD_CFG = dict(tile=(2, 4, 4), window=(3, 3, 3), shift=(0, 0, 0))
 def cfg(**kw):
     d = dict(GOOD_CFG)
     d.update(kw)
-    return L.make_cfg(d["tile"], d["window"], d["shift"])
+    c = L.make_cfg(d["tile"], d["window"], d["shift"])
+    if "window_mode" in d:
+        c.window_mode = d["window_mode"]
+    return c
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -75,6 +78,8 @@ def cfg(**kw):
     (dict(window=(3, 0, 3)), "VDSA_ERR_WINDOW"),
     (dict(shift=(2, 0, 0)), "VDSA_ERR_WINDOW"),
     (dict(shift=(0, -1, 0)), "VDSA_ERR_WINDOW"),
+    (dict(window_mode=3), "VDSA_ERR_WINDOW"),
+    (dict(window_mode=-1), "VDSA_ERR_WINDOW"),
 ])
 def test_bad_window_config(kw, code):
     assert sta(prob(), cfg(**kw)) == L.STATUS[code]
@@ -249,6 +254,12 @@ def test_variant_checks():
     assert h(n.value - 1) == L.STATUS["VDSA_ERR_WORKSPACE"]
     assert h(n.value, (ctypes.c_int32 * 2)(2, 0)) == L.STATUS["VDSA_ERR_WINDOW"]
     assert h(n.value, pool, cfg(window=(2, 3, 3))) == L.STATUS["VDSA_ERR_WINDOW"]
+    # the hierarchical variant is defined for clipped windows only
+    for mode in (1, 2):
+        assert h(n.value, pool, cfg(window_mode=mode)) == L.STATUS["VDSA_ERR_WINDOW"]
+        f = ctypes.c_double()
+        assert L.lib().vdsa_hier_flops(ctypes.byref(p), ctypes.byref(cfg(window_mode=mode)), pool,
+                                       ctypes.byref(f)) == L.STATUS["VDSA_ERR_WINDOW"]
     m = ctypes.c_size_t()
     assert L.lib().compressed_global_attn_workspace_size(ctypes.byref(p), pool, ctypes.byref(m)) == 0
     assert m.value == 2 * n.value
@@ -274,6 +285,16 @@ FLOP_CASES = [
 def test_flop_counter_matches_oracle(grid, tile, window, shift):
     got = L.sta_flops(1, 3, 128, grid, tile, window, shift)
     assert got == R.sta_flops_ref(grid, tile, window, shift, head_dim=128, heads=3)
+
+
+@pytest.mark.parametrize("mode", ["inward", "cyclic"])
+@pytest.mark.parametrize("grid,tile,window,shift", FLOP_CASES + [
+    ((6, 10, 14), (2, 4, 4), (3, 3, 3), (1, 2, 2)),
+    ((3, 12, 16), (1, 4, 4), (1, 5, 3), (0, 2, 3)),
+])
+def test_flop_counter_window_modes(grid, tile, window, shift, mode):
+    got = L.sta_flops(1, 3, 128, grid, tile, window, shift, window_mode=mode)
+    assert got == R.sta_flops_ref(grid, tile, window, shift, head_dim=128, heads=3, window_mode=mode)
 
 
 def test_global_flop_counter_matches_oracle():

@@ -25,12 +25,11 @@ import torch
 import oracle as R
 import video_dit_sparse_amd as V
 from video_dit_sparse_amd import workloads as WL
-from _parity import head_f64
+from _parity import head_f64, rel_compare
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 TDT = {"bf16": torch.bfloat16, "f32": torch.float32}
-TOL_BWD = {"bf16": (6e-2, 5e-3), "f32": (1e-4, 1e-5)}
 
 
 def say(*a):
@@ -46,21 +45,6 @@ def _gpu():
 
 def tensors(shape, dtype, seed, n=4):
     return [WL.make_tensor(shape, dtype, DEV, seed=seed + i) for i in range(n)]
-
-
-def rel_compare(got, ref, dt, what):
-    g = R.to_f64(got)
-    r = np.asarray(ref, dtype=np.float64)
-    assert g.shape == r.shape, (what, g.shape, r.shape)
-    assert np.isfinite(g).all(), f"{what}: non-finite values"
-    rms = float(np.sqrt(np.mean(r * r)))
-    err = np.abs(g - r)
-    tmax, tmean = TOL_BWD[dt]
-    worst = float((err / (rms + np.abs(r))).max())
-    mean = float(err.mean()) / rms
-    say(f"  {what}: max err {worst:.2e} (rms + |ref|), mean {mean:.2e} rms (rms {rms:.3e})")
-    assert worst <= tmax and mean <= tmean, \
-        f"{what}: max err {worst:.3e} x (rms + |ref|) (<= {tmax}), mean {mean:.3e} rms (<= {tmean})"
 
 
 STA_BWD = [

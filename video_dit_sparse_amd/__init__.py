@@ -7,9 +7,11 @@ either merge fused into it (``global_pooled_attn_merge_fwd``), the pooling
 step alone (``kv_avgpool_fwd``), UltraGen's hierarchical and compressed
 global variants (``hier_pooled_attn_fwd``, ``compressed_global_attn_fwd``),
 the backward passes (``sta_attn_bwd``,
-``global_pooled_attn_bwd``) and the effective-work counters.
+``global_pooled_attn_bwd``) and the effective-work counters.  The
+sliding-tile calls take a ``window_mode`` ("clip", "inward", "cyclic").
 """
 from ._lib import (  # noqa: F401
+    WINDOW_MODES,
     VdsaError,
     abi_version,
     compressed_global_attn_fwd,

@@ -46,7 +46,12 @@ class Problem(ctypes.Structure):
 
 
 class StaCfg(ctypes.Structure):
-    _fields_ = [("tile", ctypes.c_int32 * 3), ("window", ctypes.c_int32 * 3), ("shift", ctypes.c_int32 * 3)]
+    _fields_ = [("tile", ctypes.c_int32 * 3), ("window", ctypes.c_int32 * 3), ("shift", ctypes.c_int32 * 3),
+                ("window_mode", ctypes.c_int32)]
+
+
+# vdsa_window_mode: how windows meet the grid edge
+WINDOW_MODES = {"clip": 0, "inward": 1, "cyclic": 2}
 
 
 class Strides(ctypes.Structure):
@@ -120,10 +125,13 @@ def make_problem(batch, heads, head_dim, grid, dtype: int, scale: float) -> Prob
                    int(dtype), float(scale))
 
 
-def make_cfg(tile, window, shift=(0, 0, 0)) -> StaCfg:
+def make_cfg(tile, window, shift=(0, 0, 0), window_mode: str = "clip") -> StaCfg:
+    if window_mode not in WINDOW_MODES:
+        raise ValueError(f"window_mode must be one of {tuple(WINDOW_MODES)}, got {window_mode!r}")
     c = StaCfg()
     for i in range(3):
         c.tile[i], c.window[i], c.shift[i] = int(tile[i]), int(window[i]), int(shift[i])
+    c.window_mode = WINDOW_MODES[window_mode]
     return c
 
 
@@ -178,16 +186,17 @@ def _same(q, *others):
 # ---------------------------------------------------------------- entry points
 def sta_attn_fwd(q, k, v, grid: Sequence[int], tile: Sequence[int], window: Sequence[int],
                  shift: Sequence[int] = (0, 0, 0), scale: Optional[float] = None, out=None,
-                 lse=None, return_lse: bool = False, stream=None):
+                 lse=None, return_lse: bool = False, stream=None, window_mode: str = "clip"):
     """Sliding-tile attention (see ``sta_attn_fwd`` in include/vdsa.h).
 
     q, k, v: [B, heads, N, D] device tensors (bf16 or fp32), N = T*H*W.
+    window_mode: "clip" (default), "inward" or "cyclic" (vdsa_window_mode).
     Returns O (and LSE [B, heads, N] fp32 if requested).
     """
     torch = _torch()
     _same(q, k, v)
     prob = _problem_for(q, grid, scale)
-    cfg = make_cfg(tile, window, shift)
+    cfg = make_cfg(tile, window, shift, window_mode)
     o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
     if lse is None and return_lse:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
@@ -362,14 +371,14 @@ def sta_attn_bwd_workspace_size(batch, heads, head_dim, grid, dtype_code=VDSA_BF
 
 
 def sta_attn_bwd(q, k, v, o, do, lse, grid, tile, window, shift=(0, 0, 0), scale=None, dq=None, dk=None, dv=None,
-                 workspace=None, stream=None):
+                 workspace=None, stream=None, window_mode: str = "clip"):
     """Gradients of ``sta_attn_fwd`` (``sta_attn_bwd`` in include/vdsa.h), from
     the forward's inputs, output ``o`` and ``lse``.  Returns (dQ, dK, dV)."""
     torch = _torch()
     _same(q, k, v, o, do)
     B, Hh, N, D = q.shape
     prob = _problem_for(q, grid, scale)
-    cfg = make_cfg(tile, window, shift)
+    cfg = make_cfg(tile, window, shift, window_mode)
     need = ctypes.c_size_t()
     check(lib().sta_attn_bwd_workspace_size(ctypes.byref(prob), ctypes.byref(need)))
     if workspace is None:
@@ -421,10 +430,10 @@ def kv_avgpool_fwd(x, grid, pool_hw, out=None, stream=None):
     return y
 
 
-def sta_flops(batch, heads, head_dim, grid, tile, window, shift=(0, 0, 0)) -> float:
+def sta_flops(batch, heads, head_dim, grid, tile, window, shift=(0, 0, 0), window_mode: str = "clip") -> float:
     """Effective FLOP of one sta_attn_fwd call (4*D per attended token pair)."""
     prob = make_problem(batch, heads, head_dim, grid, VDSA_BF16, 1.0)
-    cfg = make_cfg(tile, window, shift)
+    cfg = make_cfg(tile, window, shift, window_mode)
     f = ctypes.c_double()
     check(lib().vdsa_sta_flops(ctypes.byref(prob), ctypes.byref(cfg), ctypes.byref(f)))
     return f.value

@@ -121,10 +121,37 @@ vdsa_status check_sta_cfg(const vdsa_sta_cfg* c) {
     if (c->shift[d] < 0 || c->shift[d] >= c->tile[d])
       return fail(VDSA_ERR_WINDOW, "shift[%s] = %d must be in [0, tile = %d)", nm[d], c->shift[d], c->tile[d]);
   }
+  if (c->window_mode != VDSA_WINDOW_CLIP && c->window_mode != VDSA_WINDOW_INWARD &&
+      c->window_mode != VDSA_WINDOW_CYCLIC)
+    return fail(VDSA_ERR_WINDOW, "window_mode = %d is not a vdsa_window_mode", c->window_mode);
   return VDSA_OK;
 }
 
 int tiles_along(int L, int b, int s) { return (L + s + b - 1) / b; }
+
+// Lattice offset the kernels tile with: the cyclic mode tiles the rolled
+// grid from 0 and carries the shift as the roll instead.
+int lattice_shift(const vdsa_sta_cfg* c, int d) { return c->window_mode == VDSA_WINDOW_CYCLIC ? 0 : c->shift[d]; }
+
+// Sliding-tile geometry of cfg on the token grid: query tiles, window radii,
+// the window mode and, for the cyclic mode, the roll; keys on the same grid.
+void set_sta_geometry(vdsa::BoxAttnParams& g, const vdsa_problem* prob, const vdsa_sta_cfg* cfg) {
+  g.qT = prob->grid_t; g.qH = prob->grid_h; g.qW = prob->grid_w;
+  g.bT = cfg->tile[0]; g.bH = cfg->tile[1]; g.bW = cfg->tile[2];
+  g.sT = lattice_shift(cfg, 0); g.sH = lattice_shift(cfg, 1); g.sW = lattice_shift(cfg, 2);
+  g.nT = tiles_along(g.qT, g.bT, g.sT);
+  g.nH = tiles_along(g.qH, g.bH, g.sH);
+  g.nW = tiles_along(g.qW, g.bW, g.sW);
+  g.rT = (cfg->window[0] - 1) / 2; g.rH = (cfg->window[1] - 1) / 2; g.rW = (cfg->window[2] - 1) / 2;
+  g.kT = g.qT; g.kH = g.qH; g.kW = g.qW;
+  g.dense_keys = 0;
+  g.wmode = cfg->window_mode == VDSA_WINDOW_INWARD ? vdsa::WIN_INWARD : vdsa::WIN_CLIP;
+  const bool cyc = cfg->window_mode == VDSA_WINDOW_CYCLIC;
+  // a roll by s is a roll by s mod L (s may exceed L when the tile does)
+  g.rlT = cyc ? cfg->shift[0] % g.qT : 0;
+  g.rlH = cyc ? cfg->shift[1] % g.qH : 0;
+  g.rlW = cyc ? cfg->shift[2] % g.qW : 0;
+}
 
 // Largest number of real tokens in one tile along a dim.
 int max_tile_extent(int L, int b, int s) {
@@ -553,15 +580,7 @@ vdsa_status sta_attn_fwd(const vdsa_problem* prob, const vdsa_sta_cfg* cfg, cons
   bp.lse = lse;
   bp.batch = prob->batch;
   bp.heads = prob->heads;
-  bp.qT = prob->grid_t; bp.qH = prob->grid_h; bp.qW = prob->grid_w;
-  bp.bT = cfg->tile[0]; bp.bH = cfg->tile[1]; bp.bW = cfg->tile[2];
-  bp.sT = cfg->shift[0]; bp.sH = cfg->shift[1]; bp.sW = cfg->shift[2];
-  bp.nT = tiles_along(bp.qT, bp.bT, bp.sT);
-  bp.nH = tiles_along(bp.qH, bp.bH, bp.sH);
-  bp.nW = tiles_along(bp.qW, bp.bW, bp.sW);
-  bp.rT = (cfg->window[0] - 1) / 2; bp.rH = (cfg->window[1] - 1) / 2; bp.rW = (cfg->window[2] - 1) / 2;
-  bp.kT = bp.qT; bp.kH = bp.qH; bp.kW = bp.qW;
-  bp.dense_keys = 0;
+  set_sta_geometry(bp, prob, cfg);
   return launch_attn(prob, bp, (hipStream_t)stream);
 }
 
@@ -726,6 +745,8 @@ vdsa_status hier_pooled_attn_fwd(const vdsa_problem* prob, const vdsa_sta_cfg* c
   vdsa_status s;
   if ((s = check_problem(prob)) != VDSA_OK) return s;
   if ((s = check_sta_cfg(cfg)) != VDSA_OK) return s;
+  if (cfg->window_mode != VDSA_WINDOW_CLIP)
+    return fail(VDSA_ERR_WINDOW, "hier_pooled_attn_fwd supports window_mode VDSA_WINDOW_CLIP only");
   const int64_t N = n_tokens(prob);
   View vq{"q", q, q_strides, N}, vk{"k", k, k_strides, N}, vv{"v", v, v_strides, N}, vo{"o", o, o_strides, N};
   if ((s = check_pool(prob, pool_hw)) != VDSA_OK) return s;
@@ -856,17 +877,11 @@ vdsa_status sta_attn_bwd(const vdsa_problem* prob, const vdsa_sta_cfg* cfg, cons
   if ((s = launch_delta(prob, bv, delta, (hipStream_t)stream)) != VDSA_OK) return s;
   vdsa::BoxBwdParams P = bwd_params(prob, bv, lse, delta);
   vdsa::BoxAttnParams& g = P.g;
-  g.qT = prob->grid_t; g.qH = prob->grid_h; g.qW = prob->grid_w;
-  g.bT = cfg->tile[0]; g.bH = cfg->tile[1]; g.bW = cfg->tile[2];
-  g.sT = cfg->shift[0]; g.sH = cfg->shift[1]; g.sW = cfg->shift[2];
-  g.nT = tiles_along(g.qT, g.bT, g.sT);
-  g.nH = tiles_along(g.qH, g.bH, g.sH);
-  g.nW = tiles_along(g.qW, g.bW, g.sW);
-  g.rT = (cfg->window[0] - 1) / 2; g.rH = (cfg->window[1] - 1) / 2; g.rW = (cfg->window[2] - 1) / 2;
-  g.kT = g.qT; g.kH = g.qH; g.kW = g.qW;
-  g.dense_keys = 0;
-  // the window relation is symmetric: the dK/dV pass walks the same boxes
+  set_sta_geometry(g, prob, cfg);
   if ((s = launch_bwd_pass(prob, P, false, (hipStream_t)stream)) != VDSA_OK) return s;
+  // The clipped relation is symmetric (also in the rolled grid), so the dK/dV
+  // pass walks the same boxes; inward windows walk their transpose.
+  if (g.wmode == vdsa::WIN_INWARD) g.wmode = vdsa::WIN_INWARD_T;
   if ((s = launch_bwd_pass(prob, P, true, (hipStream_t)stream)) != VDSA_OK) return s;
   return ok();
 }
@@ -971,16 +986,20 @@ vdsa_status vdsa_sta_flops(const vdsa_problem* prob, const vdsa_sta_cfg* cfg, do
   // The window mask is a product over dims and tile sizes factorise, so the
   // attended-pair count is the product of per-dim counts
   //   sum_a size(a) * sum_{|c-a| <= r} size(c).
+  // (the cyclic mode counts on the rolled grid, tiled from 0)
   const int L[3] = {prob->grid_t, prob->grid_h, prob->grid_w};
+  const int mode = cfg->window_mode == VDSA_WINDOW_INWARD ? vdsa::WIN_INWARD : vdsa::WIN_CLIP;
   double pairs = 1.0;
   for (int d = 0; d < 3; ++d) {
-    const int b = cfg->tile[d], sh = cfg->shift[d], r = (cfg->window[d] - 1) / 2;
+    const int b = cfg->tile[d], sh = lattice_shift(cfg, d), r = (cfg->window[d] - 1) / 2;
     const int n = tiles_along(L[d], b, sh);
     auto size = [&](int i) { return std::min(L[d], (i + 1) * b - sh) - std::max(0, i * b - sh); };
     double acc = 0.0;
     for (int a = 0; a < n; ++a) {
+      int c0, c1;
+      vdsa::window_range(a, r, n, mode, c0, c1);
       double keys = 0.0;
-      for (int c = std::max(0, a - r); c <= std::min(n - 1, a + r); ++c) keys += size(c);
+      for (int c = c0; c <= c1; ++c) keys += size(c);
       acc += size(a) * keys;
     }
     pairs *= acc;
@@ -994,6 +1013,8 @@ vdsa_status vdsa_hier_flops(const vdsa_problem* prob, const vdsa_sta_cfg* cfg, c
   vdsa_status s;
   if ((s = check_problem(prob)) != VDSA_OK) return s;
   if ((s = check_sta_cfg(cfg)) != VDSA_OK) return s;
+  if (cfg->window_mode != VDSA_WINDOW_CLIP)
+    return fail(VDSA_ERR_WINDOW, "vdsa_hier_flops supports window_mode VDSA_WINDOW_CLIP only");
   if ((s = check_pool(prob, pool_hw)) != VDSA_OK) return s;
   if (!flops) return fail(VDSA_ERR_NULL, "flops is NULL");
   // per dim: sum over query tiles of size(a) * cells intersecting the window

@@ -126,7 +126,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
     const int r = j - jt * plane;
     const int jh = r / qb.ew;
     const int jw = r - jh * qb.ew;
-    qtok = (uint32_t)(((qb.t0 + jt) * p.qH + qb.h0 + jh) * p.qW + qb.w0 + jw);
+    qtok = q_token(p, qb.t0 + jt, qb.h0 + jh, qb.w0 + jw);
   }
   bf16x8 qf[KSTEPS];
   {
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
     const uint32_t r = (uint32_t)j - jt * fd_plane.d;
     const uint32_t jh = fast_div(r, fd_row);
     const uint32_t jw = r - jh * fd_row.d;
-    return ((kb.t0 + jt) * p.kH + kb.h0 + jh) * p.kW + kb.w0 + jw;
+    return k_token(p, kb.t0 + (int)jt, kb.h0 + (int)jh, kb.w0 + (int)jw);
   };
 
   // V mapping: thread owns 16-byte chunk vc (head_dim [8vc, 8vc+8)) of keys

@@ -179,7 +179,7 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
     const int r = j - jt * plane;
     const int jh = r / qb.ew;
     const int jw = r - jh * qb.ew;
-    qtok[qt] = (uint32_t)(((qb.t0 + jt) * p.qH + qb.h0 + jh) * p.qW + qb.w0 + jw);
+    qtok[qt] = q_token(p, qb.t0 + jt, qb.h0 + jh, qb.w0 + jw);
     const char* src = qp + qtok[qt] * q_row + 16 * G;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[qt][ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + 64 * ks));
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
     const uint32_t r = (uint32_t)j - jt * fd_plane.d;
     const uint32_t jh = fast_div(r, fd_row);
     const uint32_t jw = r - jh * fd_row.d;
-    return ((kb.t0 + jt) * p.kH + kb.h0 + jh) * p.kW + kb.w0 + jw;
+    return k_token(p, kb.t0 + (int)jt, kb.h0 + (int)jh, kb.w0 + (int)jw);
   };
   auto stage_of = [&](int blk) -> char* { return lds + (blk % NSTAGE) * STAGE; };
 

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(NTHREADS) void box_attn_bwd_f32_kernel(const BoxBwd
   {
     const int j = min(jo, ovol - 1);
     const int jt = j / (ob.eh * ob.ew), r = j % (ob.eh * ob.ew);
-    own_tok = ((ob.t0 + jt) * g.qH + ob.h0 + r / ob.ew) * g.qW + ob.w0 + r % ob.ew;
+    own_tok = (int)q_token(g, ob.t0 + jt, ob.h0 + r / ob.ew, ob.w0 + r % ob.ew);
   }
   // own operands: (q, dO) in the dQ pass, (k, v) in the dK/dV pass
   float a[DPL], c[DPL], acc1[DPL], acc2[DPL];
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(NTHREADS) void box_attn_bwd_f32_kernel(const BoxBwd
       const int r = e / HD, d = e % HD;
       const int j = min(r0 + r, ivol - 1);
       const int jt = j / (ib.eh * ib.ew), rr = j % (ib.eh * ib.ew);
-      const int tok = ((ib.t0 + jt) * g.kH + ib.h0 + rr / ib.ew) * g.kW + ib.w0 + rr % ib.ew;
+      const int tok = (int)k_token(g, ib.t0 + jt, ib.h0 + rr / ib.ew, ib.w0 + rr % ib.ew);
       xs[r][d] = KV ? qp[(int64_t)tok * P.q_sn + d] : kp[(int64_t)tok * P.k_sn + d];
       ys[r][d] = KV ? dop[(int64_t)tok * P.do_sn + d] : vp[(int64_t)tok * P.v_sn + d];
       if (KV && d == 0) {

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bwd_bf16_kernel(const BoxBwd
     const int r = j - jt * plane;
     const int jh = r / ob.ew;
     const int jw = r - jh * ob.ew;
-    own_tok = (uint32_t)(((ob.t0 + jt) * g.qH + ob.h0 + jh) * g.qW + ob.w0 + jw);
+    own_tok = q_token(g, ob.t0 + jt, ob.h0 + jh, ob.w0 + jw);
   }
   bf16x8 af[KS], bf[KS];
 #pragma unroll
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bwd_bf16_kernel(const BoxBwd
     const uint32_t r = (uint32_t)j - jt * fd_plane.d;
     const uint32_t jh = fast_div(r, fd_row);
     const uint32_t jw = r - jh * fd_row.d;
-    return ((ib.t0 + jt) * g.kH + ib.h0 + jh) * g.kW + ib.w0 + jw;
+    return k_token(g, ib.t0 + (int)jt, ib.h0 + (int)jh, ib.w0 + (int)jw);
   };
 
   const int row_in_chunk = 8 * (l16 >> 2) + (l16 & 3);

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(NTHREADS) void box_attn_f32_kernel(const BoxAttnPar
   {
     const int j = min(jq, qvol - 1);
     const int jt = j / (qeh * qew), r = j % (qeh * qew);
-    qtok = ((qt0 + jt) * p.qH + qh0 + r / qew) * p.qW + qw0 + r % qew;
+    qtok = (int)q_token(p, qt0 + jt, qh0 + r / qew, qw0 + r % qew);
   }
   float q[DPL], o[DPL];
 #pragma unroll
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(NTHREADS) void box_attn_f32_kernel(const BoxAttnPar
       const int r = e / HD, d = e % HD;
       const int j = min(k0 + r, kvol - 1);
       const int jt = j / (keh * kew), rr = j % (keh * kew);
-      const int tok = ((kt0 + jt) * p.kH + kh0 + rr / kew) * p.kW + kw0 + rr % kew;
+      const int tok = (int)k_token(p, kt0 + jt, kh0 + rr / kew, kw0 + rr % kew);
       ks[r][d] = kp[(int64_t)tok * p.k_sn + d];
       vs[r][d] = vp[(int64_t)tok * p.v_sn + d];
     }

@@ -83,6 +83,17 @@ struct Box {
   int t0, h0, w0, et, eh, ew;
 };
 
+// Token index of box coordinate (t, h, w) on the query grid / the key grid.
+// Boxes live in the rolled grid when the window mode is cyclic (rl != 0):
+// rolled coordinate x holds the token at (x - rl) mod L.
+__device__ __forceinline__ int unroll(int x, int rl, int L) { return x - rl + (x < rl ? L : 0); }
+__device__ __forceinline__ uint32_t q_token(const BoxAttnParams& p, int t, int h, int w) {
+  return (uint32_t)((unroll(t, p.rlT, p.qT) * p.qH + unroll(h, p.rlH, p.qH)) * p.qW + unroll(w, p.rlW, p.qW));
+}
+__device__ __forceinline__ uint32_t k_token(const BoxAttnParams& p, int t, int h, int w) {
+  return (uint32_t)((unroll(t, p.rlT, p.kT) * p.kH + unroll(h, p.rlH, p.kH)) * p.kW + unroll(w, p.rlW, p.kW));
+}
+
 __device__ __forceinline__ void tile_boxes(const BoxAttnParams& p, int tile, Box& qb, Box& kb) {
   const int aw = tile % p.nW;
   const int ah = (tile / p.nW) % p.nH;
@@ -97,8 +108,9 @@ __device__ __forceinline__ void tile_boxes(const BoxAttnParams& p, int tile, Box
   if (p.dense_keys) {
     kb = Box{0, 0, 0, p.kT, p.kH, p.kW};
   } else {
-    auto wspan = [](int a, int r, int n, int b, int s, int L, int& lo, int& ext) {
-      const int c0 = max(0, a - r), c1 = min(n - 1, a + r);
+    auto wspan = [&](int a, int r, int n, int b, int s, int L, int& lo, int& ext) {
+      int c0, c1;
+      window_range(a, r, n, p.wmode, c0, c1);
       lo = max(0, c0 * b - s);
       ext = min(L, (c1 + 1) * b - s) - lo;
     };

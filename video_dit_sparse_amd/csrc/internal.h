@@ -49,6 +49,9 @@ struct BoxAttnParams {
   int32_t dense_keys;
   int32_t kpT, kpH, kpW;      // pooled keys (> 1): the key box is every k-grid cell holding
                               // a token of the window box; the k grid is the pooled grid
+  int32_t wmode;              // WIN_CLIP / WIN_INWARD / WIN_INWARD_T (window_range)
+  int32_t rlT, rlH, rlW;      // cyclic roll of the query and key grids (0: none): box
+                              // coordinate x' is the token at (x' - rl) mod L
   int32_t qblocks;            // query blocks per tile
   int32_t variant;            // which kernel shape the launcher runs (set by the host)
   int32_t total_wg;           // batch * heads * tiles * qblocks
@@ -63,6 +66,35 @@ struct BoxAttnParams {
   const float* w_g;           // MERGE_GATED: weight of this kernel's output per head
 };
 enum { MERGE_NONE = 0, MERGE_GATED = 1, MERGE_LSE = 2 };
+
+// How a window meets the lattice edge, per dim.  For query tile a of n tiles
+// and radius r, [c0, c1] are the key tiles of its window:
+//   WIN_CLIP:    [max(0, a - r), min(n - 1, a + r)];
+//   WIN_INWARD:  the 2r+1 tiles (all n if fewer) starting at
+//                clamp(a - r, 0, max(0, n - 2r - 1));
+//   WIN_INWARD_T the transpose of WIN_INWARD: the query tiles whose inward
+//                windows hold tile a.  The inward start is non-decreasing in
+//                the query tile, so these form an interval: the start values
+//                v in [max(0, a - 2r), min(m, a)], m = max(0, n - 2r - 1),
+//                and the queries taking them (v = 0 for every query up to r,
+//                v = m for every query from m + r on, else query v + r).
+enum { WIN_CLIP = 0, WIN_INWARD = 1, WIN_INWARD_T = 2 };
+__host__ __device__ inline int imax(int a, int b) { return a > b ? a : b; }
+__host__ __device__ inline int imin(int a, int b) { return a < b ? a : b; }
+__host__ __device__ inline void window_range(int a, int r, int n, int mode, int& c0, int& c1) {
+  if (mode == WIN_INWARD) {
+    c0 = imax(0, imin(a - r, n - (2 * r + 1)));
+    c1 = imin(n - 1, c0 + 2 * r);
+  } else if (mode == WIN_INWARD_T) {
+    const int m = imax(0, n - (2 * r + 1));
+    const int vlo = imax(0, a - 2 * r), vhi = imin(m, a);
+    c0 = vlo == 0 ? 0 : vlo + r;
+    c1 = vhi == m ? n - 1 : vhi + r;
+  } else {
+    c0 = imax(0, a - r);
+    c1 = imin(n - 1, a + r);
+  }
+}
 
 struct PoolParams {
   const void* x;
@@ -98,11 +130,13 @@ struct MergeParams {
 //   dQ pass:    own rows = queries (Q, dO in registers), iterated = their key
 //               boxes (K, V), exactly the forward's geometry.
 //   dK/dV pass: own rows = keys (K, V in registers), iterated = the queries
-//               whose windows contain the key tile.  The window relation
-//               |a - c| <= r is symmetric, so for sliding tiles this is the
-//               box around the key tile on the same lattice; for pooled keys
-//               (one tile over the pooled grid) it is every query (dense_keys
-//               over the query grid).
+//               whose windows contain the key tile.  The clipped window
+//               relation |a - c| <= r is symmetric, so for sliding tiles this
+//               is the box around the key tile on the same lattice (also in
+//               the rolled grid of the cyclic mode); inward windows take the
+//               transposed range (WIN_INWARD_T); for pooled keys (one tile
+//               over the pooled grid) it is every query (dense_keys over the
+//               query grid).
 struct BoxBwdParams {
   BoxAttnParams g;
   const void* q;
