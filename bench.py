@@ -104,6 +104,8 @@ def main():
     ap.add_argument("--dense-steps", type=int, default=3, help="full-window comparison calls (0 = skip)")
     ap.add_argument("--bwd-steps", type=int, default=3,
                     help="backward-pass calls of the local branch to time (0 = skip)")
+    ap.add_argument("--mode-steps", type=int, default=3,
+                    help="calls per window mode (inward, cyclic) of the local branch to time (0 = skip)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc runs)")
     args = ap.parse_args()
@@ -178,19 +180,22 @@ def main():
                 "kernel": ROOFLINE_KERNEL, "launch_ms": round(launch_ms, 4),
                 "flop_per_launch": launch_flops}
 
+    def timed(fn, n):
+        """Average ms of fn over n calls after one untimed call, with events
+        on the stream the library launches on."""
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        z.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(z) / n
+
     extra = {}
     if w.pool_hw is not None and args.steps > 0:
         # global branch: fused global + merge call against the two separate
         # calls, and the standalone exact (LSE) merge, each timed with events
-        def timed(fn, n):
-            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            fn()
-            a.record(stream)
-            for _ in range(n):
-                fn()
-            z.record(stream)
-            torch.cuda.synchronize()
-            return a.elapsed_time(z) / n
         lse_l = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
         V.sta_attn_fwd(q, k, v, w.grid, w.tile, w.window, w.shifts[0], scale=w.softmax_scale,
                        out=buf.local[0], lse=lse_l)
@@ -233,6 +238,19 @@ def main():
             "compressed_global_tflops": round(comp_fl / (comp_ms * 1e-3) / 1e12, 1)}
         log(f"[bench] hierarchical (2x2-pooled keys): {hier_ms:.3f} ms ({hier_fl / (hier_ms * 1e-3) / 1e12:.0f} TFLOP/s); "
             f"compressed global: {comp_ms:.3f} ms ({comp_fl / (comp_ms * 1e-3) / 1e12:.0f} TFLOP/s)")
+    if args.mode_steps > 0 and w.pool_hw is None:
+        # the local branch under the other window modes: edge windows moved
+        # inward (more attended pairs), and the grid rolled by half a tile
+        half = tuple(b // 2 for b in w.tile)
+        modes = {}
+        for mode, sh in (("inward", w.shifts[0]), ("cyclic", half)):
+            ms = timed(lambda: V.sta_attn_fwd(q, k, v, w.grid, w.tile, w.window, sh, scale=w.softmax_scale,
+                                              out=buf.local[0], window_mode=mode), args.mode_steps)
+            mf = V.sta_flops(w.batch, w.heads, w.head_dim, w.grid, w.tile, w.window, sh, window_mode=mode)
+            modes[mode] = {"shift": list(sh), "ms_per_call": round(ms, 3), "effective_flop": mf,
+                           "tflops": round(mf / (ms * 1e-3) / 1e12, 1)}
+            log(f"[bench] window mode {mode} (shift {sh}): {ms:.2f} ms, {mf / (ms * 1e-3) / 1e12:.0f} TFLOP/s")
+        extra["window_modes"] = modes
     if args.bwd_steps > 0:
         # backward of the local branch (first lattice shift): dQ, dK, dV from
         # the forward's output and LSE; effective work 10 * head_dim FLOP per
