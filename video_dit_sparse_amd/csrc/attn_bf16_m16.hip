@@ -262,8 +262,11 @@ __global__ __launch_bounds__(NW * 64, 2) void box_attn_bf16_m16_kernel(const Box
       bool grow = false;
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        float m = fmaxf(fmaxf(s[0][qt][0], s[0][qt][1]), fmaxf(s[0][qt][2], s[0][qt][3]));
-        m = fmaxf(m, fmaxf(fmaxf(s[1][qt][0], s[1][qt][1]), fmaxf(s[1][qt][2], s[1][qt][3])));
+        // a running chain, so that the compiler fuses it into three v_max3 and one v_max
+        float m = fmaxf(fmaxf(s[0][qt][0], s[0][qt][1]), s[0][qt][2]);
+        m = fmaxf(fmaxf(m, s[0][qt][3]), s[1][qt][0]);
+        m = fmaxf(fmaxf(m, s[1][qt][1]), s[1][qt][2]);
+        m = fmaxf(m, s[1][qt][3]);
         lmax[qt] = m;
         grow = grow || (m * cl2 > m_run[qt] + RESCALE_MARGIN);
       }
