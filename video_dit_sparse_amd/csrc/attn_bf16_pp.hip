@@ -27,12 +27,13 @@
 //
 // LDS: a ring of three stages of (16 KB K fragments + 16 KB V^T fragments),
 // each fragment the 1 KB operand of one MFMA, read as one contiguous 1 KB per
-// wave.  Block b+2 is requested at the start of M(b,1): K by direct
-// global->LDS loads, V into registers, stored transposed into its V^T
-// fragments in V(b+1,0).  K of block b+1 must have landed before group A's
-// M(b+1,0): A waits for it at the end of V(b,1), B at the end of M(b,1) (the
-// same barrier), each keeping the loads of block b+2 in flight.  The stage a
-// block overwrites was last read three phases before its first write.
+// wave.  Block b+2 is requested at the start of V(b,1), the softmax phase
+// with the most slack: K by direct global->LDS loads, V into registers,
+// stored transposed into its V^T fragments in V(b+1,0).  K of block b+1 must
+// have landed before group A's M(b+1,0): A waits for it at the end of V(b,1)
+// keeping the loads of block b+2 in flight, B at the end of M(b,1) (the same
+// barrier), before it requests block b+2.  The stage a block overwrites was
+// last read at least three phases before its first write.
 //
 // Fragment layouts (lane L = 16G + p of a wave):
 //   K fragment (c, t, ks): lane L holds head_dim [32ks + 8G, +8) of key row
@@ -407,12 +408,12 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
     phase_barrier();
     // M(blk, 1)
     __builtin_amdgcn_s_setprio(1);
-    if (more2) load_block(blk + 2);
     mphase(true, st, 0, true, st, 1);
     __builtin_amdgcn_s_setprio(0);
-    if (grp_b) vm_wait(more2);   // K of block blk+1 has landed
+    if (grp_b) vm_wait(false);   // K of block blk+1 has landed
     phase_barrier();
     // V(blk, 1)
+    if (more2) load_block(blk + 2);
     prefetch_pv(st, 1);
     softmax(nvalid - 32, partial_tag, false);
     if (!grp_b) vm_wait(more2);
