@@ -467,7 +467,7 @@ vdsa::BoxBwdParams bwd_params(const vdsa_problem* prob, const BwdViews& bv, cons
 // bT.. / sT.., iterated boxes from rT.. or dense_keys over kT..).
 vdsa_status launch_bwd_pass(const vdsa_problem* prob, vdsa::BoxBwdParams& P, bool kv, hipStream_t stream) {
   const int bf16 = prob->dtype == VDSA_BF16;
-  const int bm = vdsa::attn_bwd_block_m(bf16);
+  const int bm = vdsa::attn_bwd_block_m(bf16, kv);
   vdsa::BoxAttnParams& g = P.g;
   const int64_t mv = (int64_t)max_tile_extent(g.qT, g.bT, g.sT) * max_tile_extent(g.qH, g.bH, g.sH) *
                      max_tile_extent(g.qW, g.bW, g.sW);

@@ -19,7 +19,7 @@
 namespace vdsa {
 
 hipError_t launch_attn_bwd_bf16(const BoxBwdParams& p, bool kv, hipStream_t stream);
-int attn_bwd_bf16_block_m();
+int attn_bwd_bf16_block_m(bool kv);
 
 namespace {
 
@@ -217,7 +217,7 @@ int grid_for(int64_t work) {
 
 }  // namespace
 
-int attn_bwd_block_m(int bf16) { return bf16 ? attn_bwd_bf16_block_m() : OPB; }
+int attn_bwd_block_m(int bf16, bool kv) { return bf16 ? attn_bwd_bf16_block_m(kv) : OPB; }
 
 hipError_t launch_attn_bwd_dq(const BoxBwdParams& p, int bf16, hipStream_t stream) {
   if (bf16) return launch_attn_bwd_bf16(p, false, stream);

@@ -7,12 +7,16 @@
 //   P = exp(scale q.k - LSE),  dP = dO.v,  dS = P * (dP - delta),
 //   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
 // Two passes share one kernel template (BoxBwdParams):
-//   dQ pass (KV = false): a wave owns 16 queries (Q and dO resident as MFMA B
-//     operands) and walks the key box: S^T = K Q^T, dP^T = V dO^T,
-//     dQ^T += K^T dS^T.
-//   dK/dV pass (KV = true): a wave owns 16 keys (K and V resident) and walks
-//     the queries whose windows contain its key tile: S = Q K^T, dP = dO V^T,
-//     dK^T += Q^T dS, dV^T += dO^T P.
+//   dQ pass (KV = false): a wave owns OT tiles of 16 queries (Q and dO
+//     resident as MFMA B operands) and walks the key box: S^T = K Q^T,
+//     dP^T = V dO^T, dQ^T += K^T dS^T.
+//   dK/dV pass (KV = true): a wave owns OT tiles of 16 keys (K and V
+//     resident) and walks the queries whose windows contain its key tile:
+//     S = Q K^T, dP = dO V^T, dK^T += Q^T dS, dV^T += dO^T P.
+// Every operand fragment read from LDS feeds OT products, one per own tile.
+// The dQ pass runs OT = 2 with 4 waves and 32-token blocks (two workgroups
+// per CU); the dK/dV pass, whose two accumulator sets leave no registers for
+// a second tile, runs OT = 1 with 8 waves and 64-token blocks.
 // In both, the iterated tokens sit on the MFMA rows and the owned tokens on
 // the column, so every probability of an owned token is computed by one lane
 // group and the products reuse the forward's operand layouts: iterated rows
@@ -20,7 +24,8 @@
 // 8*(r/4) + 4t + r%4) so that the lane group G holds tokens 8G .. 8G+7 after
 // the two tiles, which is exactly the k-slice of the following product.
 //
-// Per 64-token block of the iterated box, LDS holds (double-buffered):
+// Per block of the iterated box (one or two 32-token chunks), LDS holds
+// (double-buffered):
 //   X fragments (K or Q; DMA'd, as the forward's K fragments),
 //   Y fragments (V or dO; DMA'd the same way),
 //   X^T fragments (K^T or Q^T; transposed through registers with the
@@ -44,34 +49,41 @@ typedef __attribute__((address_space(3))) uint32_t lds_u32;
 constexpr int BUF_FLAGS = 0x00020000;   // raw buffer resource word 3 (gfx9-class)
 
 constexpr int HD = 128;
-constexpr int BLOCK_N = 64;            // iterated tokens per block
-constexpr int NW = 8;                  // waves per workgroup
-constexpr int BLOCK_M = NW * 16;       // owned tokens per workgroup
 constexpr int KS = HD / 32;            // 32-wide head_dim steps
 constexpr int ND = HD / 16;            // 16-row head_dim tiles
-constexpr int NFRAG = 2 * 2 * KS;      // (chunk, t, ks) fragments of X and of Y
-constexpr int FRAG_BYTES = NFRAG * 1024;
-constexpr int T_BYTES = 2 * ND * 1024; // (chunk, dt) fragments of X^T, Y^T
-constexpr int DMA_W = NFRAG / NW;      // fragments per wave per tensor
-constexpr int VPT = BLOCK_N * HD / 8 / (NW * 64);   // 16-byte chunks per thread for a transposed copy
-constexpr int NKG = BLOCK_N / VPT;
 constexpr int WAIT_VMCNT0 = 0x0F70;    // s_waitcnt vmcnt(0), other counters untouched
-static_assert(DMA_W * NW == NFRAG && VPT == 2 && VPT * NKG == BLOCK_N, "work split");
 
-template <bool KV>
-struct Layout {
+// Shape of one pass: OT own 16-token tiles per wave, NW waves, NCH 32-token
+// chunks per block of the iterated box.
+template <bool KV, int OT_, int NW_, int NCH_>
+struct Cfg {
+  static constexpr int OT = OT_, NW = NW_, NCH = NCH_;
+  static constexpr int BLOCK_N = 32 * NCH;                 // iterated tokens per block
+  static constexpr int BLOCK_M = NW * 16 * OT;             // owned tokens per workgroup
+  static constexpr int NFRAG = NCH * 2 * KS;               // (chunk, t, ks) fragments of X and of Y
+  static constexpr int FRAG_BYTES = NFRAG * 1024;
+  static constexpr int T_BYTES = NCH * ND * 1024;          // (chunk, dt) fragments of X^T, Y^T
+  static constexpr int DMA_W = NFRAG / NW;                 // fragments per wave per tensor
+  static constexpr int VPT = BLOCK_N * HD / 8 / (NW * 64); // 16-byte chunks per thread for a transposed copy
+  static constexpr int NKG = BLOCK_N / VPT;
+  // LDS layout of one stage
   static constexpr int XF = 0;
   static constexpr int YF = FRAG_BYTES;
   static constexpr int XT = 2 * FRAG_BYTES;
-  static constexpr int YT = XT + T_BYTES;                     // dK/dV pass only
+  static constexpr int YT = XT + T_BYTES;                  // dK/dV pass only
   static constexpr int LSE = KV ? YT + T_BYTES : XT + T_BYTES;
   static constexpr int DEL = LSE + BLOCK_N * 4;
   static constexpr int STAGE = KV ? DEL + BLOCK_N * 4 : XT + T_BYTES;
+  static_assert(DMA_W * NW == NFRAG && VPT == 2 && VPT * NKG == BLOCK_N && BLOCK_N <= 64, "work split");
 };
+using CfgDQ = Cfg<false, 2, 4, 1>;
+using CfgKV = Cfg<true, 1, 8, 2>;
 
-template <bool KV>
-__global__ __launch_bounds__(NW * 64) void box_attn_bwd_bf16_kernel(const BoxBwdParams P) {
-  using Lay = Layout<KV>;
+template <bool KV, class C>
+__global__ __launch_bounds__(C::NW * 64) void box_attn_bwd_bf16_kernel(const BoxBwdParams P) {
+  using Lay = C;
+  constexpr int OT = C::OT, NW = C::NW, NCH = C::NCH, BLOCK_N = C::BLOCK_N, BLOCK_M = C::BLOCK_M;
+  constexpr int DMA_W = C::DMA_W, VPT = C::VPT, NKG = C::NKG;
   const BoxAttnParams& g = P.g;
   __shared__ __attribute__((aligned(16))) char lds[2 * Lay::STAGE];
 
@@ -116,29 +128,33 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bwd_bf16_kernel(const BoxBwd
   constexpr float LOG2E = 1.4426950408889634f;
   const float cl2 = g.scale_log2e;
 
-  // ---- this lane's own token: column l16 of the wave's 16-token tile
-  const int jo = o0 + wave * 16 + l16;
-  const bool own_valid = jo < ovol;
-  uint32_t own_tok;
-  {
+  // ---- this lane's own tokens: column l16 of each of the wave's OT tiles
+  bool own_valid[OT];
+  uint32_t own_tok[OT];
+  bf16x8 af[OT][KS], bf[OT][KS];
+  float own_lse2[OT], own_del[OT];
+#pragma unroll
+  for (int ot = 0; ot < OT; ++ot) {
+    const int jo = o0 + (wave * OT + ot) * 16 + l16;
+    own_valid[ot] = jo < ovol;
     const int j = min(jo, ovol - 1);
     const int plane = ob.eh * ob.ew;
     const int jt = j / plane;
     const int r = j - jt * plane;
     const int jh = r / ob.ew;
     const int jw = r - jh * ob.ew;
-    own_tok = q_token(g, ob.t0 + jt, ob.h0 + jh, ob.w0 + jw);
-  }
-  bf16x8 af[KS], bf[KS];
+    own_tok[ot] = q_token(g, ob.t0 + jt, ob.h0 + jh, ob.w0 + jw);
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    af[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(ap + own_tok * a_row + 64 * ks + 16 * G));
-    bf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(bp + own_tok * b_row + 64 * ks + 16 * G));
-  }
-  float own_lse2 = 0.f, own_del = 0.f;
-  if constexpr (!KV) {
-    own_lse2 = lse_bh[own_tok] * LOG2E;
-    own_del = del_bh[own_tok];
+    for (int ks = 0; ks < KS; ++ks) {
+      af[ot][ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(ap + own_tok[ot] * a_row + 64 * ks + 16 * G));
+      bf[ot][ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(bp + own_tok[ot] * b_row + 64 * ks + 16 * G));
+    }
+    own_lse2[ot] = 0.f;
+    own_del[ot] = 0.f;
+    if constexpr (!KV) {
+      own_lse2[ot] = lse_bh[own_tok[ot]] * LOG2E;
+      own_del[ot] = del_bh[own_tok[ot]];
+    }
   }
 
   // ---- iterated box addressing: token j of the box -> token index
@@ -202,7 +218,7 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bwd_bf16_kernel(const BoxBwd
         *(lds_u32*)(uintptr_t)(sbase + Lay::YT + off) = __builtin_amdgcn_perm(yreg[1][e >> 1], yreg[0][e >> 1], sel);
     }
     if constexpr (KV) {
-      if (wave == 0) {
+      if (wave == 0 && lane < BLOCK_N) {
         *(float*)(lds + stage * Lay::STAGE + Lay::LSE + 4 * lane) = lse_reg;
         *(float*)(lds + stage * Lay::STAGE + Lay::DEL + 4 * lane) = del_reg;
       }
@@ -211,16 +227,18 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bwd_bf16_kernel(const BoxBwd
 
   // A-operand read offset of a transposed fragment in chunk c: piece
   // 16G + (l16 ^ ((G << 1) | c))
-  int t_rd[2];
+  int t_rd[NCH];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) t_rd[c] = c * ND * 1024 + (16 * G + (l16 ^ ((G << 1) | c))) * 16;
+  for (int c = 0; c < NCH; ++c) t_rd[c] = c * ND * 1024 + (16 * G + (l16 ^ ((G << 1) | c))) * 16;
 
-  f32x4 acc1[ND], acc2[ND];
+  f32x4 acc1[ND][OT], acc2[ND][OT];
 #pragma unroll
-  for (int dt = 0; dt < ND; ++dt) {
-    acc1[dt] = f32x4{};
-    acc2[dt] = f32x4{};
-  }
+  for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+    for (int ot = 0; ot < OT; ++ot) {
+      acc1[dt][ot] = f32x4{};
+      acc2[dt][ot] = f32x4{};
+    }
 
   load_block(0, 0);
   store_t(0);
@@ -236,61 +254,77 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bwd_bf16_kernel(const BoxBwd
     const int nvalid = PARTIAL ? ivol - blk * BLOCK_N : BLOCK_N;
 
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      // S and dP, register v of tile t = iterated row 32c + 8G + 4t + v
-      f32x4 s[2], dp[2];
+    for (int c = 0; c < NCH; ++c) {
+      // S and dP, register v of tile (t, ot) = iterated row 32c + 8G + 4t + v
+      f32x4 s[2][OT], dp[2][OT];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        s[t] = f32x4{};
-        dp[t] = f32x4{};
+#pragma unroll
+        for (int ot = 0; ot < OT; ++ot) {
+          s[t][ot] = f32x4{};
+          dp[t][ot] = f32x4{};
+        }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const int f = (c * 2 + t) * KS + ks;
           const bf16x8 xa = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + Lay::XF + f * 1024 + lane * 16));
           const bf16x8 ya = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + Lay::YF + f * 1024 + lane * 16));
-          s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, af[ks], s[t], 0, 0, 0);
-          dp[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ya, bf[ks], dp[t], 0, 0, 0);
+#pragma unroll
+          for (int ot = 0; ot < OT; ++ot) {
+            s[t][ot] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, af[ot][ks], s[t][ot], 0, 0, 0);
+            dp[t][ot] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ya, bf[ot][ks], dp[t][ot], 0, 0, 0);
+          }
         }
       }
-      float l2[8], dl[8];
+      float l2[OT][8], dl[OT][8];
       if constexpr (KV) {
         const f32x4 la = *(const f32x4*)(st + Lay::LSE + 4 * (32 * c + 8 * G));
         const f32x4 lb = *(const f32x4*)(st + Lay::LSE + 4 * (32 * c + 8 * G + 4));
         const f32x4 da = *(const f32x4*)(st + Lay::DEL + 4 * (32 * c + 8 * G));
         const f32x4 db = *(const f32x4*)(st + Lay::DEL + 4 * (32 * c + 8 * G + 4));
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          l2[v] = la[v];
-          l2[v + 4] = lb[v];
-          dl[v] = da[v];
-          dl[v + 4] = db[v];
-        }
+        for (int ot = 0; ot < OT; ++ot)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            l2[ot][v] = la[v];
+            l2[ot][v + 4] = lb[v];
+            dl[ot][v] = da[v];
+            dl[ot][v + 4] = db[v];
+          }
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          l2[e] = own_lse2;
-          dl[e] = own_del;
-        }
-      }
-      bf16x8 pb, dsb;
+        for (int ot = 0; ot < OT; ++ot)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int t = e >> 2, v = e & 3;
-        float pv = __builtin_amdgcn_exp2f(fmaf(s[t][v], cl2, -l2[e]));
-        if constexpr (PARTIAL) {
-          if (32 * c + 8 * G + e >= nvalid) pv = 0.f;
-        }
-        pb[e] = (__bf16)pv;
-        dsb[e] = (__bf16)(pv * (dp[t][v] - dl[e]));
+          for (int e = 0; e < 8; ++e) {
+            l2[ot][e] = own_lse2[ot];
+            dl[ot][e] = own_del[ot];
+          }
       }
+      bf16x8 pb[OT], dsb[OT];
+#pragma unroll
+      for (int ot = 0; ot < OT; ++ot)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int t = e >> 2, v = e & 3;
+          float pv = __builtin_amdgcn_exp2f(fmaf(s[t][ot][v], cl2, -l2[ot][e]));
+          if constexpr (PARTIAL) {
+            if (32 * c + 8 * G + e >= nvalid) pv = 0.f;
+          }
+          pb[ot][e] = (__bf16)pv;
+          dsb[ot][e] = (__bf16)(pv * (dp[t][ot][v] - dl[ot][e]));
+        }
       // acc1 += X^T dS (dQ^T or dK^T); dK/dV pass: acc2 += Y^T P (dV^T)
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) {
         const bf16x8 xt = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + Lay::XT + t_rd[c] + dt * 1024));
-        acc1[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xt, dsb, acc1[dt], 0, 0, 0);
+#pragma unroll
+        for (int ot = 0; ot < OT; ++ot)
+          acc1[dt][ot] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xt, dsb[ot], acc1[dt][ot], 0, 0, 0);
         if constexpr (KV) {
           const bf16x8 yt = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + Lay::YT + t_rd[c] + dt * 1024));
-          acc2[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yt, pb, acc2[dt], 0, 0, 0);
+#pragma unroll
+          for (int ot = 0; ot < OT; ++ot)
+            acc2[dt][ot] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yt, pb[ot], acc2[dt][ot], 0, 0, 0);
         }
       }
     }
@@ -305,40 +339,43 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bwd_bf16_kernel(const BoxBwd
   for (int blk = 0; blk < nfull; ++blk) process(blk, std::false_type{});
   if (last_partial) process(nib - 1, std::true_type{});
 
-  // ---- epilogue: register v of acc tile dt is head_dim 16dt + 4G + v of
-  // the lane's own token
-  if (!own_valid) return;
+  // ---- epilogue: register v of acc tile (dt, ot) is head_dim 16dt + 4G + v
+  // of the lane's own token of tile ot
   const float s1 = P.scale;
-  if constexpr (!KV) {
-    char* dst = (char*)P.dq + 2 * (b * P.dq_sb + h * P.dq_sh) + own_tok * (2u * (uint32_t)P.dq_sn) + 8 * G;
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt) {
-      bf16x4 ov;
+  for (int ot = 0; ot < OT; ++ot) {
+    if (!own_valid[ot]) continue;
+    if constexpr (!KV) {
+      char* dst = (char*)P.dq + 2 * (b * P.dq_sb + h * P.dq_sh) + own_tok[ot] * (2u * (uint32_t)P.dq_sn) + 8 * G;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) ov[v] = (__bf16)(acc1[dt][v] * s1);
-      *(u32x2*)(dst + 32 * dt) = __builtin_bit_cast(u32x2, ov);
-    }
-  } else if (P.grad_f32) {
-    float* dk = (float*)P.dk + b * P.dk_sb + h * P.dk_sh + (int64_t)own_tok * P.dk_sn + 4 * G;
-    float* dv = (float*)P.dv + b * P.dv_sb + h * P.dv_sh + (int64_t)own_tok * P.dv_sn + 4 * G;
+      for (int dt = 0; dt < ND; ++dt) {
+        bf16x4 ov;
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt) {
-      *(f32x4*)(dk + 16 * dt) = acc1[dt] * s1;
-      *(f32x4*)(dv + 16 * dt) = acc2[dt];
-    }
-  } else {
-    char* dk = (char*)P.dk + 2 * (b * P.dk_sb + h * P.dk_sh) + own_tok * (2u * (uint32_t)P.dk_sn) + 8 * G;
-    char* dv = (char*)P.dv + 2 * (b * P.dv_sb + h * P.dv_sh) + own_tok * (2u * (uint32_t)P.dv_sn) + 8 * G;
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt) {
-      bf16x4 kv, vv;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        kv[v] = (__bf16)(acc1[dt][v] * s1);
-        vv[v] = (__bf16)acc2[dt][v];
+        for (int v = 0; v < 4; ++v) ov[v] = (__bf16)(acc1[dt][ot][v] * s1);
+        *(u32x2*)(dst + 32 * dt) = __builtin_bit_cast(u32x2, ov);
       }
-      *(u32x2*)(dk + 32 * dt) = __builtin_bit_cast(u32x2, kv);
-      *(u32x2*)(dv + 32 * dt) = __builtin_bit_cast(u32x2, vv);
+    } else if (P.grad_f32) {
+      float* dk = (float*)P.dk + b * P.dk_sb + h * P.dk_sh + (int64_t)own_tok[ot] * P.dk_sn + 4 * G;
+      float* dv = (float*)P.dv + b * P.dv_sb + h * P.dv_sh + (int64_t)own_tok[ot] * P.dv_sn + 4 * G;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) {
+        *(f32x4*)(dk + 16 * dt) = acc1[dt][ot] * s1;
+        *(f32x4*)(dv + 16 * dt) = acc2[dt][ot];
+      }
+    } else {
+      char* dk = (char*)P.dk + 2 * (b * P.dk_sb + h * P.dk_sh) + own_tok[ot] * (2u * (uint32_t)P.dk_sn) + 8 * G;
+      char* dv = (char*)P.dv + 2 * (b * P.dv_sb + h * P.dv_sh) + own_tok[ot] * (2u * (uint32_t)P.dv_sn) + 8 * G;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) {
+        bf16x4 kv, vv;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          kv[v] = (__bf16)(acc1[dt][ot][v] * s1);
+          vv[v] = (__bf16)acc2[dt][ot][v];
+        }
+        *(u32x2*)(dk + 32 * dt) = __builtin_bit_cast(u32x2, kv);
+        *(u32x2*)(dv + 32 * dt) = __builtin_bit_cast(u32x2, vv);
+      }
     }
   }
 }
@@ -347,12 +384,12 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bwd_bf16_kernel(const BoxBwd
 
 hipError_t launch_attn_bwd_bf16(const BoxBwdParams& p, bool kv, hipStream_t stream) {
   if (kv)
-    hipLaunchKernelGGL(box_attn_bwd_bf16_kernel<true>, dim3(p.g.total_wg), dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((box_attn_bwd_bf16_kernel<true, CfgKV>), dim3(p.g.total_wg), dim3(CfgKV::NW * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL(box_attn_bwd_bf16_kernel<false>, dim3(p.g.total_wg), dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((box_attn_bwd_bf16_kernel<false, CfgDQ>), dim3(p.g.total_wg), dim3(CfgDQ::NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
-int attn_bwd_bf16_block_m() { return BLOCK_M; }
+int attn_bwd_bf16_block_m(bool kv) { return kv ? CfgKV::BLOCK_M : CfgDQ::BLOCK_M; }
 
 }  // namespace vdsa

@@ -212,7 +212,7 @@ hipError_t launch_upsample(const UpsampleParams& p, int bf16, hipStream_t stream
 // on the vector ALU; grad_f32 applies to the fp32 kernel trivially
 hipError_t launch_attn_bwd_dq(const BoxBwdParams& p, int bf16, hipStream_t stream);
 hipError_t launch_attn_bwd_dkdv(const BoxBwdParams& p, int bf16, hipStream_t stream);
-int attn_bwd_block_m(int bf16);   // own rows per workgroup
+int attn_bwd_block_m(int bf16, bool kv);   // own rows per workgroup of the dQ or the dK/dV pass
 hipError_t launch_rowdot(const RowDotParams& p, int bf16, hipStream_t stream);
 hipError_t launch_unpool_grad(const UnpoolParams& p, int bf16, hipStream_t stream);
 
