@@ -52,6 +52,7 @@ constexpr int HD = 128;
 constexpr int KS = HD / 32;            // 32-wide head_dim steps
 constexpr int ND = HD / 16;            // 16-row head_dim tiles
 constexpr int WAIT_VMCNT0 = 0x0F70;    // s_waitcnt vmcnt(0), other counters untouched
+constexpr int RA = 3;                  // operand fragments read ahead of their products
 
 // Shape of one pass: OT own 16-token tiles per wave, NW waves, NCH 32-token
 // chunks per block of the iterated box.
@@ -255,26 +256,43 @@ __global__ __launch_bounds__(C::NW * 64) void box_attn_bwd_bf16_kernel(const Box
 
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      // S and dP, register v of tile (t, ot) = iterated row 32c + 8G + 4t + v
+      // S and dP, register v of tile (t, ot) = iterated row 32c + 8G + 4t + v.
+      // Operand fragments of the chunk in the order of their products: steps
+      // 0..7 the (X, Y) pairs of S and dP in (ks, t) order, steps 8..15 the
+      // X^T (and Y^T) tiles dt; each read RA steps ahead of its products.
+      bf16x8 fx[16], fy[16];
+      auto rd = [&](int i) __attribute__((always_inline)) {
+        if (i < 8) {
+          const int f = (c * 2 + (i & 1)) * KS + (i >> 1);
+          fx[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + Lay::XF + f * 1024 + lane * 16));
+          fy[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + Lay::YF + f * 1024 + lane * 16));
+        } else {
+          const int dt = i - 8;
+          fx[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + Lay::XT + t_rd[c] + dt * 1024));
+          if constexpr (KV) fy[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + Lay::YT + t_rd[c] + dt * 1024));
+        }
+      };
       f32x4 s[2][OT], dp[2][OT];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int ot = 0; ot < OT; ++ot) {
           s[t][ot] = f32x4{};
           dp[t][ot] = f32x4{};
         }
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int f = (c * 2 + t) * KS + ks;
-          const bf16x8 xa = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + Lay::XF + f * 1024 + lane * 16));
-          const bf16x8 ya = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + Lay::YF + f * 1024 + lane * 16));
+      for (int i = 0; i < RA; ++i) rd(i);
 #pragma unroll
-          for (int ot = 0; ot < OT; ++ot) {
-            s[t][ot] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, af[ot][ks], s[t][ot], 0, 0, 0);
-            dp[t][ot] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ya, bf[ot][ks], dp[t][ot], 0, 0, 0);
-          }
+      for (int i = 0; i < 8; ++i) {
+        rd(i + RA);
+        __builtin_amdgcn_sched_barrier(0);
+        const int ks = i >> 1, t = i & 1;
+#pragma unroll
+        for (int ot = 0; ot < OT; ++ot) {
+          s[t][ot] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fx[i], af[ot][ks], s[t][ot], 0, 0, 0);
+          dp[t][ot] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fy[i], bf[ot][ks], dp[t][ot], 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
       float l2[OT][8], dl[OT][8];
       if constexpr (KV) {
@@ -315,17 +333,19 @@ __global__ __launch_bounds__(C::NW * 64) void box_attn_bwd_bf16_kernel(const Box
         }
       // acc1 += X^T dS (dQ^T or dK^T); dK/dV pass: acc2 += Y^T P (dV^T)
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt) {
-        const bf16x8 xt = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + Lay::XT + t_rd[c] + dt * 1024));
+      for (int i = 8; i < 16; ++i) {
+        if (i + RA < 16) rd(i + RA);
+        __builtin_amdgcn_sched_barrier(0);
+        const int dt = i - 8;
 #pragma unroll
         for (int ot = 0; ot < OT; ++ot)
-          acc1[dt][ot] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xt, dsb[ot], acc1[dt][ot], 0, 0, 0);
+          acc1[dt][ot] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fx[i], dsb[ot], acc1[dt][ot], 0, 0, 0);
         if constexpr (KV) {
-          const bf16x8 yt = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + Lay::YT + t_rd[c] + dt * 1024));
 #pragma unroll
           for (int ot = 0; ot < OT; ++ot)
-            acc2[dt][ot] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yt, pb[ot], acc2[dt][ot], 0, 0, 0);
+            acc2[dt][ot] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fy[i], pb[ot], acc2[dt][ot], 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
