@@ -104,6 +104,8 @@ def main():
     ap.add_argument("--dense-steps", type=int, default=3, help="full-window comparison calls (0 = skip)")
     ap.add_argument("--bwd-steps", type=int, default=3,
                     help="backward-pass calls of the local branch to time (0 = skip)")
+    ap.add_argument("--variant-steps", type=int, default=10,
+                    help="calls per timed global-branch form and UltraGen variant (pooled workloads; 0 = skip)")
     ap.add_argument("--mode-steps", type=int, default=3,
                     help="calls per window mode (inward, cyclic) of the local branch to time (0 = skip)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -193,13 +195,13 @@ def main():
         return a.elapsed_time(z) / n
 
     extra = {}
-    if w.pool_hw is not None and args.steps > 0:
+    if w.pool_hw is not None and args.variant_steps > 0:
         # global branch: fused global + merge call against the two separate
         # calls, and the standalone exact (LSE) merge, each timed with events
         lse_l = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
         V.sta_attn_fwd(q, k, v, w.grid, w.tile, w.window, w.shifts[0], scale=w.softmax_scale,
                        out=buf.local[0], lse=lse_l)
-        n = max(1, min(args.steps, 10))
+        n = args.variant_steps
         fused_ms = timed(lambda: P.run_global(w, q, k, v, gate, buf, fused=True), n)
         unfused_ms = timed(lambda: P.run_global(w, q, k, v, gate, buf, fused=False), n)
         lse_g = torch.empty_like(lse_l)
