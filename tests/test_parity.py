@@ -85,6 +85,36 @@ def test_sta_small_all_rows(case):
     compare(lse[0].cpu(), rl, dt, name + " lse")
 
 
+OUTLIER_STA = [
+    # name, grid, tile, window, shift, dtype: each attention kernel in turn
+    ("tile384_bf16", (12, 16, 24), (6, 8, 8), (1, 3, 3), (0, 0, 0), "bf16"),
+    ("tile192_bf16", (6, 16, 24), (3, 8, 8), (3, 1, 3), (1, 4, 4), "bf16"),
+    ("tile32_bf16", (8, 16, 16), (2, 4, 4), (3, 3, 3), (0, 0, 0), "bf16"),
+    ("tile32_f32", (6, 12, 12), (2, 4, 4), (3, 1, 3), (1, 2, 0), "f32"),
+]
+
+
+@pytest.mark.parametrize("case", OUTLIER_STA, ids=[c[0] for c in OUTLIER_STA])
+def test_sta_outlier_keys(case):
+    """Large logits: 5% of the key rows scaled by 8 (exact in bf16), the
+    structure of the 2K workload's inputs.  A kernel that rounds anything
+    proportional to the logit (a pre-scaled bf16 Q, say) fails here first."""
+    name, grid, tile, window, shift, dt = case
+    say(f"[sta outliers] {name}")
+    N = int(np.prod(grid))
+    heads, D = 2, 128
+    q, k, v = qkv((1, heads, N, D), TDT[dt], seed=950)
+    gen = torch.Generator(device="cpu").manual_seed(951)
+    for h in range(heads):
+        rows = torch.randperm(N, generator=gen)[: N // 20].to(DEV)
+        k[0, h, rows] *= 8
+    o, lse = V.sta_attn_fwd(q, k, v, grid, tile, window, shift, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle_sta(q, k, v, grid, tile, window, shift, D ** -0.5)
+    compare(o[0].cpu(), ro, dt, name)
+    compare(lse[0].cpu(), rl, dt, name + " lse")
+
+
 def test_sta_bnhd_equals_bhnd():
     grid, tile, window, shift = (7, 13, 21), (3, 4, 8), (3, 3, 1), (1, 2, 4)
     N = int(np.prod(grid))

@@ -47,10 +47,7 @@
 // reference m that is raised only when some score of the wave exceeds it by
 // more than RESCALE_MARGIN (log2 units), so probabilities stay below
 // 2^RESCALE_MARGIN and the final normalisation by the same reference is
-// exact.  The resident Q is multiplied by scale*log2(e) once (rounded to
-// bf16) and every S accumulator starts at -m, so the matrix core delivers
-// s*scale*log2(e) - m and the softmax phase applies exp2 alone; the first
-// chunk sets m to its own maximum.  Each lane tests its own eight scores of a query (a chunk maximum
+// exact.  Each lane tests its own eight scores of a query (a chunk maximum
 // exceeds the threshold exactly when one of its lanes' maxima does); the
 // cross-lane maximum is formed only when some lane fires.  The row sums of P
 // (the softmax denominators) come from the matrix core: an all-ones A operand
@@ -186,12 +183,7 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
     qtok[qt] = q_token(p, qb.t0 + jt, qb.h0 + jh, qb.w0 + jw);
     const char* src = qp + qtok[qt] * q_row + 16 * G;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bf16x8 x = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + 64 * ks));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = (__bf16)((float)x[e] * p.scale_log2e);
-      qf[qt][ks] = x;
-    }
+    for (int ks = 0; ks < KS; ++ks) qf[qt][ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + 64 * ks));
   }
 
   // ---- key box addressing: key j -> token, via two divisions by invariants
@@ -260,17 +252,20 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
 
   f32x4 oacc[ND][QT];
   f32x4 lacc[QT];    // row sums of P, the same value in all four registers
-  float m_run[QT];   // per-query reference maximum (log2 units; the S accumulators start at -m_run)
+  float m_run[QT];   // per-query reference maximum (log2 units)
+  float m_thr[QT];   // m_run + RESCALE_MARGIN
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) oacc[dt][qt] = f32x4{};
     lacc[qt] = f32x4{};
-    m_run[qt] = 0.f;
+    m_run[qt] = -INFINITY;
+    m_thr[qt] = -INFINITY;
   }
   bf16x8 ones8;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones8[e] = (__bf16)1.f;
+  const float cl2 = p.scale_log2e;
 
   // ---- M phase: the 8 V^T fragments of chunk cv of st_v (P*V, fragments
   // 0..7, the first PF read by prefetch_pv in the preceding V phase), then the
@@ -299,7 +294,7 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) s[t][qt] = f32x4{-m_run[qt], -m_run[qt], -m_run[qt], -m_run[qt]};
+        for (int qt = 0; qt < QT; ++qt) s[t][qt] = f32x4{};
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -336,7 +331,7 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
 
   // ---- V phase: online softmax of one chunk; nvalid = keys of the block
   // from this chunk on (masking only in the last, partial block).
-  auto softmax = [&](int nvalid, auto partial_tag, bool first) {
+  auto softmax = [&](int nvalid, auto partial_tag) {
     constexpr bool PARTIAL = decltype(partial_tag)::value;
     float lmax[QT];
     bool grow = false;
@@ -348,29 +343,25 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
       m = fmaxf(fmaxf(m, s[1][qt][1]), s[1][qt][2]);
       m = fmaxf(m, s[1][qt][3]);
       lmax[qt] = m;
-      grow = grow || (m > RESCALE_MARGIN);
+      grow = grow || (m * cl2 > m_thr[qt]);
     }
-    if (first || __builtin_amdgcn_ballot_w64(grow)) {
+    if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        const float rmax = xrow4_max(lmax[qt]);
-        const float d = first ? rmax : fmaxf(rmax, 0.f);
-        if (!first) {
-          const float corr = __builtin_amdgcn_exp2f(-d);
-          lacc[qt] *= corr;
+        const float m_new = fmaxf(m_run[qt], xrow4_max(lmax[qt]) * cl2);
+        const float corr = __builtin_amdgcn_exp2f(m_run[qt] - m_new);
+        lacc[qt] *= corr;
 #pragma unroll
-          for (int dt = 0; dt < ND; ++dt) oacc[dt][qt] *= corr;
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t) s[t][qt] -= d;
-        m_run[qt] += d;
+        for (int dt = 0; dt < ND; ++dt) oacc[dt][qt] *= corr;
+        m_run[qt] = m_new;
+        m_thr[qt] = m_new + RESCALE_MARGIN;
       }
     }
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float pv = __builtin_amdgcn_exp2f(s[e >> 2][qt][e & 3]);
+        float pv = __builtin_amdgcn_exp2f(fmaf(s[e >> 2][qt][e & 3], cl2, -m_run[qt]));
         if constexpr (PARTIAL) {
           if (8 * G + e >= nvalid) pv = 0.f;
         }
@@ -403,7 +394,7 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
     phase_barrier();
     // V(blk, 0)
     prefetch_pv(st, 0);
-    softmax(nvalid, partial_tag, blk == 0);
+    softmax(nvalid, partial_tag);
     if (blk + 1 < nkb) store_v(blk + 1);
     phase_barrier();
     // M(blk, 1)
@@ -415,7 +406,7 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
     // V(blk, 1)
     if (more2) load_block(blk + 2);
     prefetch_pv(st, 1);
-    softmax(nvalid - 32, partial_tag, false);
+    softmax(nvalid - 32, partial_tag);
     if (!grp_b) vm_wait(more2);
     phase_barrier();
   };
