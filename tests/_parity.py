@@ -78,3 +78,51 @@ def rel_compare(got, ref, dt, what):
           file=sys.stderr, flush=True)
     assert worst <= tmax and mean <= tmean, \
         f"{what}: max err {worst:.3e} x (rms + |ref|) (<= {tmax}), mean {mean:.3e} rms (<= {tmean})"
+
+
+def bwd_rounding_bound(q, k, v, do, grid, tile, window, shift, scale, window_mode="clip"):
+    """Element-wise bound on the gradient error that the bf16 backward's own
+    roundings can cause, from fp64 quantities of one head (forward error
+    analysis, |fl(ab) - ab| <= u |a||b| with bf16 unit roundoff u = 2^-8).
+    The kernels round dS = P (dP - delta) and P to bf16 and take delta from
+    the bf16 forward output O, so per query tile, with E = u (|dS| +
+    P rowsum(|dO| |O|)):
+        |err dQ| <= scale E |K|,   |err dK| <= scale E^T |Q|,
+        |err dV| <= u P^T |dO|.
+    Returns the three bounds, each [N, D]."""
+    u = 2.0 ** -8
+    q, k, v, do = (np.asarray(R.to_f64(x)) for x in (q, k, v, do))
+    ti = R.mode_tile_index(grid, tile, shift, window_mode)
+    counts = R.mode_tile_counts(grid, tile, shift, window_mode)
+    radius = R.window_radius(window)
+    bq, bk, bv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for a in np.unique(ti, axis=0):
+        qi = np.nonzero(np.all(ti == a, axis=1))[0]
+        ki = np.nonzero(R.mode_mask_row(ti, a, radius, counts, window_mode))[0]
+        s = scale * q[qi] @ k[ki].T
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        o = p @ v[ki]
+        delta = (do[qi] * o).sum(axis=1, keepdims=True)
+        ds = p * (do[qi] @ v[ki].T - delta)
+        e = u * (np.abs(ds) + p * (np.abs(do[qi]) * np.abs(o)).sum(axis=1, keepdims=True))
+        bq[qi] += scale * e @ np.abs(k[ki])
+        bk[ki] += scale * e.T @ np.abs(q[qi])
+        bv[ki] += u * p.T @ np.abs(do[qi])
+    return bq, bk, bv
+
+
+def bound_compare(got, ref, bound, what, slack=2.0, mean_tol=5e-3):
+    """|got - ref| <= slack * bound element by element (slack for the fp32
+    accumulation and the forward's LSE), and mean |err| <= mean_tol * RMS."""
+    g = R.to_f64(got)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    assert np.isfinite(g).all(), f"{what}: non-finite values"
+    err = np.abs(g - r)
+    rms = float(np.sqrt(np.mean(r * r)))
+    ratio = float((err / (slack * bound + 1e-6 * rms)).max())
+    mean = float(err.mean()) / rms
+    print(f"  {what}: max err / ({slack} x bound) {ratio:.3f}, mean {mean:.2e} rms", file=sys.stderr, flush=True)
+    assert ratio <= 1.0 and mean <= mean_tol, \
+        f"{what}: max err {ratio:.3f} x ({slack} x rounding bound) (<= 1), mean {mean:.3e} rms (<= {mean_tol})"
