@@ -104,6 +104,38 @@ def test_sta_bwd_outlier_keys():
             bound_compare(got[0, h].cpu(), r, bd, f"outlier {nm} h{h}")
 
 
+def _bnhd(x):
+    """The same values as a [B, heads, N, D] view of a [B, N, heads, D] buffer."""
+    return x.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_bwd_bnhd_equals_bhnd(dt):
+    """Strided (token-major) inputs and gradient outputs give the same
+    gradients bit for bit, for the sliding-tile and the global backward."""
+    grid, tile, window, shift, pool = (3, 12, 16), (3, 4, 8), (1, 3, 1), (1, 2, 4), (2, 4)
+    N, D, heads = int(np.prod(grid)), 128, 3
+    say(f"[bwd bnhd] {dt}")
+    q, k, v, do = tensors((1, heads, N, D), TDT[dt], seed=870)
+    qs, ks, vs, dos = (_bnhd(x) for x in (q, k, v, do))
+    assert qs.stride(2) == heads * D
+    o, lse = V.sta_attn_fwd(q, k, v, grid, tile, window, shift, return_lse=True)
+    os_ = _bnhd(o)
+    g1 = V.sta_attn_bwd(q, k, v, o, do, lse, grid, tile, window, shift)
+    g2 = V.sta_attn_bwd(qs, ks, vs, os_, dos, lse, grid, tile, window, shift,
+                        dq=_bnhd(torch.empty_like(q)), dk=_bnhd(torch.empty_like(q)), dv=_bnhd(torch.empty_like(q)))
+    og, lg = V.global_pooled_attn_fwd(q, k, v, grid, pool, return_lse=True)
+    h1 = V.global_pooled_attn_bwd(q, k, v, og, do, lg, grid, pool)
+    h2 = V.global_pooled_attn_bwd(qs, ks, vs, _bnhd(og), dos, lg, grid, pool,
+                                  dq=_bnhd(torch.empty_like(q)), dk=_bnhd(torch.empty_like(q)), dv=_bnhd(torch.empty_like(q)))
+    torch.cuda.synchronize()
+    for nm, a, b in zip(("dq", "dk", "dv"), g1, g2):
+        assert b.stride(2) == heads * D
+        assert torch.equal(a, b), f"sta {nm}"
+    for nm, a, b in zip(("dq", "dk", "dv"), h1, h2):
+        assert torch.equal(a, b), f"global {nm}"
+
+
 GLOBAL_BWD = [
     # name, batch, grid, pool, heads, head_dim, dtype
     ("pool2x4_bf16", 1, (3, 8, 12), (2, 4), 2, 128, "bf16"),
