@@ -104,6 +104,23 @@ def test_sta_bwd_outlier_keys():
             bound_compare(got[0, h].cpu(), r, bd, f"outlier {nm} h{h}")
 
 
+def test_sta_bwd_720p_full_head():
+    """The 720P workload's shape (30x48x80 grid, 6x8x8 tiles, 3x3x5 window) in
+    the launch configuration the bench times, one head, every gradient
+    element against the oracle (about half a minute of CPU)."""
+    w = WL.WORKLOADS["sta_720p"]
+    say("[sta bwd] 720P, one head, all elements")
+    shape = (1, 1, w.n_tokens, w.head_dim)
+    q, k, v, do = tensors(shape, torch.bfloat16, seed=880)
+    o, lse = V.sta_attn_fwd(q, k, v, w.grid, w.tile, w.window, return_lse=True)
+    dq, dk, dv = V.sta_attn_bwd(q, k, v, o, do, lse, w.grid, w.tile, w.window)
+    torch.cuda.synchronize()
+    ref = R.sta_bwd_ref(head_f64(q, 0, 0), head_f64(k, 0, 0), head_f64(v, 0, 0), head_f64(do, 0, 0),
+                        w.grid, w.tile, w.window, scale=w.softmax_scale)
+    for nm, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        rel_compare(got[0, 0].cpu(), r, "bf16", f"720p {nm}")
+
+
 def _bnhd(x):
     """The same values as a [B, heads, N, D] view of a [B, N, heads, D] buffer."""
     return x.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
