@@ -121,6 +121,22 @@ def test_sta_bwd_720p_full_head():
         rel_compare(got[0, 0].cpu(), r, "bf16", f"720p {nm}")
 
 
+def test_global_bwd_1080p_full_head():
+    """The 1080P workload's global branch (171,360 queries against 4x4-pooled
+    K/V, M = 10,710), one head, every gradient element against the oracle."""
+    w = WL.WORKLOADS["dual_1080p"]
+    say("[global bwd] 1080P, one head, all elements")
+    shape = (1, 1, w.n_tokens, w.head_dim)
+    q, k, v, do = tensors(shape, torch.bfloat16, seed=890)
+    o, lse = V.global_pooled_attn_fwd(q, k, v, w.grid, w.pool_hw, return_lse=True)
+    dq, dk, dv = V.global_pooled_attn_bwd(q, k, v, o, do, lse, w.grid, w.pool_hw)
+    torch.cuda.synchronize()
+    ref = R.global_bwd_ref(head_f64(q, 0, 0), head_f64(k, 0, 0), head_f64(v, 0, 0), head_f64(do, 0, 0),
+                           w.grid, w.pool_hw, scale=w.softmax_scale)
+    for nm, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        rel_compare(got[0, 0].cpu(), r, "bf16", f"1080p global {nm}")
+
+
 def _bnhd(x):
     """The same values as a [B, heads, N, D] view of a [B, N, heads, D] buffer."""
     return x.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
