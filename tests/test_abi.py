@@ -318,3 +318,32 @@ def test_compressed_global_flop_counter():
     M = T * 17 * 30
     assert L.compressed_global_flops(1, 24, 128, (T, H, W), (4, 4)) == 4.0 * 128 * 24 * M * M
 
+
+def test_last_error_is_per_thread():
+    """vdsa_last_error is thread-local: threads failing with different
+    errors each read back their own detail, and a successful host-only call
+    clears only its own thread's message."""
+    import threading
+    results = {}
+    barrier = threading.Barrier(4)
+
+    def worker(i):
+        lib = L.lib()
+        bad = cfg(window=(2 * i + 2, 3, 3))          # even window: VDSA_ERR_WINDOW
+        barrier.wait()
+        st = sta(prob(), bad)
+        barrier.wait()                              # every thread has failed before anyone reads
+        msg = lib.vdsa_last_error().decode()
+        ok = L.sta_flops(1, 2, 128, (4, 8, 8), (2, 4, 4), (3, 3, 3))
+        results[i] = (st, msg, lib.vdsa_last_error().decode(), ok)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    for i in range(4):
+        st, msg, after, ok = results[i]
+        assert st == L.STATUS["VDSA_ERR_WINDOW"]
+        assert f"= {2 * i + 2}" in msg, msg
+        assert after == "" and ok > 0
