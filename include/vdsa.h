@@ -52,7 +52,7 @@ typedef enum {
   VDSA_ERR_SHAPE = 2,       /* a dimension <= 0, or an offset beyond the size limit */
   VDSA_ERR_WINDOW = 3,      /* tile < 1, window even or < 1, shift outside [0, tile), pool < 1,
                                unknown window_mode */
-  VDSA_ERR_UNSUPPORTED = 4, /* head_dim not in {64, 128}, unknown dtype, non-finite scale */
+  VDSA_ERR_UNSUPPORTED = 4, /* head_dim not in {64, 128}, unknown dtype, scale not finite or < 0 */
   VDSA_ERR_ALIGN = 5,       /* pointer or stride breaks the 16-byte rule */
   VDSA_ERR_ALIAS = 6,       /* an output overlaps an input it must not overlap */
   VDSA_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than the reported size */
@@ -70,7 +70,7 @@ typedef struct {
   int32_t batch, heads, head_dim;   /* head_dim in {64, 128} */
   int32_t grid_t, grid_h, grid_w;   /* N = grid_t * grid_h * grid_w */
   vdsa_dtype dtype;
-  float scale;                      /* logits = scale * (q . k) */
+  float scale;                      /* logits = scale * (q . k); finite, >= 0 */
 } vdsa_problem;
 
 /*
@@ -86,7 +86,8 @@ typedef struct {
  *             floor((x + shift) / tile), a non-cyclic offset of the tile
  *             lattice that makes edge tiles partial (the shifted partition of
  *             UltraGen section 4.3, "Cross-window Hierarchical Local
- *             Attention").  Partial tiles hold only real tokens.
+ *             Attention").  Partial tiles hold only real tokens.  Under
+ *             VDSA_WINDOW_CYCLIC the shift is a cyclic roll instead (below).
  *   window_mode (vdsa_window_mode) how windows meet the grid edge; 0 (the
  *             value of a zero-initialised struct) is VDSA_WINDOW_CLIP.
  */
