@@ -115,6 +115,22 @@ def test_sta_outlier_keys(case):
     compare(lse[0].cpu(), rl, dt, name + " lse")
 
 
+@pytest.mark.parametrize("case", OUTLIER_STA, ids=[c[0] for c in OUTLIER_STA])
+def test_sta_scale_zero(case):
+    """Degenerate softmax: scale 0 gives every key of the window the same
+    weight, so each row is the mean of V over its key box and LSE is the log
+    of the box's key count."""
+    name, grid, tile, window, shift, dt = case
+    say(f"[sta scale 0] {name}")
+    N = int(np.prod(grid))
+    q, k, v = qkv((1, 2, N, 128), TDT[dt], seed=960)
+    o, lse = V.sta_attn_fwd(q, k, v, grid, tile, window, shift, scale=0.0, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle_sta(q, k, v, grid, tile, window, shift, 0.0)
+    compare(o[0].cpu(), ro, dt, name)
+    compare(lse[0].cpu(), rl, dt, name + " lse")
+
+
 def test_sta_bnhd_equals_bhnd():
     grid, tile, window, shift = (7, 13, 21), (3, 4, 8), (3, 3, 1), (1, 2, 4)
     N = int(np.prod(grid))

@@ -253,7 +253,7 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
   f32x4 oacc[ND][QT];
   f32x4 lacc[QT];    // row sums of P, the same value in all four registers
   float m_run[QT];   // per-query reference maximum (log2 units)
-  float m_thr[QT];   // m_run + RESCALE_MARGIN
+  float m_thr[QT];   // (m_run + RESCALE_MARGIN) / (scale*log2(e)): the test runs on raw scores
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
@@ -266,6 +266,7 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones8[e] = (__bf16)1.f;
   const float cl2 = p.scale_log2e;
+  const float inv_cl2 = 1.f / cl2;   // +inf for scale 0: no growth test fires after the first chunk
 
   // ---- M phase: the 8 V^T fragments of chunk cv of st_v (P*V, fragments
   // 0..7, the first PF read by prefetch_pv in the preceding V phase), then the
@@ -343,7 +344,7 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
       m = fmaxf(fmaxf(m, s[1][qt][1]), s[1][qt][2]);
       m = fmaxf(m, s[1][qt][3]);
       lmax[qt] = m;
-      grow = grow || (m * cl2 > m_thr[qt]);
+      grow = grow || (m > m_thr[qt]);
     }
     if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
@@ -354,7 +355,7 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) oacc[dt][qt] *= corr;
         m_run[qt] = m_new;
-        m_thr[qt] = m_new + RESCALE_MARGIN;
+        m_thr[qt] = (m_new + RESCALE_MARGIN) * inv_cl2;
       }
     }
 #pragma unroll
