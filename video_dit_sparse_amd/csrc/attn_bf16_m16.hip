@@ -21,8 +21,9 @@
 //   softmax       fp32, v_exp_f32 with scale*log2(e) folded into one FMA,
 //                 against a lazy per-query reference raised only when some
 //                 score of the wave exceeds it by more than RESCALE_MARGIN;
-//                 each lane tests its own eight scores, and the cross-lane
-//                 maximum (two exchanges) is formed only when one fires.
+//                 each lane tests its own eight raw scores against that
+//                 threshold in raw-score units, and the cross-lane maximum
+//                 (two exchanges) is formed only when one fires.
 //   O^T += V^T P^T with P^T straight from the S^T accumulators (those eight
 //                 consecutive keys are one MFMA k-slice) and V^T from LDS;
 //                 an all-ones A operand times the same P^T gives the row sums
@@ -205,16 +206,19 @@ __global__ __launch_bounds__(NW * 64, 2) void box_attn_bf16_m16_kernel(const Box
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = f32x4{};
   float m_run[QT];
+  float m_thr[QT];   // (m_run + RESCALE_MARGIN) / (scale*log2(e)), in raw-score units
   f32x4 lacc[QT];   // row sums of P (all-ones A operand times P^T)
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     m_run[qt] = -INFINITY;
+    m_thr[qt] = -INFINITY;
     lacc[qt] = f32x4{};
   }
   bf16x8 ones8;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones8[e] = (__bf16)1.f;
   const float cl2 = p.scale_log2e;
+  const float inv_cl2 = 1.f / cl2;
 
   load_block(0, 0);
   store_v(0);
@@ -268,7 +272,7 @@ __global__ __launch_bounds__(NW * 64, 2) void box_attn_bf16_m16_kernel(const Box
         m = fmaxf(fmaxf(m, s[1][qt][1]), s[1][qt][2]);
         m = fmaxf(m, s[1][qt][3]);
         lmax[qt] = m;
-        grow = grow || (m * cl2 > m_run[qt] + RESCALE_MARGIN);
+        grow = grow || (m > m_thr[qt]);
       }
       if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
@@ -279,6 +283,7 @@ __global__ __launch_bounds__(NW * 64, 2) void box_attn_bf16_m16_kernel(const Box
 #pragma unroll
           for (int dt = 0; dt < ND; ++dt) oacc[dt][qt] *= corr;
           m_run[qt] = m_new;
+          m_thr[qt] = (m_new + RESCALE_MARGIN) * inv_cl2;
         }
       }
       bf16x8 pf[QT];
