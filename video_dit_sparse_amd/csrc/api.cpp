@@ -174,7 +174,9 @@ struct Bf16Shape {
 };
 
 // Largest block whose padding wastes at most 1/8 of the launched query slots,
-// else the least padding.
+// else the least padding.  The 384- and 192-query kernels (head_dim 128 only)
+// map keys to tokens with 24-bit multiplies; the offset check makes that exact,
+// since ((N-1)*stride_n + 128) * 2 < 2^32 with stride_n >= 128 gives N < 2^24.
 Bf16Shape choose_bf16_shape(int64_t max_tile_vol, int head_dim) {
   const Bf16Shape m32{vdsa::box_attn_bf16_block_m(), K_M32};
   if (head_dim != 128) return m32;

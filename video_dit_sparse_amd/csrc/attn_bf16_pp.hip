@@ -191,11 +191,7 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
   const FastDiv fd_row = make_fastdiv((uint32_t)kb.ew);
   auto key_token = [&](int j) -> uint32_t {
     j = min(j, kvol - 1);   // keys past the box repeat the last key; masked later
-    const uint32_t jt = fast_div((uint32_t)j, fd_plane);
-    const uint32_t r = (uint32_t)j - jt * fd_plane.d;
-    const uint32_t jh = fast_div(r, fd_row);
-    const uint32_t jw = r - jh * fd_row.d;
-    return k_token(p, kb.t0 + (int)jt, kb.h0 + (int)jh, kb.w0 + (int)jw);
+    return box_key_token24(p, kb, (uint32_t)j, fd_plane, fd_row);
   };
   auto stage_of = [&](int blk) -> char* { return lds + (blk % NSTAGE) * STAGE; };
 

@@ -94,6 +94,22 @@ __device__ __forceinline__ uint32_t k_token(const BoxAttnParams& p, int t, int h
   return (uint32_t)((unroll(t, p.rlT, p.kT) * p.kH + unroll(h, p.rlH, p.kH)) * p.kW + unroll(w, p.rlW, p.kW));
 }
 
+// Key j of a key box (extent ew along w, plane = eh * ew tokens) -> token, in
+// full-rate 24-bit multiplies.  Valid when the key grid has fewer than 2^24
+// tokens, which the 32-bit byte-offset bound guarantees for head_dim 128 in
+// bf16 (a key row is at least 256 bytes).
+__device__ __forceinline__ uint32_t box_key_token24(const BoxAttnParams& p, const Box& kb, uint32_t j,
+                                                    const FastDiv& fd_plane, const FastDiv& fd_row) {
+  const uint32_t jt = fast_div(j, fd_plane);
+  const uint32_t r = j - __umul24(jt, fd_plane.d);
+  const uint32_t jh = fast_div(r, fd_row);
+  const uint32_t jw = r - __umul24(jh, fd_row.d);
+  const uint32_t t = (uint32_t)unroll(kb.t0 + (int)jt, p.rlT, p.kT);
+  const uint32_t h = (uint32_t)unroll(kb.h0 + (int)jh, p.rlH, p.kH);
+  const uint32_t w = (uint32_t)unroll(kb.w0 + (int)jw, p.rlW, p.kW);
+  return __umul24(__umul24(t, (uint32_t)p.kH) + h, (uint32_t)p.kW) + w;
+}
+
 __device__ __forceinline__ void tile_boxes(const BoxAttnParams& p, int tile, Box& qb, Box& kb) {
   const int aw = tile % p.nW;
   const int ah = (tile / p.nW) % p.nH;
