@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 METRIC = "effective attention TFLOP/s + ms/call (720P-shape STA, bf16); % MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0
+NOMINAL_CLOCK_MHZ = 2400.0   # the clock the published bf16 peak assumes
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "sta_bf16_720p_counters.md")
 # 384-token (6x8x8) tiles at head_dim 128 run the 8-wave kernel of attn_bf16_pp.hip
 ROOFLINE_KERNEL = "box_attn_bf16_pp_kernel"
@@ -55,6 +56,23 @@ def measured_traffic():
     if not (m_hash and m_bytes) or m_hash.group(1) != kernel_source_hash():
         return None
     return float(m_bytes.group(1))
+
+
+def parse_gfx_clocks(text: str):
+    """Current clock (MHz) of every GFX_<i> block in `amd-smi metric -c` text."""
+    return [int(x) for x in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", text)]
+
+
+def gfx_clock_mhz():
+    """Mean current GFX clock over the XCDs, read with amd-smi (None if that
+    tool is unavailable or its output has no GFX clocks)."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-c"], capture_output=True, text=True, timeout=30)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    mhz = parse_gfx_clocks(r.stdout)
+    return sum(mhz) / len(mhz) if mhz else None
 
 
 def cpu_baseline(w, q, k, v, budget_s: float):
@@ -110,6 +128,8 @@ def main():
                     help="calls per window mode (inward, cyclic) of the local branch to time (0 = skip)")
     ap.add_argument("--hbm-steps", type=int, default=10,
                     help="calls per HBM-bound kernel (pooling, gated merge, LSE merge) to time (0 = skip)")
+    ap.add_argument("--clock-seconds", type=float, default=2.0,
+                    help="run the dominant kernel back to back this long while reading the GFX clock (0 = skip)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc runs)")
     args = ap.parse_args()
@@ -183,6 +203,30 @@ def main():
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "kernel": ROOFLINE_KERNEL, "launch_ms": round(launch_ms, 4),
                 "flop_per_launch": launch_flops}
+
+    clock = None
+    if args.clock_seconds > 0:
+        # the sustained GFX clock under this kernel, read while it runs back to
+        # back; the bf16 peak scales with the clock (2.5 PFLOP/s at 2.4 GHz)
+        import threading
+        reads = []
+        th = threading.Thread(target=lambda: [time.sleep(args.clock_seconds / 3), reads.append(gfx_clock_mhz()),
+                                              time.sleep(args.clock_seconds / 3), reads.append(gfx_clock_mhz())])
+        th.start()
+        t_end = time.perf_counter() + args.clock_seconds
+        while th.is_alive() or time.perf_counter() < t_end:
+            for i, s in enumerate(w.shifts):
+                V.sta_attn_fwd(q, k, v, w.grid, w.tile, w.window, s, scale=w.softmax_scale, out=buf.local[i])
+            torch.cuda.synchronize()
+        th.join()
+        reads = [r for r in reads if r is not None]
+        if reads:
+            mhz = sum(reads) / len(reads)
+            peak_at = PEAK_BF16_TFLOPS * mhz / NOMINAL_CLOCK_MHZ
+            clock = {"source": "amd-smi metric -c (mean over XCDs)", "gfx_mhz": round(mhz, 1), "samples": len(reads),
+                     "bf16_peak_at_clock": round(peak_at, 1), "frac_at_clock": round(achieved / peak_at, 4)}
+            log(f"[bench] GFX clock under the kernel: {mhz:.0f} MHz; {achieved:.0f} TFLOP/s is "
+                f"{100 * achieved / peak_at:.1f}% of the bf16 peak at that clock")
 
     def timed(fn, n):
         """Average ms of fn over n calls after one untimed call, with events
@@ -349,6 +393,7 @@ def main():
                    "effective_flop_per_step": step_flops},
         "pct_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline,
+        "clock": clock,
         "cpu_baseline": cpu,
         **extra,
         "device": torch.cuda.get_device_name(0),
