@@ -382,12 +382,10 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
     const int nvalid = kvol - blk * BLOCK_N;
     const bool more2 = blk + 2 < nkb;
     // M(blk, 0)
-    __builtin_amdgcn_s_setprio(1);
     if (blk > 0)
       mphase(true, stage_of(blk - 1), 1, true, st, 0);
     else
       mphase(false, st, 0, true, st, 0);
-    __builtin_amdgcn_s_setprio(0);
     phase_barrier();
     // V(blk, 0)
     prefetch_pv(st, 0);
@@ -395,9 +393,7 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
     if (blk + 1 < nkb) store_v(blk + 1);
     phase_barrier();
     // M(blk, 1)
-    __builtin_amdgcn_s_setprio(1);
     mphase(true, st, 0, true, st, 1);
-    __builtin_amdgcn_s_setprio(0);
     if (grp_b) vm_wait(false);   // K of block blk+1 has landed
     phase_barrier();
     // V(blk, 1)
@@ -411,9 +407,7 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
   const int nfull = last_partial ? nkb - 1 : nkb;
   for (int blk = 0; blk < nfull; ++blk) do_block(blk, std::false_type{});
   if (last_partial) do_block(nkb - 1, std::true_type{});
-  __builtin_amdgcn_s_setprio(1);
   mphase(true, stage_of(nkb - 1), 1, false, stage_of(nkb - 1), 0);
-  __builtin_amdgcn_s_setprio(0);
   if (!grp_b) phase_barrier();
 
   // ---- epilogue: O^T register v of tile (dt, qt) is head_dim 16dt + 4G + v;
