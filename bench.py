@@ -196,13 +196,26 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     launch_ms = e0.elapsed_time(e1) / (args.steps * n_local)
+    # the same calls one by one, each between its own pair of events: median
+    # and minimum per call
+    per_call = []
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    for a, z in pairs:
+        a.record(stream)
+        V.sta_attn_fwd(q, k, v, w.grid, w.tile, w.window, w.shifts[0], scale=w.softmax_scale, out=buf.local[0])
+        z.record(stream)
+    torch.cuda.synchronize()
+    per_call = sorted(a.elapsed_time(z) for a, z in pairs)
     launch_flops = fl["local"] / n_local
     achieved = launch_flops / (launch_ms * 1e-3) / 1e12
     traffic = measured_traffic() if w.name == "sta_720p" else None
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "kernel": ROOFLINE_KERNEL, "launch_ms": round(launch_ms, 4),
-                "flop_per_launch": launch_flops}
+                "flop_per_launch": launch_flops,
+                "per_call_ms": {"n": len(per_call), "median": round(per_call[len(per_call) // 2], 4),
+                                "min": round(per_call[0], 4)}}
 
     clock = None
     if args.clock_seconds > 0:
