@@ -115,6 +115,30 @@ def test_sta_outlier_keys(case):
     compare(lse[0].cpu(), rl, dt, name + " lse")
 
 
+BATCH_STA = [
+    # name, grid, tile, window, shift, dtype: each attention kernel with batch 2 and 3 heads
+    ("tile384_bf16", (6, 16, 16), (6, 8, 8), (1, 3, 1), (0, 0, 0), "bf16"),
+    ("tile192_bf16", (6, 16, 16), (3, 8, 8), (1, 1, 3), (1, 4, 4), "bf16"),
+    ("tile32_bf16", (4, 12, 12), (2, 4, 4), (3, 1, 3), (0, 2, 0), "bf16"),
+    ("tile32_f32", (4, 12, 12), (2, 4, 4), (1, 3, 3), (1, 0, 2), "f32"),
+]
+
+
+@pytest.mark.parametrize("case", BATCH_STA, ids=[c[0] for c in BATCH_STA])
+def test_sta_batch2_heads3(case):
+    """Batch and head decoding of the workgroup index in every kernel shape:
+    two batches of three heads, each (batch, head) pair with its own inputs."""
+    name, grid, tile, window, shift, dt = case
+    say(f"[sta batch 2] {name}")
+    N = int(np.prod(grid))
+    q, k, v = qkv((2, 3, N, 128), TDT[dt], seed=970)
+    o, lse = V.sta_attn_fwd(q, k, v, grid, tile, window, shift, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle_sta(q, k, v, grid, tile, window, shift, 128 ** -0.5)
+    compare(o.reshape(6, N, 128).cpu(), ro, dt, name)
+    compare(lse.reshape(6, N).cpu(), rl, dt, name + " lse")
+
+
 @pytest.mark.parametrize("case", OUTLIER_STA, ids=[c[0] for c in OUTLIER_STA])
 def test_sta_scale_zero(case):
     """Degenerate softmax: scale 0 gives every key of the window the same

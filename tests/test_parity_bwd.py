@@ -54,6 +54,7 @@ STA_BWD = [
     ("tile32_bf16", 1, (4, 8, 12), (2, 4, 4), (1, 3, 3), (0, 0, 0), 2, 128, "bf16"),
     ("shift_partial_bf16", 2, (3, 10, 13), (2, 4, 4), (3, 1, 3), (1, 2, 2), 1, 128, "bf16"),
     ("tile384_bf16", 1, (6, 16, 16), (6, 8, 8), (1, 3, 1), (0, 0, 0), 1, 128, "bf16"),
+    ("tile384_b2h3_bf16", 2, (6, 8, 16), (6, 8, 8), (1, 1, 3), (0, 0, 0), 3, 128, "bf16"),
     ("f32_d64", 1, (3, 6, 8), (3, 3, 4), (1, 3, 1), (0, 1, 2), 2, 64, "f32"),
     ("f32_d128", 1, (2, 6, 8), (1, 3, 4), (1, 1, 3), (0, 0, 0), 1, 128, "f32"),
 ]
