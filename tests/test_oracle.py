@@ -158,6 +158,28 @@ def test_weights_row_stochastic_and_zero_outside(grid, tile, window, shift):
     assert (P[allowed] > 0).all()
 
 
+@pytest.mark.parametrize("grid,tile,window,shift", [c for c in SPARSE_CASES if np.prod(c[0]) <= 1200]
+                         + FULL_WINDOW_CASES[:2])
+@pytest.mark.parametrize("scale", [None, 0.7])
+def test_weights_equal_torch_softmax_of_masked_scores(grid, tile, window, shift, scale):
+    # the values themselves, not only their pattern: torch's softmax of the
+    # scaled logits with every key outside an independently built mask at -inf
+    # (a wrong scale, a dropped max shift or a transposed operand fails here)
+    N = int(np.prod(grid))
+    D = 8
+    q, k = randn(22, N, D), randn(23, N, D)
+    P = R.attention_weights_ref(q, k, grid, tile, window, shift, scale=scale)
+    s = (1.0 / math.sqrt(D)) if scale is None else scale
+    logits = s * torch.from_numpy(q) @ torch.from_numpy(k).T
+    mask = torch.from_numpy(_sta_mask_by_coords(grid, tile, window, shift))
+    ref = torch.softmax(logits.masked_fill(~mask, float("-inf")), dim=1).numpy()
+    np.testing.assert_allclose(P, ref, rtol=0, atol=1e-13)
+    # and the weights reproduce the oracle's output: O = P V
+    v = randn(24, N, 5)
+    o, _ = R.sta_ref(q, k, v, grid, tile, window, shift, scale=scale)
+    np.testing.assert_allclose(P @ v, o, rtol=0, atol=1e-12)
+
+
 @pytest.mark.parametrize("window", [(1, 1, 1), (3, 3, 3), (1, 3, 5), (3, 5, 1)])
 def test_unit_tiles_equal_token_sliding_window(window):
     grid = (4, 7, 9)
@@ -590,6 +612,42 @@ def test_hier_pooled_by_explicit_cells(grid, tile, window, shift, pool):
     so, sl = R.sta_ref(q, k, v, grid, tile, window, shift, scale=0.5)
     np.testing.assert_allclose(o1, so, atol=1e-13)
     np.testing.assert_allclose(l1, sl, atol=1e-13)
+
+
+HIER_COUNT_CASES = [
+    # grid, tile, window, shift, pool: aligned, shifted, ragged cells, (4, 3) pooling
+    ((3, 8, 16), (1, 4, 4), (1, 3, 3), (0, 0, 0), (2, 2)),
+    ((2, 9, 11), (1, 3, 4), (1, 3, 3), (0, 1, 1), (2, 2)),
+    ((4, 10, 14), (2, 4, 6), (3, 1, 3), (1, 2, 3), (4, 3)),
+    ((3, 7, 9), (2, 3, 2), (1, 3, 5), (1, 1, 1), (3, 2)),
+    ((2, 6, 6), (1, 1, 1), (3, 11, 11), (0, 0, 0), (2, 2)),   # full window: every cell
+]
+
+
+@pytest.mark.parametrize("grid,tile,window,shift,pool", HIER_COUNT_CASES)
+def test_hier_pair_count_brute_force(grid, tile, window, shift, pool):
+    # query by query: the distinct pooling cells among the tokens of an
+    # independently built token mask (raw coordinates, numpy's own index
+    # decomposition, a token -> cell map written here)
+    T, H, W = grid
+    mask = _sta_mask_by_coords(grid, tile, window, shift)
+    t, h, w = np.unravel_index(np.arange(T * H * W), (T, H, W))
+    Wp = -(-W // pool[1])
+    cell = (t * (-(-H // pool[0])) + h // pool[0]) * Wp + w // pool[1]
+    brute = sum(len(set(cell[mask[n]].tolist())) for n in range(T * H * W))
+    assert R.hier_pair_count_ref(grid, tile, window, shift, pool) == brute
+
+
+def test_hier_pair_count_1080p_closed_form():
+    # 1080P local windows (21 x 17 x 30 tokens, one window per tile) over
+    # 2 x 2 cells: along H a window [17i, 17i + 17) meets cells
+    # floor(17i / 2) .. floor((17i + 16) / 2), nine for every i in 0..3; along
+    # W the 30-token windows hold exactly 15 cells; T is not pooled
+    assert R.hier_pair_count_ref((21, 68, 120), (21, 17, 30), (1, 1, 1), (0, 0, 0), (2, 2)) \
+        == 21 * 68 * 120 * (21 * 9 * 15)
+    # pooling 1 x 1 is sliding-tile attention's own pair count
+    for grid, tile, window, shift, _ in HIER_COUNT_CASES:
+        assert R.hier_pair_count_ref(grid, tile, window, shift, (1, 1)) == R.sta_pair_count_ref(grid, tile, window, shift)
 
 
 # ---------------------------------------------------------------- window modes
