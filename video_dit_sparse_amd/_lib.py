@@ -178,12 +178,98 @@ def _problem_for(q, grid, scale) -> Problem:
 
 
 def _same(q, *others):
+    """q and every tensor in ``others``: equal shape and dtype (devices are
+    checked by ``_on_device`` once every shape is known to be right)."""
+    torch = _torch()
+    for t in (q,) + others:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"expected a torch tensor, got {type(t).__name__}")
     for t in others:
-        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
-            raise ValueError("q, k, v (and outputs) must share shape, dtype and device")
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v (and outputs) must share shape and dtype: "
+                             f"{tuple(q.shape)} {q.dtype} against {tuple(t.shape)} {t.dtype}")
+
+
+def _arg(t, name, shape, dtype, contiguous=False):
+    """A caller-supplied tensor argument: exactly ``shape`` and ``dtype``
+    (and contiguous if asked).  The C ABI derives every extent from the
+    problem descriptor, so a smaller or mistyped buffer would be written past
+    its end; this check runs before any library call.  Returns ``t``."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor, got {type(t).__name__}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _workspace_arg(t):
+    """A caller's workspace: a contiguous tensor (its byte size is checked by
+    the library against the size the call needs).  ``None`` passes."""
+    torch = _torch()
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"workspace must be a torch tensor, got {type(t).__name__}")
+    if not t.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return t
+
+
+def _on_device(q, *tensors):
+    """Every tensor is GPU memory on q's device (a host pointer handed to a
+    kernel would fault the GPU).  ``None`` entries are skipped."""
+    if not q.is_cuda:
+        raise ValueError(f"tensors must be on a GPU device, got {q.device}")
+    for t in tensors:
+        if t is not None and t.device != q.device:
+            raise ValueError(f"every tensor must be on {q.device}, got one on {t.device}")
 
 
 # ---------------------------------------------------------------- entry points
+def _out_like(q, out, name="out"):
+    torch = _torch()
+    if out is None:
+        return torch.empty_like(q, memory_format=torch.contiguous_format)
+    return _arg(out, name, q.shape, q.dtype)
+
+
+def _lse_buf(q, lse, want, name="lse"):
+    """LSE output: fp32 [B, heads, N] contiguous; allocated if wanted and not given."""
+    torch = _torch()
+    shape = tuple(q.shape[:3])
+    if lse is not None:
+        return _arg(lse, name, shape, torch.float32, contiguous=True)
+    return torch.empty(shape, dtype=torch.float32, device=q.device) if want else None
+
+
+def _lse_in(q, t, name):
+    return _arg(t, name, tuple(q.shape[:3]), _torch().float32, contiguous=True)
+
+
+def _gate(w, heads, name):
+    return None if w is None else _arg(w, name, (heads,), _torch().float32, contiguous=True)
+
+
+def _ptr(t):
+    return t.data_ptr() if t is not None else None
+
+
+def _workspace(q, workspace, need):
+    torch = _torch()
+    if workspace is None:
+        return torch.empty(need, dtype=torch.uint8, device=q.device)
+    return workspace
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
 def sta_attn_fwd(q, k, v, grid: Sequence[int], tile: Sequence[int], window: Sequence[int],
                  shift: Sequence[int] = (0, 0, 0), scale: Optional[float] = None, out=None,
                  lse=None, return_lse: bool = False, stream=None, window_mode: str = "clip"):
@@ -193,17 +279,16 @@ def sta_attn_fwd(q, k, v, grid: Sequence[int], tile: Sequence[int], window: Sequ
     window_mode: "clip" (default), "inward" or "cyclic" (vdsa_window_mode).
     Returns O (and LSE [B, heads, N] fp32 if requested).
     """
-    torch = _torch()
     _same(q, k, v)
     prob = _problem_for(q, grid, scale)
     cfg = make_cfg(tile, window, shift, window_mode)
-    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
-    if lse is None and return_lse:
-        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    o = _out_like(q, out)
+    lse = _lse_buf(q, lse, return_lse)
+    _on_device(q, k, v, o, lse)
     check(lib().sta_attn_fwd(ctypes.byref(prob), ctypes.byref(cfg),
                              q.data_ptr(), ctypes.byref(_strides(q)), k.data_ptr(), ctypes.byref(_strides(k)),
                              v.data_ptr(), ctypes.byref(_strides(v)), o.data_ptr(), ctypes.byref(_strides(o)),
-                             lse.data_ptr() if lse is not None else None, _stream(stream)))
+                             _ptr(lse), _stream(stream)))
     return (o, lse) if (return_lse or lse is not None) else o
 
 
@@ -218,21 +303,19 @@ def global_pooled_attn_fwd(q, k, v, grid, pool_hw, scale=None, out=None, lse=Non
                            workspace=None, stream=None):
     """Global branch: queries attend k_h x k_w average-pooled K/V
     (``global_pooled_attn_fwd`` in include/vdsa.h).  Returns O (and LSE)."""
-    torch = _torch()
     _same(q, k, v)
     prob = _problem_for(q, grid, scale)
+    o = _out_like(q, out)
+    lse = _lse_buf(q, lse, return_lse)
+    _on_device(q, k, v, o, lse, _workspace_arg(workspace))
     need = ctypes.c_size_t()
     check(lib().global_pooled_attn_workspace_size(ctypes.byref(prob), _pool(pool_hw), ctypes.byref(need)))
-    if workspace is None:
-        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
-    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
-    if lse is None and return_lse:
-        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    workspace = _workspace(q, workspace, need.value)
     check(lib().global_pooled_attn_fwd(
         ctypes.byref(prob), _pool(pool_hw), q.data_ptr(), ctypes.byref(_strides(q)),
         k.data_ptr(), ctypes.byref(_strides(k)), v.data_ptr(), ctypes.byref(_strides(v)),
-        o.data_ptr(), ctypes.byref(_strides(o)), lse.data_ptr() if lse is not None else None,
-        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+        o.data_ptr(), ctypes.byref(_strides(o)), _ptr(lse),
+        workspace.data_ptr(), _nbytes(workspace), _stream(stream)))
     return (o, lse) if (return_lse or lse is not None) else o
 
 
@@ -240,26 +323,19 @@ def dual_branch_merge(o_local, o_global, w_global, w_local=None, out=None, strea
     """out = w_local[h] * o_local + w_global[h] * o_global (``dual_branch_merge``).
 
     ``out=o_local`` merges in place."""
-    torch = _torch()
     _same(o_local, o_global)
     B, Hh, N, D = o_local.shape
     prob = make_problem(B, Hh, D, (1, 1, N), _dtype_code(o_local), 1.0)
-    o = torch.empty_like(o_local, memory_format=torch.contiguous_format) if out is None else out
-    for w in (w_global, w_local):
-        if w is not None and (w.dtype != torch.float32 or w.numel() != Hh or not w.is_contiguous()):
-            raise ValueError("gates must be contiguous float32 tensors of length heads")
+    o = _out_like(o_local, out)
+    if w_global is None:
+        raise ValueError("w_global is required")
+    w_global, w_local = _gate(w_global, Hh, "w_global"), _gate(w_local, Hh, "w_local")
+    _on_device(o_local, o_global, o, w_global, w_local)
     check(lib().dual_branch_merge(ctypes.byref(prob), o_local.data_ptr(), ctypes.byref(_strides(o_local)),
                                   o_global.data_ptr(), ctypes.byref(_strides(o_global)),
-                                  w_local.data_ptr() if w_local is not None else None, w_global.data_ptr(),
+                                  _ptr(w_local), w_global.data_ptr(),
                                   o.data_ptr(), ctypes.byref(_strides(o)), _stream(stream)))
     return o
-
-
-def _lse_arg(t, shape, name):
-    torch = _torch()
-    if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous float32 tensor of shape {tuple(shape)}")
-    return t.data_ptr()
 
 
 def dual_branch_merge_lse(o_local, lse_local, o_global, lse_global, out=None, lse_out=None,
@@ -267,18 +343,17 @@ def dual_branch_merge_lse(o_local, lse_local, o_global, lse_global, out=None, ls
     """One softmax over the union of both branches' keys, from their LSEs
     (``dual_branch_merge_lse``).  ``out=o_local`` merges in place.  Returns O
     (and the merged LSE if requested)."""
-    torch = _torch()
     _same(o_local, o_global)
     B, Hh, N, D = o_local.shape
     prob = make_problem(B, Hh, D, (1, 1, N), _dtype_code(o_local), 1.0)
-    o = torch.empty_like(o_local, memory_format=torch.contiguous_format) if out is None else out
-    if lse_out is None and return_lse:
-        lse_out = torch.empty((B, Hh, N), dtype=torch.float32, device=o_local.device)
+    o = _out_like(o_local, out)
+    lse_local, lse_global = _lse_in(o_local, lse_local, "lse_local"), _lse_in(o_local, lse_global, "lse_global")
+    lse_out = _lse_buf(o_local, lse_out, return_lse, "lse_out")
+    _on_device(o_local, o_global, o, lse_local, lse_global, lse_out)
     check(lib().dual_branch_merge_lse(
-        ctypes.byref(prob), o_local.data_ptr(), ctypes.byref(_strides(o_local)), _lse_arg(lse_local, (B, Hh, N), "lse_local"),
-        o_global.data_ptr(), ctypes.byref(_strides(o_global)), _lse_arg(lse_global, (B, Hh, N), "lse_global"),
-        o.data_ptr(), ctypes.byref(_strides(o)),
-        _lse_arg(lse_out, (B, Hh, N), "lse_out") if lse_out is not None else None, _stream(stream)))
+        ctypes.byref(prob), o_local.data_ptr(), ctypes.byref(_strides(o_local)), lse_local.data_ptr(),
+        o_global.data_ptr(), ctypes.byref(_strides(o_global)), lse_global.data_ptr(),
+        o.data_ptr(), ctypes.byref(_strides(o)), _ptr(lse_out), _stream(stream)))
     return (o, lse_out) if (return_lse or lse_out is not None) else o
 
 
@@ -289,30 +364,26 @@ def global_pooled_attn_merge_fwd(q, k, v, grid, pool_hw, o_local, mode="gated", 
     (``global_pooled_attn_merge_fwd``): ``mode`` "gated" (w_global, optional
     w_local) or "lse" (lse_local).  ``out=o_local`` merges in place.  Returns
     the merged O (and lse_out if requested)."""
-    torch = _torch()
+    if mode not in MERGE_MODES:
+        raise ValueError(f"mode must be one of {tuple(MERGE_MODES)}, got {mode!r}")
     _same(q, k, v, o_local)
     B, Hh, N, D = q.shape
     prob = _problem_for(q, grid, scale)
+    o = _out_like(q, out)
+    lse_out = _lse_buf(q, lse_out, return_lse, "lse_out")
+    lse_local = _lse_in(q, lse_local, "lse_local") if lse_local is not None else None
+    w_global, w_local = _gate(w_global, Hh, "w_global"), _gate(w_local, Hh, "w_local")
+    _on_device(q, k, v, o_local, o, lse_out, lse_local, w_global, w_local, _workspace_arg(workspace))
     need = ctypes.c_size_t()
     check(lib().global_pooled_attn_workspace_size(ctypes.byref(prob), _pool(pool_hw), ctypes.byref(need)))
-    if workspace is None:
-        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
-    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
-    if lse_out is None and return_lse:
-        lse_out = torch.empty((B, Hh, N), dtype=torch.float32, device=q.device)
-    for w in (w_global, w_local):
-        if w is not None and (w.dtype != torch.float32 or w.numel() != Hh or not w.is_contiguous()):
-            raise ValueError("gates must be contiguous float32 tensors of length heads")
+    workspace = _workspace(q, workspace, need.value)
     check(lib().global_pooled_attn_merge_fwd(
         ctypes.byref(prob), _pool(pool_hw), q.data_ptr(), ctypes.byref(_strides(q)),
         k.data_ptr(), ctypes.byref(_strides(k)), v.data_ptr(), ctypes.byref(_strides(v)),
         MERGE_MODES[mode], o_local.data_ptr(), ctypes.byref(_strides(o_local)),
-        _lse_arg(lse_local, (B, Hh, N), "lse_local") if lse_local is not None else None,
-        w_local.data_ptr() if w_local is not None else None,
-        w_global.data_ptr() if w_global is not None else None,
-        o.data_ptr(), ctypes.byref(_strides(o)),
-        _lse_arg(lse_out, (B, Hh, N), "lse_out") if lse_out is not None else None,
-        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+        _ptr(lse_local), _ptr(w_local), _ptr(w_global),
+        o.data_ptr(), ctypes.byref(_strides(o)), _ptr(lse_out),
+        workspace.data_ptr(), _nbytes(workspace), _stream(stream)))
     return (o, lse_out) if (return_lse or lse_out is not None) else o
 
 
@@ -320,47 +391,43 @@ def hier_pooled_attn_fwd(q, k, v, grid, tile, window, pool_hw, shift=(0, 0, 0), 
                          return_lse=False, workspace=None, stream=None):
     """Full-resolution queries against the pooled K/V of their sliding-tile
     window (``hier_pooled_attn_fwd``).  Returns O (and LSE)."""
-    torch = _torch()
     _same(q, k, v)
     prob = _problem_for(q, grid, scale)
     cfg = make_cfg(tile, window, shift)
+    o = _out_like(q, out)
+    lse = _lse_buf(q, lse, return_lse)
+    _on_device(q, k, v, o, lse, _workspace_arg(workspace))
     need = ctypes.c_size_t()
     check(lib().hier_pooled_attn_workspace_size(ctypes.byref(prob), _pool(pool_hw), ctypes.byref(need)))
-    if workspace is None:
-        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
-    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
-    if lse is None and return_lse:
-        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    workspace = _workspace(q, workspace, need.value)
     check(lib().hier_pooled_attn_fwd(
         ctypes.byref(prob), ctypes.byref(cfg), _pool(pool_hw), q.data_ptr(), ctypes.byref(_strides(q)),
         k.data_ptr(), ctypes.byref(_strides(k)), v.data_ptr(), ctypes.byref(_strides(v)),
-        o.data_ptr(), ctypes.byref(_strides(o)), lse.data_ptr() if lse is not None else None,
-        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+        o.data_ptr(), ctypes.byref(_strides(o)), _ptr(lse),
+        workspace.data_ptr(), _nbytes(workspace), _stream(stream)))
     return (o, lse) if (return_lse or lse is not None) else o
 
 
 def compressed_global_attn_fwd(q, k, v, grid, pool_hw, scale=None, out=None, workspace=None, stream=None):
     """Pooled Q, K, V, full attention among pooled tokens, bilinear upsampling
     (``compressed_global_attn_fwd``).  Returns O."""
-    torch = _torch()
     _same(q, k, v)
     prob = _problem_for(q, grid, scale)
+    o = _out_like(q, out)
+    _on_device(q, k, v, o, _workspace_arg(workspace))
     need = ctypes.c_size_t()
     check(lib().compressed_global_attn_workspace_size(ctypes.byref(prob), _pool(pool_hw), ctypes.byref(need)))
-    if workspace is None:
-        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
-    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    workspace = _workspace(q, workspace, need.value)
     check(lib().compressed_global_attn_fwd(
         ctypes.byref(prob), _pool(pool_hw), q.data_ptr(), ctypes.byref(_strides(q)),
         k.data_ptr(), ctypes.byref(_strides(k)), v.data_ptr(), ctypes.byref(_strides(v)),
         o.data_ptr(), ctypes.byref(_strides(o)),
-        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+        workspace.data_ptr(), _nbytes(workspace), _stream(stream)))
     return o
 
 
 def _bwd_outputs(q, dq, dk, dv):
-    torch = _torch()
-    return tuple(torch.empty_like(q, memory_format=torch.contiguous_format) if t is None else t for t in (dq, dk, dv))
+    return tuple(_out_like(q, t, name) for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")))
 
 
 def sta_attn_bwd_workspace_size(batch, heads, head_dim, grid, dtype_code=VDSA_BF16) -> int:
@@ -374,23 +441,22 @@ def sta_attn_bwd(q, k, v, o, do, lse, grid, tile, window, shift=(0, 0, 0), scale
                  workspace=None, stream=None, window_mode: str = "clip"):
     """Gradients of ``sta_attn_fwd`` (``sta_attn_bwd`` in include/vdsa.h), from
     the forward's inputs, output ``o`` and ``lse``.  Returns (dQ, dK, dV)."""
-    torch = _torch()
     _same(q, k, v, o, do)
-    B, Hh, N, D = q.shape
     prob = _problem_for(q, grid, scale)
     cfg = make_cfg(tile, window, shift, window_mode)
+    lse = _lse_in(q, lse, "lse")
+    dq, dk, dv = _bwd_outputs(q, dq, dk, dv)
+    _on_device(q, k, v, o, do, lse, dq, dk, dv, _workspace_arg(workspace))
     need = ctypes.c_size_t()
     check(lib().sta_attn_bwd_workspace_size(ctypes.byref(prob), ctypes.byref(need)))
-    if workspace is None:
-        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
-    dq, dk, dv = _bwd_outputs(q, dq, dk, dv)
+    workspace = _workspace(q, workspace, need.value)
     check(lib().sta_attn_bwd(
         ctypes.byref(prob), ctypes.byref(cfg), q.data_ptr(), ctypes.byref(_strides(q)),
         k.data_ptr(), ctypes.byref(_strides(k)), v.data_ptr(), ctypes.byref(_strides(v)),
         o.data_ptr(), ctypes.byref(_strides(o)), do.data_ptr(), ctypes.byref(_strides(do)),
-        _lse_arg(lse, (B, Hh, N), "lse"), dq.data_ptr(), ctypes.byref(_strides(dq)),
+        lse.data_ptr(), dq.data_ptr(), ctypes.byref(_strides(dq)),
         dk.data_ptr(), ctypes.byref(_strides(dk)), dv.data_ptr(), ctypes.byref(_strides(dv)),
-        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+        workspace.data_ptr(), _nbytes(workspace), _stream(stream)))
     return dq, dk, dv
 
 
@@ -398,33 +464,35 @@ def global_pooled_attn_bwd(q, k, v, o, do, lse, grid, pool_hw, scale=None, dq=No
                            workspace=None, stream=None):
     """Gradients of ``global_pooled_attn_fwd`` through the pooling
     (``global_pooled_attn_bwd``).  Returns (dQ, dK, dV)."""
-    torch = _torch()
     _same(q, k, v, o, do)
-    B, Hh, N, D = q.shape
     prob = _problem_for(q, grid, scale)
+    lse = _lse_in(q, lse, "lse")
+    dq, dk, dv = _bwd_outputs(q, dq, dk, dv)
+    _on_device(q, k, v, o, do, lse, dq, dk, dv, _workspace_arg(workspace))
     need = ctypes.c_size_t()
     check(lib().global_pooled_attn_bwd_workspace_size(ctypes.byref(prob), _pool(pool_hw), ctypes.byref(need)))
-    if workspace is None:
-        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
-    dq, dk, dv = _bwd_outputs(q, dq, dk, dv)
+    workspace = _workspace(q, workspace, need.value)
     check(lib().global_pooled_attn_bwd(
         ctypes.byref(prob), _pool(pool_hw), q.data_ptr(), ctypes.byref(_strides(q)),
         k.data_ptr(), ctypes.byref(_strides(k)), v.data_ptr(), ctypes.byref(_strides(v)),
         o.data_ptr(), ctypes.byref(_strides(o)), do.data_ptr(), ctypes.byref(_strides(do)),
-        _lse_arg(lse, (B, Hh, N), "lse"), dq.data_ptr(), ctypes.byref(_strides(dq)),
+        lse.data_ptr(), dq.data_ptr(), ctypes.byref(_strides(dq)),
         dk.data_ptr(), ctypes.byref(_strides(dk)), dv.data_ptr(), ctypes.byref(_strides(dv)),
-        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+        workspace.data_ptr(), _nbytes(workspace), _stream(stream)))
     return dq, dk, dv
 
 
 def kv_avgpool_fwd(x, grid, pool_hw, out=None, stream=None):
     """k_h x k_w frame-wise average pooling of a [B, heads, N, D] tensor."""
     torch = _torch()
+    _same(x)
     B, Hh, N, D = x.shape
     prob = _problem_for(x, grid, 1.0)
     T, H, W = grid
     M = T * (-(-H // pool_hw[0])) * (-(-W // pool_hw[1]))
-    y = torch.empty((B, Hh, M, D), dtype=x.dtype, device=x.device) if out is None else out
+    y = torch.empty((B, Hh, M, D), dtype=x.dtype, device=x.device) if out is None else \
+        _arg(out, "out", (B, Hh, M, D), x.dtype)
+    _on_device(x, y)
     check(lib().kv_avgpool_fwd(ctypes.byref(prob), _pool(pool_hw), x.data_ptr(), ctypes.byref(_strides(x)),
                                y.data_ptr(), ctypes.byref(_strides(y)), _stream(stream)))
     return y
