@@ -75,41 +75,103 @@ def gfx_clock_mhz():
     return sum(mhz) / len(mhz) if mhz else None
 
 
-def cpu_baseline(w, q, k, v, budget_s: float):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    whole query tiles of head 0, in a seeded random order, until the time
-    budget is spent.  Returns the JSON object."""
+def cpu_model_name() -> str:
+    """The host CPU's model name (/proc/cpuinfo, as lscpu reports it)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# one CPU-baseline work item: a whole query tile of one head through the
+# oracle as it stands, on the head's Q/K/V memory-mapped from fp64 .npy files
+# (one copy in the page cache, shared by every worker)
+def _cpu_tile(job):
     import numpy as np
     import oracle as R
+    paths, slot, grid, tile, window, shift, scale, a = job
+    qh, kh, vh = (np.load(pth, mmap_mode="r")[slot] for pth in paths)
+    ti = R.tile_index(R.token_coords(grid), tile, shift)
+    rows = np.nonzero(np.all(ti == np.asarray(a)[None, :], axis=1))[0]
+    nkeys = int(R.sta_mask_row(ti, a, R.window_radius(window)).sum())
+    R.sta_ref(qh, kh, vh, grid, tile, window, shift, scale=scale, rows=rows)
+    return 4.0 * qh.shape[1] * len(rows) * nkeys
+
+
+def cpu_baseline(w, q, k, v, budget_s: float, n_heads: int = 4):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    whole query tiles of ``n_heads`` seeded heads, in a seeded random order,
+    over a pool of worker processes (one per core of the host's CPU share,
+    each with one BLAS thread) until the time budget is spent.  The rate is
+    effective FLOP of the finished tiles over the wall time; the full call's
+    CPU time is extrapolated from it.  Returns the JSON object."""
+    import multiprocessing as mp
+    import shutil
+    import tempfile
+
+    import numpy as np
+    import oracle as R
+
+    nproc = os.cpu_count() or 1
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    qh, kh, vh = (R.to_f64(x[0, 0]) for x in (q, k, v))
-    shift = w.shifts[0]
-    counts = R.tile_counts(w.grid, w.tile, shift)
-    coords = R.token_coords(w.grid)
-    ti = R.tile_index(coords, w.tile, shift)
-    radius = R.window_radius(w.window)
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        avail = nproc
+    # the host share a GPU box grants one GPU is 16 cores, whatever nproc shows
+    workers = max(1, min(avail, 16))
     rng = np.random.default_rng(0)
-    order = rng.permutation(int(np.prod(counts)))
-    done_flops, tiles, rows_done = 0.0, 0, 0
-    t0 = time.perf_counter()
-    for flat in order:
-        a = np.unravel_index(flat, counts)
-        rows = np.nonzero(np.all(ti == np.array(a)[None, :], axis=1))[0]
-        nkeys = int(R.sta_mask_row(ti, a, radius).sum())
-        R.sta_ref(qh, kh, vh, w.grid, w.tile, w.window, shift, scale=w.softmax_scale, rows=rows)
-        done_flops += 4.0 * w.head_dim * len(rows) * nkeys
-        tiles += 1
-        rows_done += len(rows)
-        if time.perf_counter() - t0 > budget_s:
-            break
-    el = time.perf_counter() - t0
-    return {"value": done_flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{tiles} whole query tiles ({rows_done} query rows) of head 0 of {w.name}, "
-                      f"fp64 NumPy, {el:.1f} s wall"}
+    heads = sorted(rng.choice(w.heads, size=min(n_heads, w.heads), replace=False).tolist())
+    tmp = tempfile.mkdtemp(prefix="vdsa_cpu_")
+    saved_env = {e: os.environ.get(e) for e in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    try:
+        paths = []
+        for name, x in (("q", q), ("k", k), ("v", v)):
+            pth = os.path.join(tmp, f"{name}.npy")
+            np.save(pth, R.to_f64(x[0, heads]))
+            paths.append(pth)
+        shift = w.shifts[0]
+        counts = R.tile_counts(w.grid, w.tile, shift)
+        jobs = [(paths, slot, w.grid, w.tile, w.window, shift, w.softmax_scale,
+                 tuple(int(c) for c in np.unravel_index(flat, counts)))
+                for slot in range(len(heads)) for flat in range(int(np.prod(counts)))]
+        jobs = [jobs[i] for i in rng.permutation(len(jobs))]
+        for e in saved_env:
+            os.environ[e] = "1"
+        ctx = mp.get_context("spawn")
+        with ctx.Pool(workers) as pool:
+            pool.map(int, range(workers))   # start every worker before the clock
+            done_flops, tiles, pending, it = 0.0, 0, [], iter(jobs)
+            t0 = time.perf_counter()
+            for _ in range(workers):
+                pending.append(pool.apply_async(_cpu_tile, (next(it),)))
+            while pending:
+                r = pending.pop(0)
+                done_flops += r.get()
+                tiles += 1
+                if time.perf_counter() - t0 < budget_s:
+                    nxt = next(it, None)
+                    if nxt is not None:
+                        pending.append(pool.apply_async(_cpu_tile, (nxt,)))
+            el = time.perf_counter() - t0
+    finally:
+        for e, val in saved_env.items():
+            if val is None:
+                os.environ.pop(e, None)
+            else:
+                os.environ[e] = val
+        shutil.rmtree(tmp, ignore_errors=True)
+    rate = done_flops / el
+    full_flop = R.sta_flops_ref(w.grid, w.tile, w.window, w.shifts[0], head_dim=w.head_dim, heads=w.heads,
+                                batch=w.batch)
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "sample": f"{tiles} whole query tiles drawn at random from heads {heads} of {w.name}, "
+                      f"fp64 NumPy oracle in {workers} worker processes (1 BLAS thread each), {el:.1f} s wall",
+            "nproc": nproc, "cpus_available": avail, "cpu_model": cpu_model_name(),
+            "wall_s": round(el, 2), "effective_flop_done": done_flops,
+            "extrapolated_full_call_s": round(full_flop / rate, 1)}
 
 
 def main():

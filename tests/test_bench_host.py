@@ -41,3 +41,16 @@ def test_parse_gfx_clocks():
 """
     assert bench.parse_gfx_clocks(text) == [2056, 2008]
     assert bench.parse_gfx_clocks("no clocks here") == []
+
+
+def test_cpu_baseline_fields_on_a_small_workload():
+    # the oracle on whole query tiles, in worker processes, on the host
+    from video_dit_sparse_amd import workloads as WL
+    w = WL.Workload("small_sparse", (4, 8, 12), heads=3, head_dim=64, dtype="bf16", tile=(2, 4, 4),
+                    window=(1, 1, 3))
+    q, k, v = WL.make_qkv(w, "cpu")
+    r = bench.cpu_baseline(w, q, k, v, 0.3, n_heads=2)
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["value"] > 0
+    assert 1 <= r["cores"] <= min(16, r["cpus_available"]) and r["nproc"] == os.cpu_count()
+    assert r["cpu_model"] and "whole query tiles" in r["sample"]
+    assert r["effective_flop_done"] > 0 and r["extrapolated_full_call_s"] > 0
