@@ -194,10 +194,11 @@ def sta_ref(q, k, v, grid, tile, window, shift=(0, 0, 0), scale=None, rows=None,
     For query token n: O_n = sum_m softmax_m(scale * q_n . k_m) v_m with m over
     the keys whose tile lies in the window around n's tile (``sta_mask_row``).
 
-    The explicit boolean mask is built row by row over all N keys; rows of one
-    query tile are checked to be identical and non-empty (the query's own tile
-    is always in its window), then that tile's rows are evaluated on exactly
-    the selected keys, which equals masking every other key to -inf.
+    Queries are grouped by their tile index; the explicit boolean mask row
+    over all N keys depends on the query only through that index, so it is
+    built once per group and checked non-empty (the query's own tile is
+    always in its window), then the group's rows are evaluated on exactly the
+    selected keys, which equals masking every other key to -inf.
 
     ``rows``: optional query token indices to evaluate (rows are independent).
     Returns (O [len(rows), D], LSE [len(rows)]).
@@ -218,12 +219,9 @@ def sta_ref(q, k, v, grid, tile, window, shift=(0, 0, 0), scale=None, rows=None,
     inv = np.asarray(inv).reshape(-1)
     for g in range(len(uniq)):
         pos = np.nonzero(inv == g)[0]
-        block = np.empty((len(pos), N), dtype=bool)
-        for j, n in enumerate(rows[pos]):
-            block[j] = mode_mask_row(ti, ti[n], radius, counts, window_mode)
-        assert block[0].any(), "a query row with no key"
-        assert (block == block[0][None, :]).all(), "rows of one query tile differ"
-        keys = np.nonzero(block[0])[0]
+        mask = mode_mask_row(ti, uniq[g], radius, counts, window_mode)
+        assert mask.any(), "a query row with no key"
+        keys = np.nonzero(mask)[0]
         o[pos], lse[pos] = _softmax_attend(q[rows[pos]], k[keys], v[keys], scale)
     return o, lse
 

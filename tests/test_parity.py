@@ -294,6 +294,11 @@ def _check_workload(name, heads_to_check, n_random_tiles=4, rows_per_tile=24):
                 kpool = ws[: w.batch * w.heads * M * w.head_dim * 2].view(torch.bfloat16).view(
                     w.batch, w.heads, M, w.head_dim)
                 compare(kpool[0, h].cpu(), kpr, w.dtype, f"{name} pooled k h{h}")
+                # pooled V follows pooled K in the workspace, 256-byte aligned
+                voff = -(-(w.batch * w.heads * M * w.head_dim * 2) // 256) * 256
+                vpool = ws[voff: voff + w.batch * w.heads * M * w.head_dim * 2].view(torch.bfloat16).view(
+                    w.batch, w.heads, M, w.head_dim)
+                compare(vpool[0, h].cpu(), vpr, w.dtype, f"{name} pooled v h{h}")
                 go, gl = R.global_ref(head_f64(q, 0, h), kpr, vpr, scale=w.softmax_scale, rows=rows)
                 compare(out["glob"][0, h, rows].cpu(), go, w.dtype, f"{name} global h{h}")
                 compare(out["glob_lse"][0, h, rows].cpu(), gl, w.dtype, f"{name} global lse h{h}")
@@ -323,6 +328,22 @@ def test_workload_tiny_all_rows():
 
 def test_workload_sta_720p():
     _check_workload("sta_720p", heads_to_check=[0, 23])
+
+
+def test_workload_sta_720p_full_head():
+    # every element of one whole 720P head, O and LSE: all 300 query tiles,
+    # corner, edge and interior, against the oracle
+    w = WL.WORKLOADS["sta_720p"]
+    h = 11
+    q, k, v = WL.make_qkv(w, DEV)
+    say(f"[workload] sta_720p full head {h}: running")
+    o, lse = V.sta_attn_fwd(q, k, v, w.grid, w.tile, w.window, scale=w.softmax_scale, return_lse=True)
+    torch.cuda.synchronize()
+    say(f"[workload] sta_720p full head {h}: oracle over all {w.n_tokens} rows")
+    ro, rl = R.sta_ref(head_f64(q, 0, h), head_f64(k, 0, h), head_f64(v, 0, h), w.grid, w.tile, w.window,
+                       (0, 0, 0), scale=w.softmax_scale)
+    compare(o[0, h].cpu(), ro, w.dtype, f"sta_720p full head {h}")
+    compare(lse[0, h].cpu(), rl, w.dtype, f"sta_720p full head {h} lse")
 
 
 def test_workload_dual_1080p():
