@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define VDSA_ABI_VERSION 3
+#define VDSA_ABI_VERSION 4
 
 typedef enum {
   VDSA_OK = 0,
@@ -172,6 +172,39 @@ vdsa_status global_pooled_attn_fwd(const vdsa_problem* prob, const int32_t pool_
                                    void* o, const vdsa_strides* o_strides,
                                    float* lse, void* workspace, size_t workspace_bytes,
                                    void* stream);
+
+/* Size of the static device scratch of global_pooled_attn_fwd_noalloc. */
+#define VDSA_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/*
+ * global_pooled_attn_fwd_noalloc - global_pooled_attn_fwd without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Computes exactly what global_pooled_attn_fwd computes (the same kernels) but
+ * keeps the pooled K and V in a static device array of
+ * VDSA_STATIC_SCRATCH_BYTES (128 MiB) that the library owns: one copy per
+ * GPU, held from the first use of the library's device code on that GPU
+ * until the process ends.  It calls no hipMalloc, hipFree or other
+ * allocating routine.  The scratch of the calling thread's current device is
+ * used, so `stream` must belong to that device; its address is resolved on
+ * the first call on each device (make that first call outside graph
+ * capture).  Every call on one GPU shares that GPU's scratch and leaves its
+ * pooled K/V there; calls that overlap in time on one GPU (other streams,
+ * other threads) race on it and must be serialised by the caller.  Nothing in
+ * it needs to start at zero: the pooling writes every byte the attention
+ * then reads.
+ *
+ * Errors: as global_pooled_attn_fwd; VDSA_ERR_WORKSPACE (before anything is
+ * launched) when the pooled K and V, 2 * round_up(batch * heads * M *
+ * head_dim * esize, 256) bytes, exceed VDSA_STATIC_SCRATCH_BYTES.
+ */
+vdsa_status global_pooled_attn_fwd_noalloc(const vdsa_problem* prob, const int32_t pool_hw[2],
+                                           const void* q, const vdsa_strides* q_strides,
+                                           const void* k, const vdsa_strides* k_strides,
+                                           const void* v, const vdsa_strides* v_strides,
+                                           void* o, const vdsa_strides* o_strides,
+                                           float* lse, void* stream);
 
 /*
  * dual_branch_merge - gated sum of the two branch outputs (UltraGen section

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert L.abi_version() == 3
+    assert L.abi_version() == 4
     for code in L.STATUS_NAMES:
         assert L.lib().vdsa_status_string(code)
 
@@ -347,3 +347,25 @@ def test_last_error_is_per_thread():
         assert st == L.STATUS["VDSA_ERR_WINDOW"]
         assert f"= {2 * i + 2}" in msg, msg
         assert after == "" and ok > 0
+
+
+def test_noalloc_global_host_checks():
+    # every check of the entry point that allocates nothing runs before its
+    # first HIP call (the scratch lookup), so each path is forced here
+    def g(p, pool=(4, 4), o=O, lse=None):
+        d = st(p, p.head_dim)
+        return L.lib().global_pooled_attn_fwd_noalloc(ctypes.byref(p), L._pool(pool), Q, ctypes.byref(d), K,
+                                                      ctypes.byref(d), V, ctypes.byref(d), o, ctypes.byref(d),
+                                                      lse, None)
+    # 4K latent, 4 x 4 pooling: pooled K + V = 2 x 263 MB, beyond the 128 MiB scratch
+    big = prob(heads=24, grid=(21, 136, 240))
+    assert g(big) == L.STATUS["VDSA_ERR_WORKSPACE"]
+    assert "static scratch" in L.lib().vdsa_last_error().decode()
+    # the same latent at 8 x 8 pooling fits (2 x 65.8 MB); it fails here only at the alignment check
+    assert g(big, pool=(8, 8), o=O + 8) == L.STATUS["VDSA_ERR_ALIGN"]
+    assert 2 * 24 * 21 * 17 * 30 * 128 * 2 <= L.STATIC_SCRATCH_BYTES
+    p = prob()
+    assert g(p, pool=(0, 4)) == L.STATUS["VDSA_ERR_WINDOW"]
+    assert g(p, o=None) == L.STATUS["VDSA_ERR_NULL"]
+    assert g(p, lse=LSE + 2) == L.STATUS["VDSA_ERR_ALIGN"]
+    assert g(p, o=Q) == L.STATUS["VDSA_ERR_ALIAS"]

@@ -1,7 +1,9 @@
 """Tile-window sparse attention for video latents on MI355X (gfx950).
 
 Python face of libvdsa.so: the three calls of the hot path
-(``sta_attn_fwd``, ``global_pooled_attn_fwd``, ``dual_branch_merge``), the
+(``sta_attn_fwd``, ``global_pooled_attn_fwd``, ``dual_branch_merge``), the global
+branch on the library's static scratch for callers that cannot allocate
+(``global_pooled_attn_fwd_noalloc``), the
 exact log-sum-exp merge (``dual_branch_merge_lse``), the global branch with
 either merge fused into it (``global_pooled_attn_merge_fwd``), the pooling
 step alone (``kv_avgpool_fwd``), UltraGen's hierarchical and compressed
@@ -21,6 +23,7 @@ from ._lib import (  # noqa: F401
     global_flops,
     hier_flops,
     global_pooled_attn_fwd,
+    global_pooled_attn_fwd_noalloc,
     global_pooled_attn_merge_fwd,
     global_pooled_attn_bwd,
     global_pooled_attn_workspace_size,

@@ -27,7 +27,7 @@ STATUS = {v: k for k, v in STATUS_NAMES.items()}
 # every symbol include/vdsa.h declares
 EXPORTED = [
     "sta_attn_fwd", "global_pooled_attn_workspace_size", "global_pooled_attn_fwd",
-    "dual_branch_merge", "dual_branch_merge_lse", "global_pooled_attn_merge_fwd",
+    "global_pooled_attn_fwd_noalloc", "dual_branch_merge", "dual_branch_merge_lse", "global_pooled_attn_merge_fwd",
     "hier_pooled_attn_workspace_size", "hier_pooled_attn_fwd", "compressed_global_attn_workspace_size",
     "compressed_global_attn_fwd",
     "sta_attn_bwd_workspace_size", "sta_attn_bwd", "global_pooled_attn_bwd_workspace_size",
@@ -82,6 +82,7 @@ def lib() -> ctypes.CDLL:
     L.sta_attn_fwd.argtypes = [P, C, vp, S, vp, S, vp, S, vp, S, fp, vp]
     L.global_pooled_attn_workspace_size.argtypes = [P, i32p, ctypes.POINTER(ctypes.c_size_t)]
     L.global_pooled_attn_fwd.argtypes = [P, i32p, vp, S, vp, S, vp, S, vp, S, fp, vp, ctypes.c_size_t, vp]
+    L.global_pooled_attn_fwd_noalloc.argtypes = [P, i32p, vp, S, vp, S, vp, S, vp, S, fp, vp]
     L.dual_branch_merge.argtypes = [P, vp, S, vp, S, fp, fp, vp, S, vp]
     L.dual_branch_merge_lse.argtypes = [P, vp, S, fp, vp, S, fp, vp, S, fp, vp]
     L.global_pooled_attn_merge_fwd.argtypes = [P, i32p, vp, S, vp, S, vp, S, ctypes.c_int, vp, S, fp, fp, fp,
@@ -317,6 +318,29 @@ def global_pooled_attn_fwd(q, k, v, grid, pool_hw, scale=None, out=None, lse=Non
         o.data_ptr(), ctypes.byref(_strides(o)), _ptr(lse),
         workspace.data_ptr(), _nbytes(workspace), _stream(stream)))
     return (o, lse) if (return_lse or lse is not None) else o
+
+
+# bytes of the static device scratch behind global_pooled_attn_fwd_noalloc
+STATIC_SCRATCH_BYTES = 128 << 20
+
+
+def global_pooled_attn_fwd_noalloc(q, k, v, grid, pool_hw, out, lse=None, scale=None, stream=None):
+    """The global branch with pooled K/V in the library's static device
+    scratch (``global_pooled_attn_fwd_noalloc``): nothing is allocated, so
+    ``out`` (and ``lse`` if wanted) must be given.  Calls that overlap in time
+    on one GPU share that scratch and race.  Returns ``out``."""
+    _same(q, k, v)
+    prob = _problem_for(q, grid, scale)
+    if out is None:
+        raise ValueError("out is required: this entry point allocates nothing")
+    o = _out_like(q, out)
+    lse = _lse_buf(q, lse, False)
+    _on_device(q, k, v, o, lse)
+    check(lib().global_pooled_attn_fwd_noalloc(
+        ctypes.byref(prob), _pool(pool_hw), q.data_ptr(), ctypes.byref(_strides(q)),
+        k.data_ptr(), ctypes.byref(_strides(k)), v.data_ptr(), ctypes.byref(_strides(v)),
+        o.data_ptr(), ctypes.byref(_strides(o)), _ptr(lse), _stream(stream)))
+    return o
 
 
 def dual_branch_merge(o_local, o_global, w_global, w_local=None, out=None, stream=None):

@@ -621,6 +621,36 @@ vdsa_status global_pooled_attn_fwd(const vdsa_problem* prob, const int32_t pool_
                           workspace_bytes, FusedMerge{}, stream);
 }
 
+vdsa_status global_pooled_attn_fwd_noalloc(const vdsa_problem* prob, const int32_t pool_hw[2], const void* q,
+                                           const vdsa_strides* q_strides, const void* k,
+                                           const vdsa_strides* k_strides, const void* v,
+                                           const vdsa_strides* v_strides, void* o, const vdsa_strides* o_strides,
+                                           float* lse, void* stream) {
+  vdsa_status s;
+  if ((s = check_problem(prob)) != VDSA_OK) return s;
+  if ((s = check_pool(prob, pool_hw)) != VDSA_OK) return s;
+  const size_t need = 2 * pooled_bytes(prob, pool_hw);
+  if (need > vdsa::STATIC_SCRATCH_BYTES)
+    return fail(VDSA_ERR_WORKSPACE, "pooled K and V need %zu bytes, beyond the %zu-byte static scratch", need,
+                vdsa::STATIC_SCRATCH_BYTES);
+  // every argument check before the scratch lookup (the first HIP call);
+  // global_attn_impl repeats them and adds the aliasing checks
+  const int64_t N = n_tokens(prob);
+  View vq{"q", q, q_strides, N}, vk{"k", k, k_strides, N}, vv{"v", v, v_strides, N}, vo{"o", o, o_strides, N};
+  for (View* vw : {&vq, &vk, &vv})
+    if ((s = check_view(prob, *vw, false)) != VDSA_OK) return s;
+  if ((s = check_view(prob, vo, true)) != VDSA_OK) return s;
+  uintptr_t l0, l1;
+  if ((s = check_lse(prob, lse, l0, l1)) != VDSA_OK) return s;
+  for (const View* in : {&vq, &vk, &vv})
+    if (overlaps(vo.lo, vo.hi, in->lo, in->hi)) return fail(VDSA_ERR_ALIAS, "o overlaps %s", in->name);
+  void* scratch = nullptr;
+  const hipError_t e = vdsa::static_scratch(&scratch);
+  if (e != hipSuccess) return fail(VDSA_ERR_HIP, "static scratch address: %s", hipGetErrorString(e));
+  return global_attn_impl(prob, pool_hw, q, q_strides, k, k_strides, v, v_strides, o, o_strides, lse, scratch,
+                          vdsa::STATIC_SCRATCH_BYTES, FusedMerge{}, stream);
+}
+
 vdsa_status global_pooled_attn_merge_fwd(const vdsa_problem* prob, const int32_t pool_hw[2], const void* q,
                                          const vdsa_strides* q_strides, const void* k, const vdsa_strides* k_strides,
                                          const void* v, const vdsa_strides* v_strides, vdsa_merge_mode mode,

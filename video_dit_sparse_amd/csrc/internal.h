@@ -196,6 +196,13 @@ struct UpsampleParams {
   int32_t T, H, W, Hp, Wp;
 };
 
+// The static device scratch of the entry point that allocates nothing
+// (scratch.hip): STATIC_SCRATCH_BYTES on every device, 256-byte aligned.
+// static_scratch() returns the current device's copy, resolving its address
+// with hipGetSymbolAddress on the first call for that device.
+constexpr size_t STATIC_SCRATCH_BYTES = size_t(128) << 20;
+hipError_t static_scratch(void** ptr);
+
 // Launchers: return hipSuccess or the launch error.  They assume the
 // parameters were validated.
 hipError_t launch_box_attn_bf16(const BoxAttnParams& p, int head_dim, hipStream_t stream);
