@@ -101,7 +101,7 @@ def _cpu_tile(job):
     return 4.0 * qh.shape[1] * len(rows) * nkeys
 
 
-def cpu_baseline(w, q, k, v, budget_s: float, n_heads: int = 4):
+def cpu_baseline(w, q, k, v, budget_s: float, n_heads: int = 6):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     whole query tiles of ``n_heads`` seeded heads, in a seeded random order,
     over a pool of worker processes (one per core of the host's CPU share,
