@@ -56,6 +56,9 @@ SMALL_STA = [
     ("tile384_self_shift_bf16", (12, 16, 16), (6, 8, 8), (1, 1, 1), (3, 4, 4), 2, 128, "bf16"),
     ("tile192_bf16", (6, 16, 24), (3, 8, 8), (3, 3, 3), (0, 0, 0), 2, 128, "bf16"),
     ("tile192_shift_bf16", (7, 12, 20), (3, 8, 8), (1, 3, 1), (1, 4, 4), 1, 128, "bf16"),
+    # 256-token tiles (the 2K workload's tile), plain and shifted with ragged edges
+    ("tile256_bf16", (8, 16, 24), (4, 8, 8), (3, 1, 3), (0, 0, 0), 2, 128, "bf16"),
+    ("tile256_shift_ragged_bf16", (9, 19, 21), (4, 8, 8), (1, 3, 3), (2, 4, 4), 1, 128, "bf16"),
 ]
 
 
@@ -212,6 +215,10 @@ def test_heads_permute():
     op = V.sta_attn_fwd(q[:, perm].contiguous(), k[:, perm].contiguous(), v[:, perm].contiguous(), grid, tile, window)
     torch.cuda.synchronize()
     assert torch.equal(o[:, perm], op)
+    # and every head of the permuted call against the oracle of the head it came from
+    for i, hsrc in enumerate(perm):
+        ro, _ = R.sta_ref(head_f64(q, 0, hsrc), head_f64(k, 0, hsrc), head_f64(v, 0, hsrc), grid, tile, window)
+        compare(op[0, i].cpu(), ro, "bf16", f"permuted head {i} (from {hsrc})")
 
 
 SMALL_GLOBAL = [

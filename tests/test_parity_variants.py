@@ -68,6 +68,11 @@ def test_hier_pooled_bnhd_strides():
     o2 = V.hier_pooled_attn_fwd(q.contiguous(), k.contiguous(), v.contiguous(), grid, tile, window, pool)
     torch.cuda.synchronize()
     assert torch.equal(o, o2)
+    # the BNHD call against the oracle, head by head
+    for h in range(2):
+        ro, _ = R.hier_pooled_ref(head_f64(q, 0, h), head_f64(k, 0, h), head_f64(v, 0, h), grid, tile, window,
+                                  (0, 0, 0), pool, scale=128 ** -0.5)
+        compare(o[0, h].cpu(), ro, "bf16", f"hier BNHD h{h}")
 
 
 COMP = [
