@@ -207,6 +207,11 @@ vdsa_status launch_attn(const vdsa_problem* prob, vdsa::BoxAttnParams& bp, hipSt
     return fail(VDSA_ERR_SHAPE, "problem needs %lld workgroups, beyond the launch limit", (long long)total);
   bp.total_wg = (int32_t)total;
   bp.scale_log2e = prob->scale * 1.4426950408889634f;
+  bp.fd_qblocks = vdsa::make_fastdiv((uint32_t)bp.qblocks);
+  bp.fd_tiles = vdsa::make_fastdiv((uint32_t)(bp.nT * bp.nH * bp.nW));
+  bp.fd_heads = vdsa::make_fastdiv((uint32_t)bp.heads);
+  bp.fd_nw = vdsa::make_fastdiv((uint32_t)bp.nW);
+  bp.fd_nh = vdsa::make_fastdiv((uint32_t)bp.nH);
   hipError_t e;
   if (prob->dtype == VDSA_F32)
     e = vdsa::launch_box_attn_f32(bp, prob->head_dim, stream);

@@ -14,9 +14,12 @@
 // Per 64-key block and wave (32 queries):
 //   S^T = K Q^T      (keys x queries; K from LDS, Q^T resident in registers)
 //   online softmax   (fp32, v_exp_f32 with scale*log2(e) folded into one FMA;
-//                     row statistics live in one lane pair, so the only
+//                     row maxima live in one lane pair, so the only
 //                     cross-lane step is one exchange with lane ^ 32)
-//   O^T += V^T P^T   (P^T taken straight from the S^T accumulators)
+//   O^T += V^T P^T   (P^T taken straight from the S^T accumulators) and the
+//                     denominators: an all-ones A operand times P^T sums the
+//                     probabilities exactly as rounded to bf16 for the
+//                     product, so a weight's rounding cancels in O
 // Both products keep the query index on the MFMA column (= lane % 32), which
 // is what lets the softmax statistics and the output rescale stay per lane.
 //
@@ -86,17 +89,21 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
   const int g = lane >> 5;
 
   // ---- which (batch, head, query tile, query block) this workgroup owns
-  const int wg = xcd_remap(blockIdx.x, p.total_wg);
-  const int qblk = wg % p.qblocks;
-  const int rest = wg / p.qblocks;
-  const int ntiles = p.nT * p.nH * p.nW;
-  const int tile = rest % ntiles;
-  const int bh = rest / ntiles;
-  const int h = bh % p.heads;
-  const int b = bh / p.heads;
+  // (divisions by invariants the host prepared)
+  const uint32_t wg = (uint32_t)xcd_remap(blockIdx.x, p.total_wg);
+  const uint32_t rest = fast_div(wg, p.fd_qblocks);
+  const int qblk = (int)(wg - rest * p.fd_qblocks.d);
+  const uint32_t bh = fast_div(rest, p.fd_tiles);
+  const uint32_t tile = rest - bh * p.fd_tiles.d;
+  const int b = (int)fast_div(bh, p.fd_heads);
+  const int h = (int)(bh - (uint32_t)b * p.fd_heads.d);
 
   Box qb, kb;
-  tile_boxes(p, tile, qb, kb);
+  {
+    const uint32_t tw = fast_div(tile, p.fd_nw);
+    const uint32_t at = fast_div(tw, p.fd_nh);
+    tile_boxes_at(p, (int)at, (int)(tw - at * p.fd_nh.d), (int)(tile - tw * p.fd_nw.d), qb, kb);
+  }
   const int qvol = qb.et * qb.eh * qb.ew;
   const int q0 = qblk * BLOCK_M;
   if (q0 >= qvol) return;  // uniform over the workgroup
@@ -120,13 +127,14 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
   const bool q_valid = jq < qvol;
   uint32_t qtok;
   {
-    const int j = min(jq, qvol - 1);
-    const int plane = qb.eh * qb.ew;
-    const int jt = j / plane;
-    const int r = j - jt * plane;
-    const int jh = r / qb.ew;
-    const int jw = r - jh * qb.ew;
-    qtok = q_token(p, qb.t0 + jt, qb.h0 + jh, qb.w0 + jw);
+    const FastDiv fq_plane = make_fastdiv_fp64((uint32_t)(qb.eh * qb.ew));
+    const FastDiv fq_row = make_fastdiv_fp64((uint32_t)qb.ew);
+    const uint32_t j = (uint32_t)min(jq, qvol - 1);
+    const uint32_t jt = fast_div(j, fq_plane);
+    const uint32_t r = j - jt * fq_plane.d;
+    const uint32_t jh = fast_div(r, fq_row);
+    const uint32_t jw = r - jh * fq_row.d;
+    qtok = q_token(p, qb.t0 + (int)jt, qb.h0 + (int)jh, qb.w0 + (int)jw);
   }
   bf16x8 qf[KSTEPS];
   {
@@ -136,8 +144,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
   }
 
   // ---- key box addressing: key j -> token, via two divisions by invariants
-  const FastDiv fd_plane = make_fastdiv((uint32_t)(kb.eh * kb.ew));
-  const FastDiv fd_row = make_fastdiv((uint32_t)kb.ew);
+  const FastDiv fd_plane = make_fastdiv_fp64((uint32_t)(kb.eh * kb.ew));
+  const FastDiv fd_row = make_fastdiv_fp64((uint32_t)kb.ew);
   auto key_token = [&](int j) -> uint32_t {
     j = min(j, kvol - 1);   // keys past the box repeat the last key; masked later
     const uint32_t jt = fast_div((uint32_t)j, fd_plane);
@@ -206,7 +214,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
 #pragma unroll
   for (int i = 0; i < NB; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY;   // running max of scale*log2(e)*logit
-  float l_run = 0.f;         // this lane's share of the running denominator
+  f32x16 lacc = f32x16{};    // row sums of P: every register holds the lane's query's sum
+  bf16x8 ones8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones8[e] = (__bf16)1.f;
   const float c = p.scale_log2e;
 
   load_block(0, 0);
@@ -257,7 +268,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
     if (__builtin_amdgcn_ballot_w64(mx > m_run + RESCALE_MARGIN)) {
       const float m_new = fmaxf(m_run, mx);
       const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= corr;
+      lacc *= corr;
 #pragma unroll
       for (int i = 0; i < NB; ++i) oacc[i] *= corr;
       m_run = m_new;
@@ -265,7 +276,6 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
     const float m_new = m_run;
     const int nvalid = PARTIAL ? kvol - blk * BLOCK_N : BLOCK_N;
     bf16x8 pf[4];
-    float lsum = 0.f;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
@@ -278,13 +288,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
           if constexpr (PARTIAL) {
             if (32 * sb + 16 * hlf + 8 * g + e >= nvalid) pv = 0.f;
           }
-          lsum += pv;
           pk[e] = (__bf16)pv;
         }
         pf[2 * sb + hlf] = pk;
       }
     }
-    l_run += lsum;
 
     // O^T += V^T P^T
     const char* vst = lds + stage * STAGE + K_STAGE;
@@ -295,6 +303,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
         const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(vst + v_rd[kc] + nb * 1024));
         oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kc], oacc[nb], 0, 0, 0);
       }
+      // the softmax denominator over the weights exactly as rounded for the
+      // product: an all-ones A operand sums each query's column of P^T
+      lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones8, pf[kc], lacc, 0, 0, 0);
     }
 
     if (more) store_v(stage ^ 1);
@@ -310,7 +321,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
   // ---- epilogue: normalise and store (lane owns query l32; register v of
   // block nb holds head_dim index 32*nb + 8*(v/4) + 4*g + v%4); with a merge,
   // the row combines with the other branch's row read at the same positions
-  const float l_tot = xhalf_sum(l_run);
+  const float l_tot = lacc[0];
   const float inv = 1.f / l_tot;
   if (q_valid) {
     float lse_row = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;

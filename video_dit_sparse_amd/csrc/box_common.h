@@ -110,10 +110,10 @@ __device__ __forceinline__ uint32_t box_key_token24(const BoxAttnParams& p, cons
   return __umul24(__umul24(t, (uint32_t)p.kH) + h, (uint32_t)p.kW) + w;
 }
 
-__device__ __forceinline__ void tile_boxes(const BoxAttnParams& p, int tile, Box& qb, Box& kb) {
-  const int aw = tile % p.nW;
-  const int ah = (tile / p.nW) % p.nH;
-  const int at = tile / (p.nW * p.nH);
+// Query box of tile (at, ah, aw) of the lattice and the box of its keys.
+// (PT: BoxAttnParams, in whichever address space the caller reads it from.)
+template <class PT>
+__device__ __forceinline__ void tile_boxes_at(const PT& p, int at, int ah, int aw, Box& qb, Box& kb) {
   auto span = [](int a, int b, int s, int L, int& lo, int& ext) {
     lo = max(0, a * b - s);
     ext = min(L, (a + 1) * b - s) - lo;
@@ -146,6 +146,10 @@ __device__ __forceinline__ void tile_boxes(const BoxAttnParams& p, int tile, Box
       cells(p.kpW, kb.w0, kb.ew);
     }
   }
+}
+
+__device__ __forceinline__ void tile_boxes(const BoxAttnParams& p, int tile, Box& qb, Box& kb) {
+  tile_boxes_at(p, tile / (p.nW * p.nH), (tile / p.nW) % p.nH, tile % p.nW, qb, kb);
 }
 
 

@@ -21,6 +21,23 @@ __host__ __device__ inline FastDiv make_fastdiv(uint32_t d) {
   return FastDiv{d, uint32_t(m), s};
 }
 
+// The same constants for 1 <= d <= 2^31 without a 64-bit integer division
+// (which kernels would expand into a long instruction sequence).  With
+// r = 2^s - d < d, m - 1 = floor(r 2^32 / d) < 2^32.  r 2^32 (at most 32
+// significant bits) and d are exact in double precision and the quotient is
+// correctly rounded (error below 2^-21), so the truncated quotient is the
+// floor or one off it; the integer check q d <= r 2^32 < (q + 1) d, whose
+// products stay below 2^64, corrects it.
+__host__ __device__ inline FastDiv make_fastdiv_fp64(uint32_t d) {
+  uint32_t s = 0;
+  while ((uint32_t(1) << s) < d) ++s;
+  const uint64_t num = (uint64_t)((uint32_t(1) << s) - d) << 32;
+  uint64_t q = (uint64_t)((double)num / (double)d);
+  if (q * d > num) --q;
+  else if ((q + 1) * d <= num) ++q;
+  return FastDiv{d, uint32_t(q + 1), s};
+}
+
 // Per-dim description of the query tiling and of where the keys come from.
 //
 // Query side: the query grid (qT, qH, qW) is cut into tiles of (bT, bH, bW)
@@ -64,6 +81,9 @@ struct BoxAttnParams {
   const float* lse_l;         // MERGE_LSE: other branch LSE, [batch, heads, N] contiguous
   const float* w_l;           // MERGE_GATED: weight of ol per head (nullable => 1)
   const float* w_g;           // MERGE_GATED: weight of this kernel's output per head
+  // Division by invariants for decoding a work-item index (set by the host):
+  // by qblocks, by the tile count nT*nH*nW, by heads, by nW and by nH.
+  FastDiv fd_qblocks, fd_tiles, fd_heads, fd_nw, fd_nh;
 };
 enum { MERGE_NONE = 0, MERGE_GATED = 1, MERGE_LSE = 2 };
 
