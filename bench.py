@@ -28,8 +28,8 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0
 NOMINAL_CLOCK_MHZ = 2400.0   # the clock the published bf16 peak assumes
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "sta_bf16_720p_counters.md")
-# 384-token (6x8x8) tiles at head_dim 128 run the 8-wave kernel of attn_bf16_pp.hip
-ROOFLINE_KERNEL = "box_attn_bf16_pp_kernel"
+# the 720P workload's 384-token (6x8x8) tiles at head_dim 128 run the 8-wave
+# kernel of attn_bf16_pp.hip; its traffic counters are tied to these sources
 KERNEL_SOURCES = [os.path.join(ROOT, "video_dit_sparse_amd", "csrc", f)
                   for f in ("attn_bf16_pp.hip", "box_common.h", "internal.h")]
 
@@ -274,7 +274,9 @@ def main():
     traffic = measured_traffic() if w.name == "sta_720p" else None
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": ROOFLINE_KERNEL, "launch_ms": round(launch_ms, 4),
+                "kernel": V.sta_kernel_name(w.batch, w.heads, w.head_dim, w.grid, w.tile, w.window, w.shifts[0],
+                                            dtype=w.dtype),
+                "launch_ms": round(launch_ms, 4),
                 "flop_per_launch": launch_flops,
                 "per_call_ms": {"n": len(per_call), "median": round(per_call[len(per_call) // 2], 4),
                                 "min": round(per_call[0], 4)}}

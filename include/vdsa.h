@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define VDSA_ABI_VERSION 4
+#define VDSA_ABI_VERSION 5
 
 typedef enum {
   VDSA_OK = 0,
@@ -411,6 +411,14 @@ vdsa_status vdsa_global_flops(const vdsa_problem* prob, const int32_t pool_hw[2]
 vdsa_status vdsa_hier_flops(const vdsa_problem* prob, const vdsa_sta_cfg* cfg, const int32_t pool_hw[2],
                             double* flops);
 vdsa_status vdsa_compressed_global_flops(const vdsa_problem* prob, const int32_t pool_hw[2], double* flops);
+
+/* Name of the kernel sta_attn_fwd launches for this problem and
+ * configuration: the host picks among the attention kernels by head_dim and
+ * by the largest query tile's token count (384-, 192- or 128-query
+ * workgroups, whichever pads the tiles least; fp32 inputs take the fp32
+ * kernel).  A static string; NULL, with vdsa_last_error set, when prob or
+ * cfg is invalid.  Host only. */
+const char* vdsa_sta_kernel(const vdsa_problem* prob, const vdsa_sta_cfg* cfg);
 
 const char* vdsa_status_string(vdsa_status s);
 const char* vdsa_last_error(void);   /* thread-local detail of the last failed call */

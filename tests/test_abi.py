@@ -32,9 +32,30 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert L.abi_version() == 4
+    assert L.abi_version() == 5
     for code in L.STATUS_NAMES:
         assert L.lib().vdsa_status_string(code)
+
+
+def test_kernel_choice_per_workload():
+    # the kernel sta_attn_fwd launches, by the largest query tile's token count
+    # (and dtype / head_dim): the workloads' tiles and two edge cases
+    from video_dit_sparse_amd import workloads as WL
+    want = {"tiny_f32": "box_attn_f32_kernel<64>", "sta_720p": "box_attn_bf16_pp_kernel",
+            "dual_1080p": "box_attn_bf16_pp_kernel", "local_global_4k": "box_attn_bf16_m16_kernel<4>",
+            "cross_window_2k": "box_attn_bf16_kernel<128>"}
+    for name, kernel in want.items():
+        w = WL.WORKLOADS[name]
+        for s in w.shifts:
+            assert L.sta_kernel_name(w.batch, w.heads, w.head_dim, w.grid, w.tile, w.window, s,
+                                     dtype=w.dtype) == kernel, (name, s)
+    # head_dim 64 always takes the 128-query kernel; a 384-token tile in a
+    # grid that clips it to 40 tokens pads a 384-query block by far more than
+    # 1/8, so the 128-query kernel takes it
+    assert L.sta_kernel_name(1, 2, 64, (12, 16, 24), (6, 8, 8), (1, 3, 3)) == "box_attn_bf16_kernel<64>"
+    assert L.sta_kernel_name(1, 2, 128, (5, 1, 8), (6, 8, 8), (1, 1, 1)) == "box_attn_bf16_kernel<128>"
+    with pytest.raises(ValueError, match="window"):
+        L.sta_kernel_name(1, 2, 128, (4, 8, 8), (2, 4, 4), (2, 3, 3))
 
 
 # fake, 256-aligned device addresses: validation fails before any use

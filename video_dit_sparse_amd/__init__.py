@@ -34,4 +34,5 @@ from ._lib import (  # noqa: F401
     sta_attn_bwd,
     sta_attn_bwd_workspace_size,
     sta_flops,
+    sta_kernel_name,
 )

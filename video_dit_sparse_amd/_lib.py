@@ -33,7 +33,7 @@ EXPORTED = [
     "sta_attn_bwd_workspace_size", "sta_attn_bwd", "global_pooled_attn_bwd_workspace_size",
     "global_pooled_attn_bwd",
     "kv_avgpool_fwd", "vdsa_sta_flops", "vdsa_global_flops", "vdsa_hier_flops", "vdsa_compressed_global_flops",
-    "vdsa_status_string", "vdsa_last_error", "vdsa_abi_version",
+    "vdsa_status_string", "vdsa_last_error", "vdsa_abi_version", "vdsa_sta_kernel",
 ]
 VDSA_MERGE_GATED, VDSA_MERGE_LSE = 0, 1
 MERGE_MODES = {"gated": VDSA_MERGE_GATED, "lse": VDSA_MERGE_LSE}
@@ -107,6 +107,8 @@ def lib() -> ctypes.CDLL:
     L.vdsa_last_error.argtypes = []
     L.vdsa_last_error.restype = ctypes.c_char_p
     L.vdsa_abi_version.argtypes = []
+    L.vdsa_sta_kernel.argtypes = [P, C]
+    L.vdsa_sta_kernel.restype = ctypes.c_char_p
     for name in ("sta_attn_fwd", "global_pooled_attn_workspace_size", "global_pooled_attn_fwd",
                  "dual_branch_merge", "kv_avgpool_fwd", "vdsa_sta_flops", "vdsa_global_flops",
                  "vdsa_abi_version"):
@@ -529,6 +531,20 @@ def sta_flops(batch, heads, head_dim, grid, tile, window, shift=(0, 0, 0), windo
     f = ctypes.c_double()
     check(lib().vdsa_sta_flops(ctypes.byref(prob), ctypes.byref(cfg), ctypes.byref(f)))
     return f.value
+
+
+def sta_kernel_name(batch, heads, head_dim, grid, tile, window, shift=(0, 0, 0), window_mode: str = "clip",
+                    dtype: str = "bf16") -> str:
+    """Name of the kernel sta_attn_fwd launches for this configuration
+    (``vdsa_sta_kernel``; host only).  dtype: "bf16" or "f32"."""
+    if dtype not in ("bf16", "f32"):
+        raise ValueError(f"dtype must be 'bf16' or 'f32', got {dtype!r}")
+    prob = make_problem(batch, heads, head_dim, grid, VDSA_BF16 if dtype == "bf16" else VDSA_F32, 1.0)
+    cfg = make_cfg(tile, window, shift, window_mode)
+    name = lib().vdsa_sta_kernel(ctypes.byref(prob), ctypes.byref(cfg))
+    if name is None:
+        raise ValueError(lib().vdsa_last_error().decode())
+    return name.decode()
 
 
 def global_flops(batch, heads, head_dim, grid, pool_hw) -> float:

@@ -195,9 +195,25 @@ Bf16Shape choose_bf16_shape(int64_t max_tile_vol, int head_dim) {
   return best;
 }
 
+// Largest number of real tokens in one query tile of bp's lattice.
+int64_t max_tile_volume(const vdsa::BoxAttnParams& bp) {
+  return (int64_t)max_tile_extent(bp.qT, bp.bT, bp.sT) * max_tile_extent(bp.qH, bp.bH, bp.sH) *
+         max_tile_extent(bp.qW, bp.bW, bp.sW);
+}
+
+// Name of the kernel launch_attn runs for bp (the same choice, no launch).
+const char* attn_kernel_name(const vdsa_problem* prob, const vdsa::BoxAttnParams& bp) {
+  const bool d128 = prob->head_dim == 128;
+  if (prob->dtype == VDSA_F32) return d128 ? "box_attn_f32_kernel<128>" : "box_attn_f32_kernel<64>";
+  switch (choose_bf16_shape(max_tile_volume(bp), prob->head_dim).kernel) {
+    case K_PP_8W: return "box_attn_bf16_pp_kernel";
+    case K_M16_4W: return "box_attn_bf16_m16_kernel<4>";
+    default: return d128 ? "box_attn_bf16_kernel<128>" : "box_attn_bf16_kernel<64>";
+  }
+}
+
 vdsa_status launch_attn(const vdsa_problem* prob, vdsa::BoxAttnParams& bp, hipStream_t stream) {
-  const int64_t mv = (int64_t)max_tile_extent(bp.qT, bp.bT, bp.sT) * max_tile_extent(bp.qH, bp.bH, bp.sH) *
-                     max_tile_extent(bp.qW, bp.bW, bp.sW);
+  const int64_t mv = max_tile_volume(bp);
   Bf16Shape shape{vdsa::box_attn_f32_block_m(), K_M32};
   if (prob->dtype == VDSA_BF16) shape = choose_bf16_shape(mv, prob->head_dim);
   bp.qblocks = (int32_t)((mv + shape.block_m - 1) / shape.block_m);
@@ -542,6 +558,16 @@ vdsa_status check_pooled_call(const vdsa_problem* prob, const int32_t* pool_hw, 
 extern "C" {
 
 int vdsa_abi_version(void) { return VDSA_ABI_VERSION; }
+
+const char* vdsa_sta_kernel(const vdsa_problem* prob, const vdsa_sta_cfg* cfg) {
+  if (check_problem(prob) != VDSA_OK || check_sta_cfg(cfg) != VDSA_OK) return nullptr;
+  vdsa::BoxAttnParams bp{};
+  bp.batch = prob->batch;
+  bp.heads = prob->heads;
+  set_sta_geometry(bp, prob, cfg);
+  ok();
+  return attn_kernel_name(prob, bp);
+}
 
 const char* vdsa_status_string(vdsa_status s) {
   switch (s) {
