@@ -41,14 +41,23 @@ def test_kernel_choice_per_workload():
     # the kernel sta_attn_fwd launches, by the largest query tile's token count
     # (and dtype / head_dim): the workloads' tiles and two edge cases
     from video_dit_sparse_amd import workloads as WL
-    want = {"tiny_f32": "box_attn_f32_kernel<64>", "sta_720p": "box_attn_bf16_pp_kernel",
-            "dual_1080p": "box_attn_bf16_pp_kernel", "local_global_4k": "box_attn_bf16_m16_kernel<4>",
+    want = {"tiny_f32": "box_attn_f32_kernel<64>", "sta_720p": "box_attn_bf16_pp_kernel<1>",
+            "dual_1080p": "box_attn_bf16_pp_kernel<0>", "local_global_4k": "box_attn_bf16_m16_kernel<4>",
             "cross_window_2k": "box_attn_bf16_kernel<128>"}
     for name, kernel in want.items():
         w = WL.WORKLOADS[name]
         for s in w.shifts:
             assert L.sta_kernel_name(w.batch, w.heads, w.head_dim, w.grid, w.tile, w.window, s,
                                      dtype=w.dtype) == kernel, (name, s)
+    # the 384-query kernel's key walk: tile by tile when every tile is full and
+    # a tile frame is 64 tokens (on the rolled grid for the cyclic mode), else
+    # raster (a lattice shift makes edge tiles partial; so does a ragged grid)
+    g720, t720, w720 = (30, 48, 80), (6, 8, 8), (3, 3, 5)
+    assert L.sta_kernel_name(1, 24, 128, g720, t720, w720, (3, 4, 4), "cyclic") == "box_attn_bf16_pp_kernel<2>"
+    assert L.sta_kernel_name(1, 24, 128, g720, t720, w720, (0, 0, 0), "inward") == "box_attn_bf16_pp_kernel<1>"
+    assert L.sta_kernel_name(1, 24, 128, g720, t720, w720, (3, 4, 4)) == "box_attn_bf16_pp_kernel<0>"
+    assert L.sta_kernel_name(1, 24, 128, (30, 48, 81), t720, w720) == "box_attn_bf16_pp_kernel<0>"
+    assert L.sta_kernel_name(1, 24, 128, (30, 48, 80), (6, 4, 16), w720) == "box_attn_bf16_pp_kernel<1>"
     # head_dim 64 always takes the 128-query kernel; a 384-token tile in a
     # grid that clips it to 40 tokens pads a 384-query block by far more than
     # 1/8, so the 128-query kernel takes it

@@ -190,6 +190,37 @@ def test_sta_deterministic_and_no_stray_writes():
     compare(o.reshape(4, N, 128).cpu(), ro, "bf16", "batch 2")
 
 
+TILE_WALK = [
+    # name, grid, tile, window, shift, mode, walk: every tile full and a tile
+    # frame of 64 tokens, so the 384-query kernel walks the key boxes tile by
+    # tile (walk 1), on the rolled grid in the cyclic mode (walk 2)
+    ("whole_tiles", (12, 16, 24), (6, 8, 8), (3, 3, 3), (0, 0, 0), "clip", 1),
+    ("whole_tiles_4x16", (6, 8, 32), (6, 4, 16), (1, 3, 3), (0, 0, 0), "clip", 1),
+    ("whole_tiles_inward", (12, 16, 40), (6, 8, 8), (1, 1, 3), (0, 0, 0), "inward", 1),
+    ("rolled_whole_tiles", (12, 16, 24), (6, 8, 8), (3, 3, 5), (3, 4, 4), "cyclic", 2),
+]
+
+
+@pytest.mark.parametrize("case", TILE_WALK, ids=[c[0] for c in TILE_WALK])
+def test_tile_walk_bnhd_batch2(case):
+    """The 384-query kernel's tile-by-tile key walks on batch 2, 2 heads,
+    token-major [B, N, heads, D] inputs, with LSE, against the oracle."""
+    name, grid, tile, window, shift, mode, walk = case
+    assert V.sta_kernel_name(2, 2, 128, grid, tile, window, shift, mode) == f"box_attn_bf16_pp_kernel<{walk}>"
+    say(f"[tile walk] {name}")
+    N = int(np.prod(grid))
+    q, k, v = [WL.make_tensor((2, 2, N, 128), torch.bfloat16, DEV, seed=1500 + i) for i in range(3)]
+    qb, kb, vb = [x.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3) for x in (q, k, v)]
+    o, lse = V.sta_attn_fwd(qb, kb, vb, grid, tile, window, shift, return_lse=True, window_mode=mode)
+    torch.cuda.synchronize()
+    for b in range(2):
+        for h in range(2):
+            ro, rl = R.sta_ref(head_f64(q, b, h), head_f64(k, b, h), head_f64(v, b, h), grid, tile, window, shift,
+                               scale=128 ** -0.5, window_mode=mode)
+            compare(o[b, h].cpu(), ro, "bf16", f"{name} b{b} h{h}")
+            compare(lse[b, h].cpu(), rl, "bf16", f"{name} lse b{b} h{h}")
+
+
 def test_reference_raise_pass():
     """Keys late in each key box whose logits jump far above the first keys'
     seen: the kernel must raise its softmax reference and repeat the walk."""

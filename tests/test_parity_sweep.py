@@ -6,7 +6,9 @@ draws grids, tiles, windows, lattice shifts, window modes, batch, heads,
 head_dim, dtype and with / without LSE from a fixed seed, so that the kernels'
 tile decode, box walk, partial blocks and edge tiles meet combinations nobody
 chose.  Tiles are drawn from families whose token counts send the call to each
-attention kernel (384-, 192- and 128-query bf16, head_dim 64, fp32); the CPU
+attention kernel (384-, 192- and 128-query bf16, head_dim 64, fp32; for the
+384-query kernel half the draws are whole-tile lattices, which it walks tile by
+tile); the CPU
 test checks, with the library's own selection (``vdsa_sta_kernel``), that the
 sweep reaches every kernel several times.  Sizes stay small enough for the
 oracle to finish each case in about a second.  The backward sweep draws from
@@ -46,15 +48,23 @@ def draw_cases(n, seed, max_tokens):
         if D is None:
             D = int(rng.choice([64, 128]))
         tile = tiles[int(rng.integers(len(tiles)))]
+        # half the 384-token draws: whole tiles and no lattice shift, where the
+        # 384-query kernel walks its key boxes tile by tile
+        whole = fam == "t384" and rng.random() < 0.5
         while True:
             # each dim holds at least one full tile and up to about three
-            grid = tuple(int(rng.integers(b, 3 * b + 3)) for b in tile)
+            if whole:
+                grid = tuple(b * int(rng.integers(1, 4)) for b in tile)
+            else:
+                grid = tuple(int(rng.integers(b, 3 * b + 3)) for b in tile)
             if int(np.prod(grid)) <= max_tokens:
                 break
         counts = [(L + b - 1) // b for L, b in zip(grid, tile)]
         window = tuple(int(rng.choice([w for w in (1, 3, 5) if w <= 2 * c + 1])) for c in counts)
         shift = tuple(int(rng.integers(b)) if rng.random() < 0.6 else 0 for b in tile)
         mode = str(rng.choice(["clip", "clip", "inward", "cyclic"]))
+        if whole and mode != "cyclic":
+            shift = (0, 0, 0)
         batch = 2 if rng.random() < 0.25 else 1
         heads = 1 if batch == 2 else int(rng.integers(1, 3))
         with_lse = bool(rng.random() < 0.7)
@@ -74,10 +84,12 @@ def test_sweep_reaches_every_kernel():
         name, B, H, grid, tile, window, shift, mode, D, dt, _ = c
         k = V.sta_kernel_name(B, H, D, grid, tile, window, shift, mode, dtype=dt)
         seen[k] = seen.get(k, 0) + 1
-    want = ["box_attn_bf16_pp_kernel", "box_attn_bf16_m16_kernel<4>", "box_attn_bf16_kernel<128>",
+    want = ["box_attn_bf16_pp_kernel<0>", "box_attn_bf16_m16_kernel<4>", "box_attn_bf16_kernel<128>",
             "box_attn_bf16_kernel<64>", "box_attn_f32_kernel<64>", "box_attn_f32_kernel<128>"]
     for k in want:
         assert seen.get(k, 0) >= 2, (k, seen)
+    # the 384-query kernel's tile walks, plain and on the rolled grid
+    assert seen.get("box_attn_bf16_pp_kernel<1>", 0) + seen.get("box_attn_bf16_pp_kernel<2>", 0) >= 2, seen
     modes = [c[7] for c in FWD]
     assert min(modes.count(m) for m in ("clip", "inward", "cyclic")) >= 5
     assert sum(1 for c in FWD if any(c[6])) >= 15   # shifted lattices

@@ -126,6 +126,23 @@ __device__ __forceinline__ void pin(bf16x8& x) {
 
 __device__ __forceinline__ bf16x8 lds_frag(const char* p) { return __builtin_bit_cast(bf16x8, *(const u32x4*)p); }
 
+// Key walk of a workgroup (BoxAttnParams::tile_walk, chosen by the host):
+//   WALK_RASTER  the key box in raster order, 64 consecutive keys per block,
+//                each lane's key token from two divisions by invariants and
+//                handed to the lanes that load it by cross-lane shuffles;
+//   WALK_TILES   every tile of the lattice full, no lattice shift and 64
+//                tokens per tile frame: the box tile by tile in raster order
+//                of tiles, one frame of a tile per block.  A lane's key rows
+//                then sit at the same token offset from the block's first
+//                token in every block, so a request is the block's base
+//                token (uniform) plus one add per load;
+//   WALK_TILES_ROLLED  the same walk on the rolled grid of the cyclic mode:
+//                the frame's base is uniform, and each lane unrolls its rows'
+//                h and w coordinates.  The keys come in the order the clipped
+//                mode visits them on rolled tensors.
+enum { WALK_RASTER = 0, WALK_TILES = 1, WALK_TILES_ROLLED = 2 };
+
+template <int WALK>
 __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttnParams p) {
   __shared__ __attribute__((aligned(16))) char lds[NSTAGE * STAGE];
 
@@ -202,21 +219,94 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
   const int vk = tid % NKG;
   const int vc = tid / NKG;
   u32x4 vreg[VPT];
-  auto load_block = [&](int blk) {
-    const uint32_t my_tok = key_token(blk * BLOCK_N + lane);
-    char* st = stage_of(blk);
+  // the block rows this lane loads: K row of each of its KDMA_W fragments,
+  // V rows VPT*vk + i
+  auto k_row_of = [&](int i) {
+    const int f = wave * KDMA_W + i;   // fragment = (c*2 + t)*KS + ks
+    return 32 * (f / (2 * KS)) + 4 * ((f / KS) & 1) + k_row_in_chunk;
+  };
+  auto k_chunk_of = [&](int i) { return (uint32_t)(4 * ((wave * KDMA_W + i) % KS) + G) * 16u; };
+
+  // ---- tile walk: the key box as whole tiles (extents multiples of the tile,
+  // origins on tile boundaries), walked tile by tile, frame by frame.  The
+  // request cursor (uniform) names the next block's tile and frame.
+  const int w_log = __builtin_ctz((unsigned)max(p.bW, 1));   // bW divides 64: a power of two
+  int cur_tt = 0, cur_th = 0, cur_tw = 0, cur_f = 0;
+  const int n_tt = WALK != WALK_RASTER ? kb.et / max(p.bT, 1) : 0;
+  const int n_th = WALK != WALK_RASTER ? kb.eh / max(p.bH, 1) : 0;
+  const int n_tw = WALK != WALK_RASTER ? kb.ew / max(p.bW, 1) : 0;
+  // WALK_TILES: the rows' byte offsets from the block's first token
+  uint32_t k_off[KDMA_W], v_off[VPT];
+  if constexpr (WALK == WALK_TILES) {
 #pragma unroll
     for (int i = 0; i < KDMA_W; ++i) {
-      const int f = wave * KDMA_W + i;           // fragment = (c*2 + t)*KS + ks
-      const int ks = f % KS, t = (f / KS) & 1, c = f / (2 * KS);
-      const uint32_t tok = (uint32_t)__shfl((int)my_tok, 32 * c + 4 * t + k_row_in_chunk, 64);
-      const uint32_t off = tok * k_row + (uint32_t)(4 * ks + G) * 16u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void*)(st + f * 1024), 16, (int)off, 0, 0, 0);
+      const int r = k_row_of(i);
+      k_off[i] = (uint32_t)((r >> w_log) * p.kW + (r & (p.bW - 1))) * k_row + k_chunk_of(i);
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const uint32_t tok = (uint32_t)__shfl((int)my_tok, VPT * vk + i, 64);
-      vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrsrc, (int)(tok * v_row + vc * 16), 0, 0));
+      const int r = VPT * vk + i;
+      v_off[i] = (uint32_t)((r >> w_log) * p.kW + (r & (p.bW - 1))) * v_row + (uint32_t)vc * 16u;
+    }
+  }
+
+  auto load_block = [&](int blk) {
+    char* st = stage_of(blk);
+    if constexpr (WALK == WALK_RASTER) {
+      const uint32_t my_tok = key_token(blk * BLOCK_N + lane);
+#pragma unroll
+      for (int i = 0; i < KDMA_W; ++i) {
+        const int f = wave * KDMA_W + i;
+        const uint32_t tok = (uint32_t)__shfl((int)my_tok, k_row_of(i), 64);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void*)(st + f * 1024), 16,
+                                                 (int)(tok * k_row + k_chunk_of(i)), 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const uint32_t tok = (uint32_t)__shfl((int)my_tok, VPT * vk + i, 64);
+        vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrsrc, (int)(tok * v_row + vc * 16), 0, 0));
+      }
+    } else {
+      // the block: frame cur_f of key-box tile (cur_tt, cur_th, cur_tw)
+      const int t = kb.t0 + cur_tt * p.bT + cur_f;
+      const int h = kb.h0 + cur_th * p.bH;
+      const int w = kb.w0 + cur_tw * p.bW;
+      if (++cur_f == p.bT) {
+        cur_f = 0;
+        if (++cur_tw == n_tw) {
+          cur_tw = 0;
+          if (++cur_th == n_th) {
+            cur_th = 0;
+            ++cur_tt;
+          }
+        }
+      }
+      if constexpr (WALK == WALK_TILES) {
+        const uint32_t base = (uint32_t)((t * p.kH + h) * p.kW + w);
+        const uint32_t kb_off = base * k_row, vb_off = base * v_row;
+#pragma unroll
+        for (int i = 0; i < KDMA_W; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void*)(st + (wave * KDMA_W + i) * 1024), 16,
+                                                   (int)(kb_off + k_off[i]), 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
+          vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrsrc, (int)(vb_off + v_off[i]), 0, 0));
+      } else {
+        const uint32_t trow = (uint32_t)(unroll(t, p.rlT, p.kT) * p.kH);
+        auto tok_of = [&](int r) -> uint32_t {
+          const int hh = unroll(h + (r >> w_log), p.rlH, p.kH);
+          const int ww = unroll(w + (r & (p.bW - 1)), p.rlW, p.kW);
+          return (trow + (uint32_t)hh) * (uint32_t)p.kW + (uint32_t)ww;
+        };
+#pragma unroll
+        for (int i = 0; i < KDMA_W; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void*)(st + (wave * KDMA_W + i) * 1024), 16,
+                                                   (int)(tok_of(k_row_of(i)) * k_row + k_chunk_of(i)), 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
+          vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  vrsrc, (int)(tok_of(VPT * vk + i) * v_row + vc * 16), 0, 0));
+      }
     }
   };
   // Transposing store of the V registers: element e of the thread's two keys
@@ -457,7 +547,12 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
 }  // namespace
 
 hipError_t launch_box_attn_bf16_pp(const BoxAttnParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(box_attn_bf16_pp_kernel, dim3(p.total_wg), dim3(NW * 64), 0, stream, p);
+  if (p.tile_walk == WALK_TILES)
+    hipLaunchKernelGGL(box_attn_bf16_pp_kernel<WALK_TILES>, dim3(p.total_wg), dim3(NW * 64), 0, stream, p);
+  else if (p.tile_walk == WALK_TILES_ROLLED)
+    hipLaunchKernelGGL(box_attn_bf16_pp_kernel<WALK_TILES_ROLLED>, dim3(p.total_wg), dim3(NW * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL(box_attn_bf16_pp_kernel<WALK_RASTER>, dim3(p.total_wg), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -71,6 +71,8 @@ struct BoxAttnParams {
                               // coordinate x' is the token at (x' - rl) mod L
   int32_t qblocks;            // query blocks per tile
   int32_t variant;            // which kernel shape the launcher runs (set by the host)
+  int32_t tile_walk;          // 384-query kernel's key walk: 0 raster, 1 whole tiles, 2 whole
+                              // tiles of the rolled grid (set by the host; see attn_bf16_pp.hip)
   int32_t total_wg;           // batch * heads * tiles * qblocks
   float scale_log2e;          // scale * log2(e)
   // Optional merge with another branch's output in the epilogue (merge !=
