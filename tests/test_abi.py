@@ -42,7 +42,7 @@ def test_kernel_choice_per_workload():
     # (and dtype / head_dim): the workloads' tiles and two edge cases
     from video_dit_sparse_amd import workloads as WL
     want = {"tiny_f32": "box_attn_f32_kernel<64>", "sta_720p": "box_attn_bf16_pp_kernel<1>",
-            "dual_1080p": "box_attn_bf16_pp_kernel<0>", "local_global_4k": "box_attn_bf16_m16_kernel<4>",
+            "dual_1080p": "box_attn_bf16_pp_kernel<0>", "local_global_4k": "box_attn_bf16_m16_kernel<4, 1>",
             "cross_window_2k": "box_attn_bf16_kernel<128>"}
     for name, kernel in want.items():
         w = WL.WORKLOADS[name]
@@ -58,6 +58,11 @@ def test_kernel_choice_per_workload():
     assert L.sta_kernel_name(1, 24, 128, g720, t720, w720, (3, 4, 4)) == "box_attn_bf16_pp_kernel<0>"
     assert L.sta_kernel_name(1, 24, 128, (30, 48, 81), t720, w720) == "box_attn_bf16_pp_kernel<0>"
     assert L.sta_kernel_name(1, 24, 128, (30, 48, 80), (6, 4, 16), w720) == "box_attn_bf16_pp_kernel<1>"
+    # the 192-query kernel walks whole tiles too, but keeps the raster walk
+    # in the cyclic mode
+    g4k, t4k, w4k = (21, 136, 240), (3, 8, 8), (3, 5, 5)
+    assert L.sta_kernel_name(1, 24, 128, g4k, t4k, w4k, (1, 4, 4), "cyclic") == "box_attn_bf16_m16_kernel<4, 0>"
+    assert L.sta_kernel_name(1, 24, 128, g4k, t4k, w4k, (1, 4, 4)) == "box_attn_bf16_m16_kernel<4, 0>"
     # head_dim 64 always takes the 128-query kernel; a 384-token tile in a
     # grid that clips it to 40 tokens pads a 384-query block by far more than
     # 1/8, so the 128-query kernel takes it

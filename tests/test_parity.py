@@ -191,22 +191,25 @@ def test_sta_deterministic_and_no_stray_writes():
 
 
 TILE_WALK = [
-    # name, grid, tile, window, shift, mode, walk: every tile full and a tile
-    # frame of 64 tokens, so the 384-query kernel walks the key boxes tile by
-    # tile (walk 1), on the rolled grid in the cyclic mode (walk 2)
-    ("whole_tiles", (12, 16, 24), (6, 8, 8), (3, 3, 3), (0, 0, 0), "clip", 1),
-    ("whole_tiles_4x16", (6, 8, 32), (6, 4, 16), (1, 3, 3), (0, 0, 0), "clip", 1),
-    ("whole_tiles_inward", (12, 16, 40), (6, 8, 8), (1, 1, 3), (0, 0, 0), "inward", 1),
-    ("rolled_whole_tiles", (12, 16, 24), (6, 8, 8), (3, 3, 5), (3, 4, 4), "cyclic", 2),
+    # name, grid, tile, window, shift, mode, kernel: every tile full and a
+    # tile frame of 64 tokens, so the key boxes are walked tile by tile (walk
+    # 1), on the rolled grid in the cyclic mode (walk 2)
+    ("whole_tiles", (12, 16, 24), (6, 8, 8), (3, 3, 3), (0, 0, 0), "clip", "box_attn_bf16_pp_kernel<1>"),
+    ("whole_tiles_4x16", (6, 8, 32), (6, 4, 16), (1, 3, 3), (0, 0, 0), "clip", "box_attn_bf16_pp_kernel<1>"),
+    ("whole_tiles_inward", (12, 16, 40), (6, 8, 8), (1, 1, 3), (0, 0, 0), "inward", "box_attn_bf16_pp_kernel<1>"),
+    ("rolled_whole_tiles", (12, 16, 24), (6, 8, 8), (3, 3, 5), (3, 4, 4), "cyclic", "box_attn_bf16_pp_kernel<2>"),
+    ("whole_tiles_192", (9, 16, 24), (3, 8, 8), (3, 3, 3), (0, 0, 0), "clip", "box_attn_bf16_m16_kernel<4, 1>"),
+    ("whole_tiles_192_inward", (6, 24, 32), (3, 4, 16), (1, 5, 1), (0, 0, 0), "inward",
+     "box_attn_bf16_m16_kernel<4, 1>"),
 ]
 
 
 @pytest.mark.parametrize("case", TILE_WALK, ids=[c[0] for c in TILE_WALK])
 def test_tile_walk_bnhd_batch2(case):
-    """The 384-query kernel's tile-by-tile key walks on batch 2, 2 heads,
-    token-major [B, N, heads, D] inputs, with LSE, against the oracle."""
-    name, grid, tile, window, shift, mode, walk = case
-    assert V.sta_kernel_name(2, 2, 128, grid, tile, window, shift, mode) == f"box_attn_bf16_pp_kernel<{walk}>"
+    """The 384- and 192-query kernels' tile-by-tile key walks on batch 2, 2
+    heads, token-major [B, N, heads, D] inputs, with LSE, against the oracle."""
+    name, grid, tile, window, shift, mode, kernel = case
+    assert V.sta_kernel_name(2, 2, 128, grid, tile, window, shift, mode) == kernel
     say(f"[tile walk] {name}")
     N = int(np.prod(grid))
     q, k, v = [WL.make_tensor((2, 2, N, 128), torch.bfloat16, DEV, seed=1500 + i) for i in range(3)]

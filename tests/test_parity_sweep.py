@@ -7,8 +7,8 @@ head_dim, dtype and with / without LSE from a fixed seed, so that the kernels'
 tile decode, box walk, partial blocks and edge tiles meet combinations nobody
 chose.  Tiles are drawn from families whose token counts send the call to each
 attention kernel (384-, 192- and 128-query bf16, head_dim 64, fp32; for the
-384-query kernel half the draws are whole-tile lattices, which it walks tile by
-tile); the CPU
+384- and 192-query kernels half the draws are whole-tile lattices, which they
+walk tile by tile); the CPU
 test checks, with the library's own selection (``vdsa_sta_kernel``), that the
 sweep reaches every kernel several times.  Sizes stay small enough for the
 oracle to finish each case in about a second.  The backward sweep draws from
@@ -47,10 +47,11 @@ def draw_cases(n, seed, max_tokens):
         fam, tiles, D, dt = FAMILIES[i % len(FAMILIES)]
         if D is None:
             D = int(rng.choice([64, 128]))
-        tile = tiles[int(rng.integers(len(tiles)))]
-        # half the 384-token draws: whole tiles and no lattice shift, where the
-        # 384-query kernel walks its key boxes tile by tile
-        whole = fam == "t384" and rng.random() < 0.5
+        # alternate 384- and 192-token draws: whole tiles with 64-token frames
+        # and no lattice shift, which those kernels walk tile by tile
+        whole = fam in ("t384", "t192") and (i // len(FAMILIES)) % 2 == 0
+        pick = [t for t in tiles if t[1] * t[2] == 64] if whole else tiles
+        tile = pick[int(rng.integers(len(pick)))]
         while True:
             # each dim holds at least one full tile and up to about three
             if whole:
@@ -84,12 +85,14 @@ def test_sweep_reaches_every_kernel():
         name, B, H, grid, tile, window, shift, mode, D, dt, _ = c
         k = V.sta_kernel_name(B, H, D, grid, tile, window, shift, mode, dtype=dt)
         seen[k] = seen.get(k, 0) + 1
-    want = ["box_attn_bf16_pp_kernel<0>", "box_attn_bf16_m16_kernel<4>", "box_attn_bf16_kernel<128>",
+    want = ["box_attn_bf16_pp_kernel<0>", "box_attn_bf16_m16_kernel<4, 0>", "box_attn_bf16_kernel<128>",
             "box_attn_bf16_kernel<64>", "box_attn_f32_kernel<64>", "box_attn_f32_kernel<128>"]
     for k in want:
         assert seen.get(k, 0) >= 2, (k, seen)
-    # the 384-query kernel's tile walks, plain and on the rolled grid
+    # the tile walks: the 384-query kernel's, plain and on the rolled grid,
+    # and the 192-query kernel's
     assert seen.get("box_attn_bf16_pp_kernel<1>", 0) + seen.get("box_attn_bf16_pp_kernel<2>", 0) >= 2, seen
+    assert seen.get("box_attn_bf16_m16_kernel<4, 1>", 0) >= 1, seen
     modes = [c[7] for c in FWD]
     assert min(modes.count(m) for m in ("clip", "inward", "cyclic")) >= 5
     assert sum(1 for c in FWD if any(c[6])) >= 15   # shifted lattices

@@ -201,7 +201,7 @@ int64_t max_tile_volume(const vdsa::BoxAttnParams& bp) {
          max_tile_extent(bp.qW, bp.bW, bp.sW);
 }
 
-// Key walk of the 384-query kernel: tile by tile when every tile of the
+// Key walk of the 384- and 192-query kernels: tile by tile when every tile of the
 // lattice is full (no lattice shift, grid dims multiples of the tile) and a
 // tile frame holds exactly one 64-key block (tile h x w = 64), on the rolled
 // grid for the cyclic mode; else the raster walk over the key box.  Sliding
@@ -222,7 +222,8 @@ const char* attn_kernel_name(const vdsa_problem* prob, const vdsa::BoxAttnParams
                                           "box_attn_bf16_pp_kernel<2>"};
   switch (choose_bf16_shape(max_tile_volume(bp), prob->head_dim).kernel) {
     case K_PP_8W: return pp_names[tile_walk_mode(bp)];
-    case K_M16_4W: return "box_attn_bf16_m16_kernel<4>";
+    case K_M16_4W:
+      return tile_walk_mode(bp) == 1 ? "box_attn_bf16_m16_kernel<4, 1>" : "box_attn_bf16_m16_kernel<4, 0>";
     default: return d128 ? "box_attn_bf16_kernel<128>" : "box_attn_bf16_kernel<64>";
   }
 }
@@ -233,7 +234,11 @@ vdsa_status launch_attn(const vdsa_problem* prob, vdsa::BoxAttnParams& bp, hipSt
   if (prob->dtype == VDSA_BF16) shape = choose_bf16_shape(mv, prob->head_dim);
   bp.qblocks = (int32_t)((mv + shape.block_m - 1) / shape.block_m);
   bp.variant = (int32_t)shape.kernel;
-  bp.tile_walk = prob->dtype == VDSA_BF16 && shape.kernel == K_PP_8W ? tile_walk_mode(bp) : 0;
+  // (the 192-query kernel has no rolled tile walk: the cyclic mode stays raster)
+  bp.tile_walk = prob->dtype != VDSA_BF16                                   ? 0
+                 : shape.kernel == K_PP_8W                                  ? tile_walk_mode(bp)
+                 : shape.kernel == K_M16_4W && tile_walk_mode(bp) == 1      ? 1
+                                                                            : 0;
   const int64_t total = (int64_t)bp.batch * bp.heads * bp.nT * bp.nH * bp.nW * bp.qblocks;
   if (total >= (int64_t(1) << 31) / 512)
     return fail(VDSA_ERR_SHAPE, "problem needs %lld workgroups, beyond the launch limit", (long long)total);

@@ -68,7 +68,8 @@ constexpr int WAIT_VMCNT0 = 0x0F70;   // s_waitcnt vmcnt(0), other counters unto
 constexpr float RESCALE_MARGIN = 8.f;
 constexpr int RA = 3;   // operand fragments read ahead of their MFMAs
 
-template <int NW>
+// WALK: the key walk (box_common.h), chosen by the host.
+template <int NW, int WALK>
 __global__ __launch_bounds__(NW * 64, 2) void box_attn_bf16_m16_kernel(const BoxAttnParams p) {
   constexpr int BLOCK_M = NW * 16 * QT;
   constexpr int KDMA_W = NFRAG_K / NW;           // K fragments loaded per wave per block
@@ -151,21 +152,70 @@ __global__ __launch_bounds__(NW * 64, 2) void box_attn_bf16_m16_kernel(const Box
   const int vc = tid / NKG;
   u32x4 vreg[VPT];
 
+  // the block rows this lane loads: K row of each of its KDMA_W fragments,
+  // V rows VPT*vk + i
+  auto k_row_of = [&](int i) {
+    const int f = wave * KDMA_W + i;   // fragment = (c*2 + t)*KS + ks
+    return 32 * (f / (2 * KS)) + 4 * ((f / KS) & 1) + k_row_in_chunk;
+  };
+  auto k_chunk_of = [&](int i) { return (uint32_t)(4 * ((wave * KDMA_W + i) % KS) + G) * 16u; };
+
+  // ---- tile walk (WALK_TILES*): the request cursor, and in WALK_TILES the
+  // rows' byte offsets from the block's first token
+  const int w_log = __builtin_ctz((unsigned)max(p.bW, 1));   // bW divides 64: a power of two
+  TileCursor cur;
+  if constexpr (WALK != WALK_RASTER) cur.init(p, kb);
+  uint32_t k_off[KDMA_W], v_off[VPT];
+  if constexpr (WALK == WALK_TILES) {
+#pragma unroll
+    for (int i = 0; i < KDMA_W; ++i)
+      k_off[i] = (uint32_t)tile_row_offset(p, k_row_of(i), w_log) * k_row + k_chunk_of(i);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+      v_off[i] = (uint32_t)tile_row_offset(p, VPT * vk + i, w_log) * v_row + (uint32_t)vc * 16u;
+  }
+
+  // Requests of consecutive blocks come in order (the tile cursor advances
+  // once per call).
   auto load_block = [&](int blk, int stage) {
-    const uint32_t my_tok = key_token(blk * BLOCK_N + lane);
     char* st = lds + stage * STAGE;
+    if constexpr (WALK == WALK_RASTER) {
+      const uint32_t my_tok = key_token(blk * BLOCK_N + lane);
 #pragma unroll
-    for (int i = 0; i < KDMA_W; ++i) {
-      const int f = wave * KDMA_W + i;           // fragment = (c*2 + t)*KS + ks
-      const int ks = f % KS, t = (f / KS) & 1, c = f / (2 * KS);
-      const uint32_t tok = (uint32_t)__shfl((int)my_tok, 32 * c + 4 * t + k_row_in_chunk, 64);
-      const uint32_t off = tok * k_row + (uint32_t)(4 * ks + G) * 16u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void*)(st + f * 1024), 16, (int)off, 0, 0, 0);
-    }
+      for (int i = 0; i < KDMA_W; ++i) {
+        const uint32_t tok = (uint32_t)__shfl((int)my_tok, k_row_of(i), 64);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void*)(st + (wave * KDMA_W + i) * 1024), 16,
+                                                 (int)(tok * k_row + k_chunk_of(i)), 0, 0, 0);
+      }
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const uint32_t tok = (uint32_t)__shfl((int)my_tok, VPT * vk + i, 64);
-      vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrsrc, (int)(tok * v_row + vc * 16), 0, 0));
+      for (int i = 0; i < VPT; ++i) {
+        const uint32_t tok = (uint32_t)__shfl((int)my_tok, VPT * vk + i, 64);
+        vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrsrc, (int)(tok * v_row + vc * 16), 0, 0));
+      }
+    } else {
+      int t, h, w;
+      cur.next(p, kb, t, h, w);
+      if constexpr (WALK == WALK_TILES) {
+        const uint32_t base = (uint32_t)((t * p.kH + h) * p.kW + w);
+        const uint32_t kb_off = base * k_row, vb_off = base * v_row;
+#pragma unroll
+        for (int i = 0; i < KDMA_W; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void*)(st + (wave * KDMA_W + i) * 1024), 16,
+                                                   (int)(kb_off + k_off[i]), 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
+          vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrsrc, (int)(vb_off + v_off[i]), 0, 0));
+      } else {
+        auto tok_of = [&](int r) { return tile_row_token_rolled(p, t, h, w, r, w_log); };
+#pragma unroll
+        for (int i = 0; i < KDMA_W; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void*)(st + (wave * KDMA_W + i) * 1024), 16,
+                                                   (int)(tok_of(k_row_of(i)) * k_row + k_chunk_of(i)), 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
+          vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  vrsrc, (int)(tok_of(VPT * vk + i) * v_row + vc * 16), 0, 0));
+      }
     }
   };
   // Transposing store of the V registers into the V fragments of `stage`.
@@ -372,8 +422,14 @@ __global__ __launch_bounds__(NW * 64, 2) void box_attn_bf16_m16_kernel(const Box
 
 }  // namespace
 
+// The rolled tile walk is not instantiated here: unrolling the eight rows a
+// thread loads spills registers, so the host keeps the cyclic mode on the
+// raster walk for this kernel.
 hipError_t launch_box_attn_bf16_m16(const BoxAttnParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(box_attn_bf16_m16_kernel<4>, dim3(p.total_wg), dim3(4 * 64), 0, stream, p);
+  if (p.tile_walk == WALK_TILES)
+    hipLaunchKernelGGL((box_attn_bf16_m16_kernel<4, WALK_TILES>), dim3(p.total_wg), dim3(4 * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((box_attn_bf16_m16_kernel<4, WALK_RASTER>), dim3(p.total_wg), dim3(4 * 64), 0, stream, p);
   return hipGetLastError();
 }
 

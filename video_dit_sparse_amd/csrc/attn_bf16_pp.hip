@@ -126,22 +126,7 @@ __device__ __forceinline__ void pin(bf16x8& x) {
 
 __device__ __forceinline__ bf16x8 lds_frag(const char* p) { return __builtin_bit_cast(bf16x8, *(const u32x4*)p); }
 
-// Key walk of a workgroup (BoxAttnParams::tile_walk, chosen by the host):
-//   WALK_RASTER  the key box in raster order, 64 consecutive keys per block,
-//                each lane's key token from two divisions by invariants and
-//                handed to the lanes that load it by cross-lane shuffles;
-//   WALK_TILES   every tile of the lattice full, no lattice shift and 64
-//                tokens per tile frame: the box tile by tile in raster order
-//                of tiles, one frame of a tile per block.  A lane's key rows
-//                then sit at the same token offset from the block's first
-//                token in every block, so a request is the block's base
-//                token (uniform) plus one add per load;
-//   WALK_TILES_ROLLED  the same walk on the rolled grid of the cyclic mode:
-//                the frame's base is uniform, and each lane unrolls its rows'
-//                h and w coordinates.  The keys come in the order the clipped
-//                mode visits them on rolled tensors.
-enum { WALK_RASTER = 0, WALK_TILES = 1, WALK_TILES_ROLLED = 2 };
-
+// WALK: the key walk (box_common.h), chosen by the host.
 template <int WALK>
 __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttnParams p) {
   __shared__ __attribute__((aligned(16))) char lds[NSTAGE * STAGE];
@@ -227,27 +212,19 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
   };
   auto k_chunk_of = [&](int i) { return (uint32_t)(4 * ((wave * KDMA_W + i) % KS) + G) * 16u; };
 
-  // ---- tile walk: the key box as whole tiles (extents multiples of the tile,
-  // origins on tile boundaries), walked tile by tile, frame by frame.  The
-  // request cursor (uniform) names the next block's tile and frame.
+  // ---- tile walk (WALK_TILES*): the request cursor, and in WALK_TILES the
+  // rows' byte offsets from the block's first token
   const int w_log = __builtin_ctz((unsigned)max(p.bW, 1));   // bW divides 64: a power of two
-  int cur_tt = 0, cur_th = 0, cur_tw = 0, cur_f = 0;
-  const int n_tt = WALK != WALK_RASTER ? kb.et / max(p.bT, 1) : 0;
-  const int n_th = WALK != WALK_RASTER ? kb.eh / max(p.bH, 1) : 0;
-  const int n_tw = WALK != WALK_RASTER ? kb.ew / max(p.bW, 1) : 0;
-  // WALK_TILES: the rows' byte offsets from the block's first token
+  TileCursor cur;
+  if constexpr (WALK != WALK_RASTER) cur.init(p, kb);
   uint32_t k_off[KDMA_W], v_off[VPT];
   if constexpr (WALK == WALK_TILES) {
 #pragma unroll
-    for (int i = 0; i < KDMA_W; ++i) {
-      const int r = k_row_of(i);
-      k_off[i] = (uint32_t)((r >> w_log) * p.kW + (r & (p.bW - 1))) * k_row + k_chunk_of(i);
-    }
+    for (int i = 0; i < KDMA_W; ++i)
+      k_off[i] = (uint32_t)tile_row_offset(p, k_row_of(i), w_log) * k_row + k_chunk_of(i);
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int r = VPT * vk + i;
-      v_off[i] = (uint32_t)((r >> w_log) * p.kW + (r & (p.bW - 1))) * v_row + (uint32_t)vc * 16u;
-    }
+    for (int i = 0; i < VPT; ++i)
+      v_off[i] = (uint32_t)tile_row_offset(p, VPT * vk + i, w_log) * v_row + (uint32_t)vc * 16u;
   }
 
   auto load_block = [&](int blk) {
@@ -267,20 +244,8 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
         vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrsrc, (int)(tok * v_row + vc * 16), 0, 0));
       }
     } else {
-      // the block: frame cur_f of key-box tile (cur_tt, cur_th, cur_tw)
-      const int t = kb.t0 + cur_tt * p.bT + cur_f;
-      const int h = kb.h0 + cur_th * p.bH;
-      const int w = kb.w0 + cur_tw * p.bW;
-      if (++cur_f == p.bT) {
-        cur_f = 0;
-        if (++cur_tw == n_tw) {
-          cur_tw = 0;
-          if (++cur_th == n_th) {
-            cur_th = 0;
-            ++cur_tt;
-          }
-        }
-      }
+      int t, h, w;
+      cur.next(p, kb, t, h, w);
       if constexpr (WALK == WALK_TILES) {
         const uint32_t base = (uint32_t)((t * p.kH + h) * p.kW + w);
         const uint32_t kb_off = base * k_row, vb_off = base * v_row;
@@ -292,12 +257,7 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
         for (int i = 0; i < VPT; ++i)
           vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrsrc, (int)(vb_off + v_off[i]), 0, 0));
       } else {
-        const uint32_t trow = (uint32_t)(unroll(t, p.rlT, p.kT) * p.kH);
-        auto tok_of = [&](int r) -> uint32_t {
-          const int hh = unroll(h + (r >> w_log), p.rlH, p.kH);
-          const int ww = unroll(w + (r & (p.bW - 1)), p.rlW, p.kW);
-          return (trow + (uint32_t)hh) * (uint32_t)p.kW + (uint32_t)ww;
-        };
+        auto tok_of = [&](int r) { return tile_row_token_rolled(p, t, h, w, r, w_log); };
 #pragma unroll
         for (int i = 0; i < KDMA_W; ++i)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void*)(st + (wave * KDMA_W + i) * 1024), 16,

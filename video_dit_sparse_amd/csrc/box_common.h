@@ -152,5 +152,61 @@ __device__ __forceinline__ void tile_boxes(const BoxAttnParams& p, int tile, Box
   tile_boxes_at(p, tile / (p.nW * p.nH), (tile / p.nW) % p.nH, tile % p.nW, qb, kb);
 }
 
+// Key walks of the 384- and 192-query kernels (BoxAttnParams::tile_walk):
+//   WALK_RASTER        the key box in raster order, 64 consecutive keys per
+//                      block (each lane's key token from two divisions by
+//                      invariants, handed to the loading lanes by shuffles);
+//   WALK_TILES         every tile of the lattice full, no lattice shift, 64
+//                      tokens per tile frame: the box tile by tile (raster
+//                      order of tiles), one frame of one tile per block, so a
+//                      lane's rows sit at fixed token offsets from the block's
+//                      first token;
+//   WALK_TILES_ROLLED  the same on the rolled grid of the cyclic mode (uniform
+//                      frame, per-lane unroll of h and w), visiting keys in
+//                      the order the clipped walk visits rolled tensors.
+enum { WALK_RASTER = 0, WALK_TILES = 1, WALK_TILES_ROLLED = 2 };
+
+// Cursor of a tile walk: the next block is frame f of key-box tile
+// (tt, th, tw); the box is whole tiles, so its extents are multiples of the
+// tile and its origin on tile boundaries.  Uniform over the workgroup.
+struct TileCursor {
+  int tt = 0, th = 0, tw = 0, f = 0;
+  int n_th = 1, n_tw = 1;
+  __device__ void init(const BoxAttnParams& p, const Box& kb) {
+    n_th = kb.eh / p.bH;
+    n_tw = kb.ew / p.bW;
+  }
+  // Rolled-grid coordinates of the next block's first token; then advance.
+  __device__ void next(const BoxAttnParams& p, const Box& kb, int& t, int& h, int& w) {
+    t = kb.t0 + tt * p.bT + f;
+    h = kb.h0 + th * p.bH;
+    w = kb.w0 + tw * p.bW;
+    if (++f == p.bT) {
+      f = 0;
+      if (++tw == n_tw) {
+        tw = 0;
+        if (++th == n_th) {
+          th = 0;
+          ++tt;
+        }
+      }
+    }
+  }
+};
+
+// Token offset, within the key grid, of row r of a tile-frame block from the
+// block's first token (tile width 2^w_log).
+__device__ __forceinline__ int tile_row_offset(const BoxAttnParams& p, int r, int w_log) {
+  return (r >> w_log) * p.kW + (r & (p.bW - 1));
+}
+// Token of row r of the tile-frame block at rolled (t, h, w), cyclic mode.
+__device__ __forceinline__ uint32_t tile_row_token_rolled(const BoxAttnParams& p, int t, int h, int w, int r,
+                                                          int w_log) {
+  const int tu = unroll(t, p.rlT, p.kT);
+  const int hu = unroll(h + (r >> w_log), p.rlH, p.kH);
+  const int wu = unroll(w + (r & (p.bW - 1)), p.rlW, p.kW);
+  return (uint32_t)((tu * p.kH + hu) * p.kW + wu);
+}
+
 
 }  // namespace vdsa
