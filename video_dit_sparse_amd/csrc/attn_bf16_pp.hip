@@ -89,23 +89,6 @@ constexpr int PF = 4;                                // operand fragments read a
 constexpr float RESCALE_MARGIN = 8.f;
 static_assert(KDMA_W * NW == NFRAG_K && VPT == 2 && VPT * NKG == BLOCK_N, "work split");
 
-// s_waitcnt immediate: vmcnt(vm), lgkmcnt(lgkm), expcnt untouched
-__device__ __forceinline__ constexpr int wait_enc(int vm, int lgkm) {
-  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
-}
-
-// Phase boundary: this wave's LDS accesses are complete, then a workgroup
-// barrier.  Outstanding global loads stay in flight.  Neither the compiler's
-// scheduler nor its memory optimisations move work across it.
-__device__ __forceinline__ void phase_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(wait_enc(63, 0));
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // Wait until at most `keep` of this wave's vector-memory loads are in flight.
 __device__ __forceinline__ void vm_wait(bool keep_one_block) {
   if (keep_one_block)

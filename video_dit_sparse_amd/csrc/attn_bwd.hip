@@ -20,6 +20,8 @@ namespace vdsa {
 
 hipError_t launch_attn_bwd_bf16(const BoxBwdParams& p, bool kv, hipStream_t stream);
 int attn_bwd_bf16_block_m(bool kv);
+hipError_t launch_attn_bwd_dkdv_pp(const BoxBwdParams& p, hipStream_t stream);
+int attn_bwd_dkdv_pp_block_m();
 
 namespace {
 
@@ -217,7 +219,10 @@ int grid_for(int64_t work) {
 
 }  // namespace
 
-int attn_bwd_block_m(int bf16, bool kv) { return bf16 ? attn_bwd_bf16_block_m(kv) : OPB; }
+int attn_bwd_block_m(int bf16, bool kv) {
+  if (!bf16) return OPB;
+  return kv ? attn_bwd_dkdv_pp_block_m() : attn_bwd_bf16_block_m(false);
+}
 
 hipError_t launch_attn_bwd_dq(const BoxBwdParams& p, int bf16, hipStream_t stream) {
   if (bf16) return launch_attn_bwd_bf16(p, false, stream);
@@ -230,7 +235,7 @@ hipError_t launch_attn_bwd_dq(const BoxBwdParams& p, int bf16, hipStream_t strea
 }
 
 hipError_t launch_attn_bwd_dkdv(const BoxBwdParams& p, int bf16, hipStream_t stream) {
-  if (bf16) return launch_attn_bwd_bf16(p, true, stream);
+  if (bf16) return launch_attn_bwd_dkdv_pp(p, stream);
   const dim3 grid(p.g.total_wg), block(NTHREADS);
   if (p.head_dim == 128)
     hipLaunchKernelGGL((box_attn_bwd_f32_kernel<128, true>), grid, block, 0, stream, p);

@@ -68,6 +68,24 @@ __device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv& f) {
   return (__umulhi(n, f.m) + n) >> f.s;
 }
 
+// s_waitcnt immediate: vmcnt(vm), lgkmcnt(lgkm), expcnt untouched
+__device__ __forceinline__ constexpr int wait_enc(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
+}
+
+// Phase boundary of the kernels whose two wave groups alternate matrix-core
+// and vector phases: this wave's LDS accesses are complete, then a workgroup
+// barrier.  Outstanding global loads stay in flight.  Neither the compiler's
+// scheduler nor its memory optimisations move work across it.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(wait_enc(63, 0));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // The hardware hands workgroup i to XCD i % 8.  Renumber so that consecutive
 // logical ids (the query blocks of one tile, then neighbouring tiles, whose
 // key boxes overlap) run on the same XCD and share its L2.
