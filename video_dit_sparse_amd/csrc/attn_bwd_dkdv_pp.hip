@@ -79,6 +79,19 @@ __device__ __forceinline__ void pin(bf16x8& x) {
 
 __device__ __forceinline__ bf16x8 lds_frag(const char* p) { return __builtin_bit_cast(bf16x8, *(const u32x4*)p); }
 
+// Lane n of each 16-lane row broadcast to the whole row (DPP row_newbcast:n).
+template <int N>
+__device__ __forceinline__ float row_bcast(int x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x150 + N, 0xF, 0xF, false));
+}
+// a[e] = x of lane e of the row, b[e] = x of lane 8 + e.
+__device__ __forceinline__ void row_bcast8(int x, float (&a)[8], float (&b)[8]) {
+  a[0] = row_bcast<0>(x); a[1] = row_bcast<1>(x); a[2] = row_bcast<2>(x); a[3] = row_bcast<3>(x);
+  a[4] = row_bcast<4>(x); a[5] = row_bcast<5>(x); a[6] = row_bcast<6>(x); a[7] = row_bcast<7>(x);
+  b[0] = row_bcast<8>(x); b[1] = row_bcast<9>(x); b[2] = row_bcast<10>(x); b[3] = row_bcast<11>(x);
+  b[4] = row_bcast<12>(x); b[5] = row_bcast<13>(x); b[6] = row_bcast<14>(x); b[7] = row_bcast<15>(x);
+}
+
 __global__ __launch_bounds__(NW * 64) void box_attn_bwd_dkdv_pp_kernel(const BoxBwdParams P) {
   __shared__ __attribute__((aligned(16))) char lds[NSTAGE * STAGE];
   const BoxAttnParams& g = P.g;
@@ -293,17 +306,20 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bwd_dkdv_pp_kernel(const Box
 
   // ---- V phase: P and dS of chunk c from its S and dP; nvalid = queries of
   // the box from this chunk on (masking only in the last, partial chunk).
+  // Each lane of 16-lane row G reads one value, LSE (lanes 0-7) or delta
+  // (lanes 8-15) of query row 8G + (lane & 7); row broadcasts (DPP
+  // row_newbcast) hand every lane of the row all sixteen.
+  const int ld_rd = LD + 4 * (8 * G + (l16 & 7)) + (l16 >> 3) * (4 * CHUNK);
   auto vphase = [&](const char* st, int nvalid, auto partial_tag) {
     constexpr bool PARTIAL = decltype(partial_tag)::value;
-    const f32x4 la = *(const f32x4*)(st + LD + 4 * (8 * G));
-    const f32x4 lb = *(const f32x4*)(st + LD + 4 * (8 * G + 4));
-    const f32x4 da = *(const f32x4*)(st + LD + 4 * (CHUNK + 8 * G));
-    const f32x4 db = *(const f32x4*)(st + LD + 4 * (CHUNK + 8 * G + 4));
+    const int x = *(const int*)(st + ld_rd);
+    float l2s[8], dls[8];
+    row_bcast8(x, l2s, dls);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int t = e >> 2, v = e & 3;
-      const float l2 = t ? lb[v] : la[v];
-      const float dl = t ? db[v] : da[v];
+      const float l2 = l2s[e];
+      const float dl = dls[e];
       float pv = __builtin_amdgcn_exp2f(fmaf(s[t][v], cl2, -l2));
       if constexpr (PARTIAL) {
         if (8 * G + e >= nvalid) pv = 0.f;
