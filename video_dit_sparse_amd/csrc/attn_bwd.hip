@@ -18,10 +18,10 @@
 
 namespace vdsa {
 
-hipError_t launch_attn_bwd_bf16(const BoxBwdParams& p, bool kv, hipStream_t stream);
-int attn_bwd_bf16_block_m(bool kv);
 hipError_t launch_attn_bwd_dkdv_pp(const BoxBwdParams& p, hipStream_t stream);
 int attn_bwd_dkdv_pp_block_m();
+hipError_t launch_attn_bwd_dq_pp(const BoxBwdParams& p, hipStream_t stream);
+int attn_bwd_dq_pp_block_m();
 
 namespace {
 
@@ -221,11 +221,11 @@ int grid_for(int64_t work) {
 
 int attn_bwd_block_m(int bf16, bool kv) {
   if (!bf16) return OPB;
-  return kv ? attn_bwd_dkdv_pp_block_m() : attn_bwd_bf16_block_m(false);
+  return kv ? attn_bwd_dkdv_pp_block_m() : attn_bwd_dq_pp_block_m();
 }
 
 hipError_t launch_attn_bwd_dq(const BoxBwdParams& p, int bf16, hipStream_t stream) {
-  if (bf16) return launch_attn_bwd_bf16(p, false, stream);
+  if (bf16) return launch_attn_bwd_dq_pp(p, stream);
   const dim3 grid(p.g.total_wg), block(NTHREADS);
   if (p.head_dim == 128)
     hipLaunchKernelGGL((box_attn_bwd_f32_kernel<128, false>), grid, block, 0, stream, p);

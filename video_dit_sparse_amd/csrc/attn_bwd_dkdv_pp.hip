@@ -2,15 +2,20 @@
 // 128, fp32 accumulation, with the matrix-core work of one half of the
 // workgroup overlapping the softmax terms of the other half.
 //
-// What it computes (the second pass of attn_bwd_bf16.hip, same operands and
-// fragment layouts): for the keys a workgroup owns, over every query whose key
-// box holds them,
+// What it computes: for the keys a workgroup owns, over every query whose key
+// box holds them (the queries of the key tile's transposed window),
 //   P = exp(scale q.k - LSE),  dP = dO.v,  dS = P * (dP - delta),
 //   dK = scale dS^T Q,  dV = P^T dO.
 // Each wave owns one 16-key tile (K and V resident as MFMA B operands) and
 // walks the queries of its tile's transposed window in 32-query chunks:
 // S = Q K^T and dP = dO V^T (rows: queries, columns: the wave's keys), then
-// dK^T += Q^T dS and dV^T += dO^T P.
+// dK^T += Q^T dS and dV^T += dO^T P.  The queries sit on the MFMA rows, so
+// every probability of a key is computed by one lane group and the S and dP
+// accumulators are already the B operands of the gradient products: query
+// rows are permuted inside each chunk (row r of 16-row tile t is query
+// 8*(r/4) + 4t + r%4), so that lane group G holds queries 8G .. 8G+7 after
+// the two tiles, the k-slice of the following product.  The Q^T and dO^T
+// operands use the forward kernels' XOR-swizzled transposed layout.
 //
 // Schedule.  Eight waves, two per SIMD: group A (waves 0-3) and group B
 // (waves 4-7) hold one wave on every SIMD each.  Every wave alternates
