@@ -58,6 +58,12 @@ STA_BWD = [
     # whole tiles of 64-token frames (4x16 and 2x32), walked tile by tile
     ("tile4x16_bf16", 1, (6, 8, 32), (6, 4, 16), (1, 3, 3), (0, 0, 0), 2, 128, "bf16"),
     ("tile2x32_bf16", 1, (4, 6, 64), (2, 2, 32), (3, 3, 1), (0, 0, 0), 1, 128, "bf16"),
+    # self windows: boxes of one 32-token chunk (the dQ pass's odd-chunk group
+    # has none), of two chunks, and of three with ragged edge tiles (a partial
+    # last chunk in the 48-token tiles)
+    ("self_1chunk_bf16", 1, (4, 8, 8), (2, 4, 4), (1, 1, 1), (0, 0, 0), 2, 128, "bf16"),
+    ("self_2chunks_bf16", 1, (4, 8, 8), (2, 4, 8), (1, 1, 1), (0, 0, 0), 1, 128, "bf16"),
+    ("self_3chunks_ragged_bf16", 2, (3, 8, 12), (3, 4, 8), (1, 1, 1), (0, 0, 0), 1, 128, "bf16"),
     ("f32_d64", 1, (3, 6, 8), (3, 3, 4), (1, 3, 1), (0, 1, 2), 2, 64, "f32"),
     ("f32_d128", 1, (2, 6, 8), (1, 3, 4), (1, 1, 3), (0, 0, 0), 1, 128, "f32"),
 ]
