@@ -144,6 +144,10 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bwd_dkdv_pp_kernel(const Box
   // ---- this lane's key: column l16 of the wave's tile
   const int jo = o0 + wave * 16 + l16;
   const bool own_valid = jo < ovol;
+  // A wave whose keys all lie past the tile (the last workgroup of a tile
+  // whose size is not a multiple of BLOCK_M) keeps its requests, stores and
+  // barriers but skips its products and softmax terms.
+  const bool active = o0 + wave * 16 < ovol;   // uniform over the wave
   uint32_t own_tok;
   bf16x8 kf[KS], vf[KS];
   {
@@ -193,7 +197,7 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bwd_dkdv_pp_kernel(const Box
   // chunk c+1 waits for its store while chunk c+2's requests are in flight).
   u32x4 treg[2][2];   // [chunk parity][row]
   float ldreg[2];
-  auto load_chunk = [&](int c, auto par) {
+  auto load_chunk = [&](int c, auto par) __attribute__((always_inline)) {
     constexpr int PAR = decltype(par)::value;
     char* st = stage_of(c);
     const uint32_t my_tok = iter_token(c * CHUNK + (lane & 31));
@@ -222,7 +226,7 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bwd_dkdv_pp_kernel(const Box
   const int vsig = ((vk0 >> 3) << 1);
   const uint32_t vw_base =
       (uint32_t)((grp_b ? YT : XT) + (vk0 >> 3) * 256 + (vk0 & 7) * 2 + (vc >> 1) * 1024 + (vc & 1) * 128);
-  auto store_chunk = [&](int c, auto par) {
+  auto store_chunk = [&](int c, auto par) __attribute__((always_inline)) {
     constexpr int PAR = decltype(par)::value;
     const uint32_t sbase = (uint32_t)(uintptr_t)stage_of(c);
 #pragma unroll
@@ -259,7 +263,7 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bwd_dkdv_pp_kernel(const Box
   // (t, ks) in (ks, t) order, dependent products four MFMAs apart).
   // Fragment pairs are read PF steps ahead.
   bf16x8 fx[16], fy[16];
-  auto mphase = [&](const char* st_g, const char* st_s, auto with_s_tag) {
+  auto mphase = [&](const char* st_g, const char* st_s, auto with_s_tag) __attribute__((always_inline)) {
     constexpr bool WITH_S = decltype(with_s_tag)::value;
     constexpr int i1 = WITH_S ? 16 : 8;
     auto rd = [&](int i) __attribute__((always_inline)) {
@@ -315,7 +319,7 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bwd_dkdv_pp_kernel(const Box
   // (lanes 8-15) of query row 8G + (lane & 7); row broadcasts (DPP
   // row_newbcast) hand every lane of the row all sixteen.
   const int ld_rd = LD + 4 * (8 * G + (l16 & 7)) + (l16 >> 3) * (4 * CHUNK);
-  auto vphase = [&](const char* st, int nvalid, auto partial_tag) {
+  auto vphase = [&](const char* st, int nvalid, auto partial_tag) __attribute__((always_inline)) {
     constexpr bool PARTIAL = decltype(partial_tag)::value;
     const int x = *(const int*)(st + ld_rd);
     float l2s[8], dls[8];
@@ -346,37 +350,46 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bwd_dkdv_pp_kernel(const Box
   phase_barrier();
   if (grp_b) phase_barrier();
 
-  // chunk c, of parity PAR (c % 2)
-  auto do_chunk = [&](int c, auto par, auto partial_tag) {
+  // chunk c, of parity PAR (c % 2); ACTIVE: the wave computes (a compile-time
+  // flag: the whole walk is instantiated with and without the compute)
+  auto do_chunk = [&](int c, auto par, auto partial_tag, auto active_tag) __attribute__((always_inline)) {
     constexpr int PAR = decltype(par)::value;
+    constexpr bool ACTIVE = decltype(active_tag)::value;
     using Next = std::integral_constant<int, PAR ^ 1>;
     // M(c)
     load_chunk(c + 2, par);
     // (chunk 0's M phase multiplies zero P and dS into chunk 0's finite
     // transposed fragments: it adds exactly zero)
-    mphase(stage_of(c > 0 ? c - 1 : 0), stage_of(c), std::true_type{});
+    if constexpr (ACTIVE) mphase(stage_of(c > 0 ? c - 1 : 0), stage_of(c), std::true_type{});
     vm_wait_keep_one();   // this wave's requests of chunk c+1 have landed
     phase_barrier();
     // V(c)
     if (c + 1 < nch) store_chunk(c + 1, Next{});
-    vphase(stage_of(c), ivol - c * CHUNK, partial_tag);
+    if constexpr (ACTIVE) vphase(stage_of(c), ivol - c * CHUNK, partial_tag);
     phase_barrier();
   };
   const bool last_partial = ivol % CHUNK != 0;
   const int nfull = last_partial ? nch - 1 : nch;
-  int c = 0;
-  for (; c + 1 < nfull; c += 2) {
-    do_chunk(c, Even{}, std::false_type{});
-    do_chunk(c + 1, Odd{}, std::false_type{});
-  }
-  if (c < nfull) do_chunk(c++, Even{}, std::false_type{});
-  if (last_partial) {
-    if (c & 1)
-      do_chunk(c, Odd{}, std::true_type{});
-    else
-      do_chunk(c, Even{}, std::true_type{});
-  }
-  mphase(stage_of(nch - 1), stage_of(nch - 1), std::false_type{});
+  auto walk = [&](auto active_tag) __attribute__((always_inline)) {
+    constexpr bool ACTIVE = decltype(active_tag)::value;
+    int c = 0;
+    for (; c + 1 < nfull; c += 2) {
+      do_chunk(c, Even{}, std::false_type{}, active_tag);
+      do_chunk(c + 1, Odd{}, std::false_type{}, active_tag);
+    }
+    if (c < nfull) do_chunk(c++, Even{}, std::false_type{}, active_tag);
+    if (last_partial) {
+      if (c & 1)
+        do_chunk(c, Odd{}, std::true_type{}, active_tag);
+      else
+        do_chunk(c, Even{}, std::true_type{}, active_tag);
+    }
+    if constexpr (ACTIVE) mphase(stage_of(nch - 1), stage_of(nch - 1), std::false_type{});
+  };
+  if (active)
+    walk(std::true_type{});
+  else
+    walk(std::false_type{});
   __builtin_amdgcn_s_waitcnt(wait_enc(0, 15));   // the requests past the end have landed
   if (!grp_b) phase_barrier();
 

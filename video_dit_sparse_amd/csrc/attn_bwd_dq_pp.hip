@@ -156,6 +156,12 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bwd_dq_pp_kernel(const BoxBw
     own_del[ot] = del_bh[own_tok[ot]];
   }
 
+  // A wave whose queries all lie past the tile (the last workgroup of a tile
+  // whose size is not a multiple of BLOCK_M) keeps its requests, stores and
+  // barriers but skips its products and softmax terms (its partner in the
+  // other group owns the same queries and skips them too).
+  const bool active = o0 + w4 * OT * 16 < ovol;   // uniform over the wave
+
   // ---- key box addressing: key j of the box -> token
   const FastDiv fd_plane = make_fastdiv((uint32_t)(ib.eh * ib.ew));
   const FastDiv fd_row = make_fastdiv((uint32_t)ib.ew);
@@ -294,7 +300,8 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bwd_dq_pp_kernel(const BoxBw
 
   // ---- V phase: dS^T of chunk c from its S^T and dP^T; keys of the box
   // from this chunk on: nvalid (masking only in the last, partial chunk).
-  auto vphase = [&](int nvalid) {
+  auto vphase_impl = [&](int nvalid, auto partial_tag) {
+    constexpr bool PARTIAL = decltype(partial_tag)::value;
     const int lim = nvalid - 8 * G;   // rows e >= lim of this lane are past the box
 #pragma unroll
     for (int ot = 0; ot < OT; ++ot) {
@@ -302,11 +309,19 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bwd_dq_pp_kernel(const BoxBw
       for (int e = 0; e < 8; ++e) {
         const int t = e >> 2, v = e & 3;
         float pv = __builtin_amdgcn_exp2f(fmaf(s[t][ot][v], cl2, -own_lse2[ot]));
-        if (e >= lim) pv = 0.f;
+        if constexpr (PARTIAL) {
+          if (e >= lim) pv = 0.f;
+        }
         dsb[ot][e] = (__bf16)(pv * (dp[t][ot][v] - own_del[ot]));
       }
       pin(dsb[ot]);
     }
+  };
+  auto vphase = [&](int nvalid) {
+    if (nvalid >= CHUNK)   // uniform: every chunk but a partial last one
+      vphase_impl(nvalid, std::false_type{});
+    else
+      vphase_impl(nvalid, std::true_type{});
   };
 
   using Even = std::integral_constant<int, 0>;
@@ -338,12 +353,12 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bwd_dq_pp_kernel(const BoxBw
     load_chunk(c + AHEAD, par);
     // (a group's first M phase multiplies zero dS into the finite K^T
     // fragments of its own chunk: it adds exactly zero)
-    mphase(stage_of(c >= 2 ? c - 2 : c), stage_of(c), std::true_type{});
+    if (active) mphase(stage_of(c >= 2 ? c - 2 : c), stage_of(c), std::true_type{});
     vm_wait_keep_one();   // this wave's requests of chunk c+1 have landed
     phase_barrier();
     // V(c), slot c+1
     if (c >= 2) store_chunk(c + 1, Prev{});
-    vphase(ivol - c * CHUNK);
+    if (active) vphase(ivol - c * CHUNK);
     phase_barrier();
   };
   int c = grp;
@@ -356,7 +371,7 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bwd_dq_pp_kernel(const BoxBw
   const int n_own = (nch - grp + 1) / 2;   // chunks of this group
   if (n_own > 0) {
     const int c_last = grp + 2 * (n_own - 1);
-    mphase(stage_of(c_last), stage_of(c_last), std::false_type{});
+    if (active) mphase(stage_of(c_last), stage_of(c_last), std::false_type{});
   }
   __builtin_amdgcn_s_waitcnt(wait_enc(0, 15));   // every request (also past the end) has landed
   phase_barrier();
