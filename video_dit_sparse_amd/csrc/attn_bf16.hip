@@ -47,15 +47,6 @@
 namespace vdsa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void;
-// raw buffer resource word 3 for gfx9-class parts (32-bit data format)
-constexpr int BUF_FLAGS = 0x00020000;
-
 constexpr int BLOCK_M = 128;   // queries per workgroup
 constexpr int BLOCK_N = 64;    // keys per iteration
 constexpr int NTHREADS = 256;  // 4 waves of 64

@@ -46,14 +46,6 @@
 namespace vdsa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void;
-constexpr int BUF_FLAGS = 0x00020000;   // raw buffer resource word 3 (gfx9-class)
-
 constexpr int HD = 128;
 constexpr int BLOCK_N = 64;   // keys per block
 constexpr int QT = 3;         // 16-query tiles per wave

@@ -60,15 +60,6 @@
 namespace vdsa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) uint32_t lds_u32;
-constexpr int BUF_FLAGS = 0x00020000;   // raw buffer resource word 3 (gfx9-class)
-
 constexpr int HD = 128;
 constexpr int BLOCK_N = 64;             // keys per block
 constexpr int QT = 3;                   // 16-query tiles per wave
@@ -96,18 +87,6 @@ __device__ __forceinline__ void vm_wait(bool keep_one_block) {
   else
     __builtin_amdgcn_s_waitcnt(wait_enc(0, 15));
 }
-
-// Empty asm statements that claim to rewrite their operands: the values are
-// computed before this point, so the work of a phase cannot sink into the next.
-__device__ __forceinline__ void pin(f32x4& a, f32x4& b, f32x4& c) { asm volatile("" : "+v"(a), "+v"(b), "+v"(c)); }
-__device__ __forceinline__ void pin(float& a, float& b, float& c) { asm volatile("" : "+v"(a), "+v"(b), "+v"(c)); }
-__device__ __forceinline__ void pin(bf16x8& x) {
-  u32x4 u = __builtin_bit_cast(u32x4, x);
-  asm volatile("" : "+v"(u));
-  x = __builtin_bit_cast(bf16x8, u);
-}
-
-__device__ __forceinline__ bf16x8 lds_frag(const char* p) { return __builtin_bit_cast(bf16x8, *(const u32x4*)p); }
 
 // WALK: the key walk (box_common.h), chosen by the host.
 template <int WALK>

@@ -42,15 +42,6 @@
 namespace vdsa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) uint32_t lds_u32;
-constexpr int BUF_FLAGS = 0x00020000;   // raw buffer resource word 3 (gfx9-class)
-
 constexpr int HD = 128;
 constexpr int KS = HD / 32;             // 32-wide head_dim steps of S and dP
 constexpr int ND = HD / 16;             // 16-row head_dim tiles of dQ^T
@@ -72,17 +63,6 @@ constexpr int PF = 2;                   // fragment pairs read ahead in an M pha
 static_assert(FPW * (NW / 2) == NFRAG, "fragments per wave");
 static_assert(NSTAGE * STAGE <= 160 * 1024, "LDS");
 static_assert((NW / 2) * 64 * OT * ND * 16 <= NSTAGE * STAGE, "partial dQ hand-over fits the ring");
-
-// Empty asm statements that claim to rewrite their operands: the values are
-// computed before this point, so the work of a phase cannot sink into the next.
-__device__ __forceinline__ void pin(f32x4& a) { asm volatile("" : "+v"(a)); }
-__device__ __forceinline__ void pin(bf16x8& x) {
-  u32x4 u = __builtin_bit_cast(u32x4, x);
-  asm volatile("" : "+v"(u));
-  x = __builtin_bit_cast(bf16x8, u);
-}
-
-__device__ __forceinline__ bf16x8 lds_frag(const char* p) { return __builtin_bit_cast(bf16x8, *(const u32x4*)p); }
 
 __global__ __launch_bounds__(NW * 64) void box_attn_bwd_dq_pp_kernel(const BoxBwdParams P) {
   __shared__ __attribute__((aligned(16))) char lds[NSTAGE * STAGE];

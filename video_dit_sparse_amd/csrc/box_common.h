@@ -6,6 +6,35 @@
 
 namespace vdsa {
 
+// Vector types of MFMA operands and accumulators and of 8- and 16-byte
+// memory chunks; LDS pointer types for direct global->LDS loads and 4-byte
+// LDS stores.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+// raw buffer resource word 3 for gfx9-class parts (32-bit data format)
+constexpr int BUF_FLAGS = 0x00020000;
+
+// One 16-byte MFMA operand fragment read from LDS.
+__device__ __forceinline__ bf16x8 lds_frag(const char* p) { return __builtin_bit_cast(bf16x8, *(const u32x4*)p); }
+
+// Empty asm statements that claim to rewrite their operands: the values are
+// computed before this point, so the work of a phase cannot sink into the
+// next one across the kernels' phase barriers.
+__device__ __forceinline__ void pin(f32x4& a) { asm volatile("" : "+v"(a)); }
+__device__ __forceinline__ void pin(f32x4& a, f32x4& b, f32x4& c) { asm volatile("" : "+v"(a), "+v"(b), "+v"(c)); }
+__device__ __forceinline__ void pin(float& a, float& b, float& c) { asm volatile("" : "+v"(a), "+v"(b), "+v"(c)); }
+__device__ __forceinline__ void pin(bf16x8& x) {
+  u32x4 u = __builtin_bit_cast(u32x4, x);
+  asm volatile("" : "+v"(u));
+  x = __builtin_bit_cast(bf16x8, u);
+}
+
 // Max over the two 32-lane halves of a wave (lanes l and l ^ 32), on the
 // vector ALU: v_permlane32_swap with both operands x hands every lane both
 // halves' values.
