@@ -115,64 +115,73 @@ __global__ __launch_bounds__(NTHREADS) void avgpool_kernel(const PoolParams p) {
   }
 }
 
-// Each thread takes MU chunks, one grid stride apart, and issues all their
-// loads before the arithmetic.
+// The grid's y index walks the (batch, head) slices, so batch, head and the
+// gates are uniform per workgroup; within a slice, chunk i of the slice is
+// token i / cpr, chunk i % cpr (cpr a power of two: a shift and a mask).  Each
+// thread takes MU chunks, one grid stride apart, and issues all their loads
+// before the arithmetic.
 constexpr int MU = 4;
 
 template <bool BF16>
 __global__ __launch_bounds__(NTHREADS) void merge_kernel(const MergeParams p) {
   using C = Chunk<BF16>;
   const int cpr = p.head_dim / C::E;
-  const int64_t total = (int64_t)p.batch * p.heads * p.n_tokens * cpr;
+  const int cpr_log = __builtin_ctz((unsigned)cpr);
+  const int64_t per_slice = p.n_tokens * cpr;
   const size_t esz = BF16 ? 2 : 4;
+  const int64_t a_row = p.a_sn * (int64_t)esz, g_row = p.g_sn * (int64_t)esz, o_row = p.o_sn * (int64_t)esz;
+  const bool lse_mode = p.lse_a != nullptr;
   const int64_t stride = (int64_t)gridDim.x * NTHREADS;
-  for (int64_t i0 = (int64_t)blockIdx.x * NTHREADS + threadIdx.x; i0 < total; i0 += MU * stride) {
-    u32x4 ua[MU], ug[MU];
-    float la[MU], lg[MU];
-    int64_t orow[MU];
+  for (int bh = blockIdx.y; bh < p.batch * p.heads; bh += gridDim.y) {
+    const int h = bh % p.heads, b = bh / p.heads;
+    const char* ab = (const char*)p.a + (b * p.a_sb + h * p.a_sh) * (int64_t)esz;
+    const char* gb = (const char*)p.g + (b * p.g_sb + h * p.g_sh) * (int64_t)esz;
+    char* ob = (char*)p.out + (b * p.o_sb + h * p.o_sh) * (int64_t)esz;
+    const int64_t row0 = (int64_t)bh * p.n_tokens;   // the slice's first row of the LSE arrays
+    const float wa_gate = lse_mode ? 0.f : (p.w_a ? p.w_a[h] : 1.f);
+    const float wg_gate = lse_mode ? 0.f : p.w_g[h];
+    for (int64_t i0 = (int64_t)blockIdx.x * NTHREADS + threadIdx.x; i0 < per_slice; i0 += MU * stride) {
+      u32x4 ua[MU], ug[MU];
+      float la[MU], lg[MU];
 #pragma unroll
-    for (int u = 0; u < MU; ++u) {
-      const int64_t idx = i0 + u * stride;
-      if (idx < total) {
-        const int ch = (int)(idx % cpr);
-        const int64_t row = idx / cpr;
-        const int64_t n = row % p.n_tokens;
-        const int bh = (int)(row / p.n_tokens);
-        const int h = bh % p.heads, b = bh / p.heads;
-        ua[u] = __builtin_nontemporal_load((const u32x4*)((const char*)p.a + (b * p.a_sb + h * p.a_sh + n * p.a_sn) * esz + ch * 16));
-        ug[u] = __builtin_nontemporal_load((const u32x4*)((const char*)p.g + (b * p.g_sb + h * p.g_sh + n * p.g_sn) * esz + ch * 16));
-        if (p.lse_a != nullptr) {
-          la[u] = p.lse_a[row];
-          lg[u] = p.lse_g[row];
-        } else {
-          la[u] = p.w_a ? p.w_a[h] : 1.f;
-          lg[u] = p.w_g[h];
+      for (int u = 0; u < MU; ++u) {
+        const int64_t idx = i0 + u * stride;
+        if (idx < per_slice) {
+          const int64_t n = idx >> cpr_log;
+          const int ch = (int)(idx & (cpr - 1));
+          ua[u] = __builtin_nontemporal_load((const u32x4*)(ab + n * a_row + ch * 16));
+          ug[u] = __builtin_nontemporal_load((const u32x4*)(gb + n * g_row + ch * 16));
+          if (lse_mode) {
+            la[u] = p.lse_a[row0 + n];
+            lg[u] = p.lse_g[row0 + n];
+          }
         }
-        orow[u] = (b * p.o_sb + h * p.o_sh + n * p.o_sn) * esz + ch * 16;
       }
-    }
 #pragma unroll
-    for (int u = 0; u < MU; ++u) {
-      const int64_t idx = i0 + u * stride;
-      if (idx >= total) continue;
-      float wa = la[u], wg = lg[u];
-      if (p.lse_a != nullptr) {
-        // one softmax over the union of both key sets: weights from the two
-        // log-sum-exps (natural log) of the row
-        constexpr float LOG2E = 1.4426950408889634f, LN2 = 0.69314718055994531f;
-        const float m = fmaxf(la[u], lg[u]);
-        const float ea = __builtin_amdgcn_exp2f((la[u] - m) * LOG2E), eg = __builtin_amdgcn_exp2f((lg[u] - m) * LOG2E);
-        const float z = ea + eg;
-        wa = ea / z;
-        wg = eg / z;
-        if (p.lse_out != nullptr && idx % cpr == 0) p.lse_out[idx / cpr] = m + __builtin_amdgcn_logf(z) * LN2;
+      for (int u = 0; u < MU; ++u) {
+        const int64_t idx = i0 + u * stride;
+        if (idx >= per_slice) continue;
+        const int64_t n = idx >> cpr_log;
+        const int ch = (int)(idx & (cpr - 1));
+        float wa = wa_gate, wg = wg_gate;
+        if (lse_mode) {
+          // one softmax over the union of both key sets: weights from the two
+          // log-sum-exps (natural log) of the row
+          constexpr float LOG2E = 1.4426950408889634f, LN2 = 0.69314718055994531f;
+          const float m = fmaxf(la[u], lg[u]);
+          const float ea = __builtin_amdgcn_exp2f((la[u] - m) * LOG2E), eg = __builtin_amdgcn_exp2f((lg[u] - m) * LOG2E);
+          const float z = ea + eg;
+          wa = ea / z;
+          wg = eg / z;
+          if (p.lse_out != nullptr && ch == 0) p.lse_out[row0 + n] = m + __builtin_amdgcn_logf(z) * LN2;
+        }
+        float fa[C::E], fg[C::E];
+        C::unpack(ua[u], fa);
+        C::unpack(ug[u], fg);
+#pragma unroll
+        for (int e = 0; e < C::E; ++e) fa[e] = fmaf(wg, fg[e], wa * fa[e]);
+        __builtin_nontemporal_store(C::pack(fa), (u32x4*)(ob + n * o_row + ch * 16));
       }
-      float fa[C::E], fg[C::E];
-      C::unpack(ua[u], fa);
-      C::unpack(ug[u], fg);
-#pragma unroll
-      for (int e = 0; e < C::E; ++e) fa[e] = fmaf(wg, fg[e], wa * fa[e]);
-      __builtin_nontemporal_store(C::pack(fa), (u32x4*)((char*)p.out + orow[u]));
     }
   }
 }
@@ -238,11 +247,16 @@ hipError_t launch_avgpool(const PoolParams& p, int bf16, hipStream_t stream) {
 
 hipError_t launch_merge(const MergeParams& p, int bf16, hipStream_t stream) {
   const int cpr = p.head_dim / (bf16 ? 8 : 4);
-  const int64_t work = (int64_t)p.batch * p.heads * p.n_tokens * cpr;
+  const int64_t slices = (int64_t)p.batch * p.heads;
+  const int gy = (int)(slices < 65535 ? slices : 65535);
+  // about as many workgroups in all as grid_for gives, split over the slices
+  const int64_t per_slice = (p.n_tokens * cpr + (int64_t)NTHREADS * MU - 1) / ((int64_t)NTHREADS * MU);
+  const int64_t cap = (256 * 8 * 16 + gy - 1) / gy;
+  const dim3 grid((unsigned)(per_slice < cap ? (per_slice > 0 ? per_slice : 1) : cap), (unsigned)gy);
   if (bf16)
-    hipLaunchKernelGGL(merge_kernel<true>, dim3(grid_for((work + MU - 1) / MU)), dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL(merge_kernel<true>, grid, dim3(NTHREADS), 0, stream, p);
   else
-    hipLaunchKernelGGL(merge_kernel<false>, dim3(grid_for((work + MU - 1) / MU)), dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL(merge_kernel<false>, grid, dim3(NTHREADS), 0, stream, p);
   return hipGetLastError();
 }
 
