@@ -313,6 +313,8 @@ vdsa::PoolParams pool_params(const vdsa_problem* p, const int32_t* pool, const v
   pp.kh = pool[0]; pp.kw = pool[1];
   pp.Hp = (p->grid_h + pool[0] - 1) / pool[0];
   pp.Wp = (p->grid_w + pool[1] - 1) / pool[1];
+  pp.fd_wp = vdsa::make_fastdiv((uint32_t)pp.Wp);
+  pp.fd_hp = vdsa::make_fastdiv((uint32_t)pp.Hp);
   return pp;
 }
 

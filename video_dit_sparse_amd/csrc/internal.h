@@ -127,6 +127,7 @@ struct PoolParams {
   int32_t T, H, W;
   int32_t kh, kw;
   int32_t Hp, Wp;
+  FastDiv fd_wp, fd_hp;   // division by Wp and Hp (pooled cell coordinates)
 };
 
 struct MergeParams {
@@ -206,6 +207,7 @@ struct UnpoolParams {
   int32_t T, H, W;
   int32_t kh, kw;
   int32_t Hp, Wp;
+  FastDiv fd_wp, fd_hp;   // division by Wp and Hp (pooled cell coordinates)
 };
 
 // Frame-wise bilinear upsampling of a pooled tensor back to the grid

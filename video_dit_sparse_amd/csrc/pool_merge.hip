@@ -14,13 +14,10 @@
 // The streamed rows are read and written with nontemporal loads and stores:
 // nothing re-reads them soon, and keeping them out of the caches' normal
 // replacement raised the sustained rate by 5-14% (pooling about 6.1 TB/s).
-#include "internal.h"
+#include "box_common.h"
 
 namespace vdsa {
 namespace {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int NTHREADS = 256;
 
@@ -60,58 +57,65 @@ struct Chunk<false> {
   }
 };
 
+// The grid's y index walks the (batch, head) slices; within a slice, chunk i
+// is pooled cell i / cpr, chunk i % cpr (cpr a power of two), and the cell's
+// (t, i, j) come from divisions by invariants.
 template <bool BF16>
 __global__ __launch_bounds__(NTHREADS) void avgpool_kernel(const PoolParams p) {
   using C = Chunk<BF16>;
   constexpr int NF = 8;               // taps of a cell whose loads are in flight together
   const int cpr = p.head_dim / C::E;  // chunks per row
+  const int cpr_log = __builtin_ctz((unsigned)cpr);
   const int M = p.T * p.Hp * p.Wp;
-  const int64_t total = (int64_t)p.batch * p.heads * M * cpr;
+  const int64_t per_slice = (int64_t)M * cpr;
   const size_t esz = BF16 ? 2 : 4;
   const int64_t col_step = p.x_sn * (int64_t)esz, row_step = (int64_t)p.W * col_step;
-  for (int64_t idx = (int64_t)blockIdx.x * NTHREADS + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * NTHREADS) {
-    const int ch = (int)(idx % cpr);
-    const int64_t row = idx / cpr;
-    const int m = (int)(row % M);
-    const int bh = (int)(row / M);
+  for (int bh = blockIdx.y; bh < p.batch * p.heads; bh += gridDim.y) {
     const int h = bh % p.heads, b = bh / p.heads;
-    const int j = m % p.Wp, i = (m / p.Wp) % p.Hp, t = m / (p.Wp * p.Hp);
-    const int h0 = i * p.kh, h1 = min(p.H, h0 + p.kh);
-    const int w0 = j * p.kw, w1 = min(p.W, w0 + p.kw);
-    const int nw = w1 - w0, ntap = (h1 - h0) * nw;
-    // the cell's first token; taps in row-major order, NF loads issued before their adds
-    const char* cell = (const char*)p.x + (b * p.x_sb + h * p.x_sh) * esz + ch * 16 +
-                       (((int64_t)t * p.H + h0) * p.W + w0) * col_step;
-    float acc[C::E];
+    const char* xb = (const char*)p.x + (b * p.x_sb + h * p.x_sh) * (int64_t)esz;
+    char* yb = (char*)p.y + (b * p.y_sb + h * p.y_sh) * (int64_t)esz;
+    for (int64_t idx = (int64_t)blockIdx.x * NTHREADS + threadIdx.x; idx < per_slice;
+         idx += (int64_t)gridDim.x * NTHREADS) {
+      const int ch = (int)(idx & (cpr - 1));
+      const uint32_t m = (uint32_t)(idx >> cpr_log);
+      const uint32_t q = fast_div(m, p.fd_wp);   // t * Hp + i
+      const int j = (int)(m - q * (uint32_t)p.Wp);
+      const uint32_t t = fast_div(q, p.fd_hp);
+      const int i = (int)(q - t * (uint32_t)p.Hp);
+      const int h0 = i * p.kh, h1 = min(p.H, h0 + p.kh);
+      const int w0 = j * p.kw, w1 = min(p.W, w0 + p.kw);
+      const int nw = w1 - w0, ntap = (h1 - h0) * nw;
+      // the cell's first token; taps in row-major order, NF loads issued before their adds
+      const char* cell = xb + ch * 16 + (((int64_t)t * p.H + h0) * p.W + w0) * col_step;
+      float acc[C::E];
 #pragma unroll
-    for (int e = 0; e < C::E; ++e) acc[e] = 0.f;
-    int dh = 0, dw = 0;
-    for (int c0 = 0; c0 < ntap; c0 += NF) {
-      u32x4 u[NF];
+      for (int e = 0; e < C::E; ++e) acc[e] = 0.f;
+      int dh = 0, dw = 0;
+      for (int c0 = 0; c0 < ntap; c0 += NF) {
+        u32x4 u[NF];
 #pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        if (c0 + f < ntap) u[f] = __builtin_nontemporal_load((const u32x4*)(cell + dh * row_step + dw * col_step));
-        if (++dw == nw) {
-          dw = 0;
-          ++dh;
+        for (int f = 0; f < NF; ++f) {
+          if (c0 + f < ntap) u[f] = __builtin_nontemporal_load((const u32x4*)(cell + dh * row_step + dw * col_step));
+          if (++dw == nw) {
+            dw = 0;
+            ++dh;
+          }
+        }
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          if (c0 + f < ntap) {
+            float x[C::E];
+            C::unpack(u[f], x);
+#pragma unroll
+            for (int e = 0; e < C::E; ++e) acc[e] += x[e];
+          }
         }
       }
+      const float inv = 1.f / (float)ntap;
 #pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        if (c0 + f < ntap) {
-          float x[C::E];
-          C::unpack(u[f], x);
-#pragma unroll
-          for (int e = 0; e < C::E; ++e) acc[e] += x[e];
-        }
-      }
+      for (int e = 0; e < C::E; ++e) acc[e] *= inv;
+      __builtin_nontemporal_store(C::pack(acc), (u32x4*)(yb + (int64_t)m * p.y_sn * (int64_t)esz + ch * 16));
     }
-    const float inv = 1.f / (float)ntap;
-#pragma unroll
-    for (int e = 0; e < C::E; ++e) acc[e] *= inv;
-    char* yb = (char*)p.y + ((b * p.y_sb + h * p.y_sh) + (int64_t)m * p.y_sn) * esz + ch * 16;
-    __builtin_nontemporal_store(C::pack(acc), (u32x4*)yb);
   }
 }
 
@@ -235,24 +239,28 @@ int grid_for(int64_t work) {
 
 }  // namespace
 
+// Grid for per-slice work: the y index over the (batch, head) slices, about
+// as many workgroups in all as grid_for gives.
+dim3 slice_grid(int64_t slices, int64_t per_slice_work) {
+  const int gy = (int)(slices < 65535 ? slices : 65535);
+  const int64_t gx = (per_slice_work + NTHREADS - 1) / NTHREADS;
+  const int64_t cap = (256 * 8 * 16 + gy - 1) / gy;
+  return dim3((unsigned)(gx < cap ? (gx > 0 ? gx : 1) : cap), (unsigned)gy);
+}
+
 hipError_t launch_avgpool(const PoolParams& p, int bf16, hipStream_t stream) {
   const int cpr = p.head_dim / (bf16 ? 8 : 4);
-  const int64_t work = (int64_t)p.batch * p.heads * p.T * p.Hp * p.Wp * cpr;
+  const dim3 grid = slice_grid((int64_t)p.batch * p.heads, (int64_t)p.T * p.Hp * p.Wp * cpr);
   if (bf16)
-    hipLaunchKernelGGL(avgpool_kernel<true>, dim3(grid_for(work)), dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL(avgpool_kernel<true>, grid, dim3(NTHREADS), 0, stream, p);
   else
-    hipLaunchKernelGGL(avgpool_kernel<false>, dim3(grid_for(work)), dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL(avgpool_kernel<false>, grid, dim3(NTHREADS), 0, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_merge(const MergeParams& p, int bf16, hipStream_t stream) {
   const int cpr = p.head_dim / (bf16 ? 8 : 4);
-  const int64_t slices = (int64_t)p.batch * p.heads;
-  const int gy = (int)(slices < 65535 ? slices : 65535);
-  // about as many workgroups in all as grid_for gives, split over the slices
-  const int64_t per_slice = (p.n_tokens * cpr + (int64_t)NTHREADS * MU - 1) / ((int64_t)NTHREADS * MU);
-  const int64_t cap = (256 * 8 * 16 + gy - 1) / gy;
-  const dim3 grid((unsigned)(per_slice < cap ? (per_slice > 0 ? per_slice : 1) : cap), (unsigned)gy);
+  const dim3 grid = slice_grid((int64_t)p.batch * p.heads, (p.n_tokens * cpr + MU - 1) / MU);
   if (bf16)
     hipLaunchKernelGGL(merge_kernel<true>, grid, dim3(NTHREADS), 0, stream, p);
   else
