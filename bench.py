@@ -435,6 +435,26 @@ def main():
                              "effective_flop_per_call": bwd_flops,
                              "frac_of_peak": round(bwd_flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         log(f"[bench] backward: {bwd_ms:.2f} ms per call, {bwd_flops / (bwd_ms * 1e-3) / 1e12:.1f} effective TFLOP/s")
+        if w.pool_hw is not None:
+            # backward of the global branch from its own output and LSE:
+            # delta, K/V pooling, the dQ and dK/dV passes over the pooled
+            # keys and the pooling gradient; 2.5x the forward's FLOP
+            lse_g = torch.empty_like(lse_f)
+            o_g = V.global_pooled_attn_fwd(q, k, v, w.grid, w.pool_hw, scale=w.softmax_scale, lse=lse_g)[0]
+            ws_g = torch.empty(V.global_pooled_attn_bwd_workspace_size(w.batch, w.heads, w.head_dim, w.grid,
+                                                                       w.pool_hw, 1 if w.dtype == "bf16" else 0),
+                               dtype=torch.uint8, device=dev)
+            gbwd_ms = timed(lambda: V.global_pooled_attn_bwd(q, k, v, o_g, do, lse_g, w.grid, w.pool_hw,
+                                                             scale=w.softmax_scale, dq=grads[0], dk=grads[1],
+                                                             dv=grads[2], workspace=ws_g), args.bwd_steps)
+            gbwd_flops = 2.5 * fl["global"]
+            extra["backward_global"] = {"call": "global_pooled_attn_bwd", "ms_per_call": round(gbwd_ms, 3),
+                                        "effective_tflops": round(gbwd_flops / (gbwd_ms * 1e-3) / 1e12, 1),
+                                        "effective_flop_per_call": gbwd_flops,
+                                        "frac_of_peak": round(gbwd_flops / (gbwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            log(f"[bench] global backward: {gbwd_ms:.2f} ms per call, "
+                f"{gbwd_flops / (gbwd_ms * 1e-3) / 1e12:.1f} effective TFLOP/s")
+            del o_g, lse_g, ws_g
         del grads, do, o_f, lse_f
     if args.dense_steps > 0 and w.pool_hw is None:
         # the same kernel with a window covering the whole tile lattice = dense attention

@@ -26,6 +26,7 @@ from ._lib import (  # noqa: F401
     global_pooled_attn_fwd_noalloc,
     global_pooled_attn_merge_fwd,
     global_pooled_attn_bwd,
+    global_pooled_attn_bwd_workspace_size,
     global_pooled_attn_workspace_size,
     hier_pooled_attn_fwd,
     kv_avgpool_fwd,

@@ -486,6 +486,13 @@ def sta_attn_bwd(q, k, v, o, do, lse, grid, tile, window, shift=(0, 0, 0), scale
     return dq, dk, dv
 
 
+def global_pooled_attn_bwd_workspace_size(batch, heads, head_dim, grid, pool_hw, dtype_code=VDSA_BF16) -> int:
+    prob = make_problem(batch, heads, head_dim, grid, dtype_code, 1.0)
+    n = ctypes.c_size_t()
+    check(lib().global_pooled_attn_bwd_workspace_size(ctypes.byref(prob), _pool(pool_hw), ctypes.byref(n)))
+    return n.value
+
+
 def global_pooled_attn_bwd(q, k, v, o, do, lse, grid, pool_hw, scale=None, dq=None, dk=None, dv=None,
                            workspace=None, stream=None):
     """Gradients of ``global_pooled_attn_fwd`` through the pooling
