@@ -310,23 +310,63 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
   if (last_partial) process(nkb - 1, std::true_type{});
 
   // ---- epilogue: normalise and store (lane owns query l32; register v of
-  // block nb holds head_dim index 32*nb + 8*(v/4) + 4*g + v%4); with a merge,
-  // the row combines with the other branch's row read at the same positions
+  // block nb holds head_dim index 32*nb + 8*(v/4) + 4*g + v%4)
   const float l_tot = lacc[0];
   const float inv = 1.f / l_tot;
+  if (p.merge == MERGE_NONE) {
+    // The wave's 32 rows go through LDS (row-major, 8-byte pieces XOR-
+    // swizzled by row, free of bank conflicts) so that every store writes
+    // whole rows, 16 bytes per lane: a lane's own pieces of O are 8 bytes
+    // of each of 16 head_dim quarters, which as direct stores leave every
+    // cache line to be assembled from 8 partial writes.  The loop's last
+    // barrier has retired every read of the K/V stages.
+    constexpr int ROWB = 2 * HD;             // bytes per row
+    constexpr int NC8 = HD / 4;              // 8-byte pieces per row
+    constexpr int LPR = ROWB / 16;           // lanes per row in the stores
+    constexpr int RPI = 64 / LPR;            // rows per store instruction
+    char* stg = lds + wave * (32 * ROWB + 128);
+    uint32_t* toks = (uint32_t*)(stg + 32 * ROWB);   // row -> token, ~0u past the tile
+    const int xw = l32 & (NC8 - 1);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        bf16x4 ov;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(oacc[nb][4 * r4 + e] * inv);
+        const int c8 = 8 * nb + 2 * r4 + g;
+        *(u32x2*)(stg + l32 * ROWB + (c8 ^ xw) * 8) = __builtin_bit_cast(u32x2, ov);
+      }
+    if (g == 0) {
+      toks[l32] = q_valid ? qtok : ~0u;
+      if (q_valid && p.lse != nullptr) {
+        const int64_t N = (int64_t)p.qT * p.qH * p.qW;
+        p.lse[((int64_t)b * p.heads + h) * N + qtok] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+      }
+    }
+    __syncthreads();
+    const int j = lane % LPR;   // 16-byte piece of the row: 8-byte pieces 2j, 2j+1
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = i * RPI + lane / LPR;
+      const uint32_t tok = toks[r];
+      const int xr = r & (NC8 - 1);
+      u32x4 v = *(const u32x4*)(stg + r * ROWB + (((2 * j) ^ xr) & ~1) * 8);
+      if (xr & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+      if (tok != ~0u) *(u32x4*)(op + tok * o_row + 16 * j) = v;
+    }
+    return;
+  }
+  // with a merge, the row combines with the other branch's row read at the
+  // same positions
   if (q_valid) {
     float lse_row = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
-    float wa = 0.f, sc = inv;
-    if (p.merge != MERGE_NONE) {
-      const RowMerge rm = row_merge(p, b, h, qtok, lse_row);
-      wa = rm.wa;
-      sc = rm.wb * inv;
-      lse_row = rm.lse;
-    }
+    const RowMerge rm = row_merge(p, b, h, qtok, lse_row);
+    const float wa = rm.wa;
+    const float sc = rm.wb * inv;
+    lse_row = rm.lse;
     char* dst = op + qtok * o_row + 8 * g;
-    const char* src = p.merge != MERGE_NONE
-                          ? (const char*)p.ol + 2 * (b * p.ol_sb + h * p.ol_sh) + qtok * (2u * (uint32_t)p.ol_sn) + 8 * g
-                          : nullptr;
+    const char* src = (const char*)p.ol + 2 * (b * p.ol_sb + h * p.ol_sh) + qtok * (2u * (uint32_t)p.ol_sn) + 8 * g;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -334,13 +374,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void box_attn_bf16_kernel(const BoxAtt
         float f[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) f[e] = oacc[nb][4 * r4 + e] * sc;
-        if (p.merge != MERGE_NONE) {
-          const u32x2 raw = *(const u32x2*)(src + 64 * nb + 16 * r4);
-          float a[4];
-          bf16x4_to_f32(raw[0], raw[1], a);
+        const u32x2 raw = *(const u32x2*)(src + 64 * nb + 16 * r4);
+        float a[4];
+        bf16x4_to_f32(raw[0], raw[1], a);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) f[e] = fmaf(wa, a[e], f[e]);
-        }
+        for (int e = 0; e < 4; ++e) f[e] = fmaf(wa, a[e], f[e]);
         bf16x4 ov;
 #pragma unroll
         for (int e = 0; e < 4; ++e) ov[e] = (__bf16)f[e];
