@@ -42,20 +42,12 @@ __device__ __forceinline__ float xhalf_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float xhalf_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-// Max / sum over the four 16-lane rows of a wave (lanes l % 16 + 16 G):
+// Max over the four 16-lane rows of a wave (lanes l % 16 + 16 G):
 // v_permlane16_swap pairs rows (0,1) and (2,3), then the 32-lane swap pairs
 // the halves.
 __device__ __forceinline__ float xrow4_max(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return xhalf_max(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
-}
-__device__ __forceinline__ float xrow4_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return xhalf_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
 }
 
 // Weights of the epilogue merge for one query row: out = wa * o_other +
