@@ -261,6 +261,11 @@ SMALL_GLOBAL = [
     ("pool8x8_bf16", (2, 17, 30), (8, 8), 1, 128, "bf16"),
     ("pool_f32_d64", (3, 9, 10), (2, 3), 2, 64, "f32"),
     ("pool1_dense_bf16", (2, 6, 10), (1, 1), 1, 128, "bf16"),
+    # 384-query blocks over the whole grid, the pooled keys walked in token
+    # order: 540 keys (eight full 64-key blocks and a partial one), and 512
+    # (whole blocks only)
+    ("pool2x2_multi_block_bf16", (3, 20, 36), (2, 2), 2, 128, "bf16"),
+    ("pool2x2_whole_blocks_bf16", (4, 16, 32), (2, 2), 1, 128, "bf16"),
 ]
 
 

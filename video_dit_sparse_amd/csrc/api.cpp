@@ -201,13 +201,14 @@ int64_t max_tile_volume(const vdsa::BoxAttnParams& bp) {
          max_tile_extent(bp.qW, bp.bW, bp.sW);
 }
 
-// Key walk of the 384- and 192-query kernels: tile by tile when every tile of the
-// lattice is full (no lattice shift, grid dims multiples of the tile) and a
-// tile frame holds exactly one 64-key block (tile h x w = 64), on the rolled
-// grid for the cyclic mode; else the raster walk over the key box.  Sliding
-// tiles only (not pooled or dense keys).
+// Key walk of the 384- and 192-query kernels: dense keys in token order (the
+// 384-query kernel only); tile by tile when every tile of the lattice is full
+// (no lattice shift, grid dims multiples of the tile) and a tile frame holds
+// exactly one 64-key block (tile h x w = 64), on the rolled grid for the
+// cyclic mode; else the raster walk over the key box.
 int tile_walk_mode(const vdsa::BoxAttnParams& bp) {
-  if (bp.dense_keys || bp.kpT > 1 || bp.kpH > 1 || bp.kpW > 1) return 0;
+  if (bp.dense_keys) return (bp.rlT | bp.rlH | bp.rlW) ? 0 : 3;
+  if (bp.kpT > 1 || bp.kpH > 1 || bp.kpW > 1) return 0;
   if (bp.sT || bp.sH || bp.sW || bp.bH * bp.bW != 64) return 0;
   if (bp.qT % bp.bT || bp.qH % bp.bH || bp.qW % bp.bW) return 0;
   if (bp.kT != bp.qT || bp.kH != bp.qH || bp.kW != bp.qW) return 0;
@@ -218,8 +219,8 @@ int tile_walk_mode(const vdsa::BoxAttnParams& bp) {
 const char* attn_kernel_name(const vdsa_problem* prob, const vdsa::BoxAttnParams& bp) {
   const bool d128 = prob->head_dim == 128;
   if (prob->dtype == VDSA_F32) return d128 ? "box_attn_f32_kernel<128>" : "box_attn_f32_kernel<64>";
-  static const char* const pp_names[3] = {"box_attn_bf16_pp_kernel<0>", "box_attn_bf16_pp_kernel<1>",
-                                          "box_attn_bf16_pp_kernel<2>"};
+  static const char* const pp_names[4] = {"box_attn_bf16_pp_kernel<0>", "box_attn_bf16_pp_kernel<1>",
+                                          "box_attn_bf16_pp_kernel<2>", "box_attn_bf16_pp_kernel<3>"};
   switch (choose_bf16_shape(max_tile_volume(bp), prob->head_dim).kernel) {
     case K_PP_8W: return pp_names[tile_walk_mode(bp)];
     case K_M16_4W:

@@ -178,8 +178,14 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
   // rows' byte offsets from the block's first token
   const int w_log = __builtin_ctz((unsigned)max(p.bW, 1));   // bW divides 64: a power of two
   TileCursor cur;
-  if constexpr (WALK != WALK_RASTER) cur.init(p, kb);
+  if constexpr (WALK == WALK_TILES || WALK == WALK_TILES_ROLLED) cur.init(p, kb);
   uint32_t k_off[KDMA_W], v_off[VPT];
+  if constexpr (WALK == WALK_LINEAR) {
+#pragma unroll
+    for (int i = 0; i < KDMA_W; ++i) k_off[i] = (uint32_t)k_row_of(i) * k_row + k_chunk_of(i);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) v_off[i] = (uint32_t)(VPT * vk + i) * v_row + (uint32_t)vc * 16u;
+  }
   if constexpr (WALK == WALK_TILES) {
 #pragma unroll
     for (int i = 0; i < KDMA_W; ++i)
@@ -205,6 +211,20 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
         const uint32_t tok = (uint32_t)__shfl((int)my_tok, VPT * vk + i, 64);
         vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrsrc, (int)(tok * v_row + vc * 16), 0, 0));
       }
+    } else if constexpr (WALK == WALK_LINEAR) {
+      // rows past the box (only in the last block) are clamped to its last
+      // key at the same 16-byte piece, as the raster walk repeats that key
+      const uint32_t base = (uint32_t)blk * BLOCK_N;
+      const uint32_t kb_off = base * k_row, vb_off = base * v_row;
+      const uint32_t k_last = (uint32_t)(kvol - 1) * k_row, v_last = (uint32_t)(kvol - 1) * v_row;
+#pragma unroll
+      for (int i = 0; i < KDMA_W; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void*)(st + (wave * KDMA_W + i) * 1024), 16,
+                                                 (int)min(kb_off + k_off[i], k_last + k_chunk_of(i)), 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < VPT; ++i)
+        vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                vrsrc, (int)min(vb_off + v_off[i], v_last + (uint32_t)vc * 16u), 0, 0));
     } else {
       int t, h, w;
       cur.next(p, kb, t, h, w);
@@ -471,6 +491,8 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
 hipError_t launch_box_attn_bf16_pp(const BoxAttnParams& p, hipStream_t stream) {
   if (p.tile_walk == WALK_TILES)
     hipLaunchKernelGGL(box_attn_bf16_pp_kernel<WALK_TILES>, dim3(p.total_wg), dim3(NW * 64), 0, stream, p);
+  else if (p.tile_walk == WALK_LINEAR)
+    hipLaunchKernelGGL(box_attn_bf16_pp_kernel<WALK_LINEAR>, dim3(p.total_wg), dim3(NW * 64), 0, stream, p);
   else if (p.tile_walk == WALK_TILES_ROLLED)
     hipLaunchKernelGGL(box_attn_bf16_pp_kernel<WALK_TILES_ROLLED>, dim3(p.total_wg), dim3(NW * 64), 0, stream, p);
   else

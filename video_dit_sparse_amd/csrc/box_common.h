@@ -202,8 +202,11 @@ __device__ __forceinline__ void tile_boxes(const BoxAttnParams& p, int tile, Box
 //                      first token;
 //   WALK_TILES_ROLLED  the same on the rolled grid of the cyclic mode (uniform
 //                      frame, per-lane unroll of h and w), visiting keys in
-//                      the order the clipped walk visits rolled tensors.
-enum { WALK_RASTER = 0, WALK_TILES = 1, WALK_TILES_ROLLED = 2 };
+//                      the order the clipped walk visits rolled tensors;
+//   WALK_LINEAR        dense keys (the box is the whole key grid, unrolled):
+//                      key j is token j, so block b is tokens 64b .. 64b+63
+//                      and a lane's rows again sit at fixed offsets.
+enum { WALK_RASTER = 0, WALK_TILES = 1, WALK_TILES_ROLLED = 2, WALK_LINEAR = 3 };
 
 // Cursor of a tile walk: the next block is frame f of key-box tile
 // (tt, th, tw); the box is whole tiles, so its extents are multiples of the

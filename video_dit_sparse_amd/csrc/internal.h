@@ -72,7 +72,8 @@ struct BoxAttnParams {
   int32_t qblocks;            // query blocks per tile
   int32_t variant;            // which kernel shape the launcher runs (set by the host)
   int32_t tile_walk;          // 384-query kernel's key walk: 0 raster, 1 whole tiles, 2 whole
-                              // tiles of the rolled grid (set by the host; see attn_bf16_pp.hip)
+                              // tiles of the rolled grid, 3 the whole key grid in token order
+                              // (set by the host; see box_common.h)
   int32_t total_wg;           // batch * heads * tiles * qblocks
   float scale_log2e;          // scale * log2(e)
   // Optional merge with another branch's output in the epilogue (merge !=
