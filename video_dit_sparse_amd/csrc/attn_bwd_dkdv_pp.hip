@@ -77,6 +77,10 @@ __device__ __forceinline__ void row_bcast8(int x, float (&a)[8], float (&b)[8]) 
   b[4] = row_bcast<12>(x); b[5] = row_bcast<13>(x); b[6] = row_bcast<14>(x); b[7] = row_bcast<15>(x);
 }
 
+// LIN: the iterated box is the whole grid in token order (dense keys: every
+// query of the global branch), so query j is token j and a lane's rows sit at
+// fixed offsets from the chunk's first token; else raster order over the box.
+template <bool LIN>
 __global__ __launch_bounds__(NW * 64) void box_attn_bwd_dkdv_pp_kernel(const BoxBwdParams P) {
   __shared__ __attribute__((aligned(16))) char lds[NSTAGE * STAGE];
   const BoxAttnParams& g = P.g;
@@ -180,15 +184,17 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bwd_dkdv_pp_kernel(const Box
   auto load_chunk = [&](int c, auto par) __attribute__((always_inline)) {
     constexpr int PAR = decltype(par)::value;
     char* st = stage_of(c);
-    const uint32_t my_tok = iter_token(c * CHUNK + (lane & 31));
-    const uint32_t ftok = (uint32_t)__shfl((int)my_tok, frag_row, 64);
+    // rows past the box repeat its last token (their terms are masked)
+    auto lin_tok = [&](int r) { return (uint32_t)min(c * CHUNK + r, ivol - 1); };
+    const uint32_t my_tok = LIN ? lin_tok(lane & 31) : iter_token(c * CHUNK + (lane & 31));
+    const uint32_t ftok = LIN ? lin_tok(frag_row) : (uint32_t)__shfl((int)my_tok, frag_row, 64);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(qrsrc, (lds_void*)(st + XF + wave * 1024), 16,
                                              (int)(ftok * q_row + frag_col), 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(dorsrc, (lds_void*)(st + YF + wave * 1024), 16,
                                              (int)(ftok * do_row + frag_col), 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const uint32_t tok = (uint32_t)__shfl((int)my_tok, 2 * vk + i, 64);
+      const uint32_t tok = LIN ? lin_tok(2 * vk + i) : (uint32_t)__shfl((int)my_tok, 2 * vk + i, 64);
       treg[PAR][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(trsrc, (int)(tok * t_row + vc * 16), 0, 0));
     }
     ldreg[PAR] = ld_src[my_tok];
@@ -405,7 +411,10 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bwd_dkdv_pp_kernel(const Box
 }  // namespace
 
 hipError_t launch_attn_bwd_dkdv_pp(const BoxBwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(box_attn_bwd_dkdv_pp_kernel, dim3(p.g.total_wg), dim3(NW * 64), 0, stream, p);
+  if (p.g.dense_keys && !(p.g.rlT | p.g.rlH | p.g.rlW))
+    hipLaunchKernelGGL(box_attn_bwd_dkdv_pp_kernel<true>, dim3(p.g.total_wg), dim3(NW * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL(box_attn_bwd_dkdv_pp_kernel<false>, dim3(p.g.total_wg), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -64,6 +64,10 @@ static_assert(FPW * (NW / 2) == NFRAG, "fragments per wave");
 static_assert(NSTAGE * STAGE <= 160 * 1024, "LDS");
 static_assert((NW / 2) * 64 * OT * ND * 16 <= NSTAGE * STAGE, "partial dQ hand-over fits the ring");
 
+// LIN: the iterated box is the whole key grid in token order (dense keys:
+// the global branch's pooled keys), so key j is token j and a lane's rows sit
+// at fixed offsets from the chunk's first token; else raster order over the box.
+template <bool LIN>
 __global__ __launch_bounds__(NW * 64) void box_attn_bwd_dq_pp_kernel(const BoxBwdParams P) {
   __shared__ __attribute__((aligned(16))) char lds[NSTAGE * STAGE];
   const BoxAttnParams& g = P.g;
@@ -169,12 +173,14 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bwd_dq_pp_kernel(const BoxBw
   auto load_chunk = [&](int c, auto par) {
     constexpr int PAR = decltype(par)::value;
     char* st = stage_of(c);
-    const uint32_t my_tok = iter_token(c * CHUNK + (lane & 31));
+    // rows past the box repeat its last token (their terms are masked)
+    auto lin_tok = [&](int r) { return (uint32_t)min(c * CHUNK + r, ivol - 1); };
+    const uint32_t my_tok = LIN ? 0u : iter_token(c * CHUNK + (lane & 31));
 #pragma unroll
     for (int i = 0; i < FPW; ++i) {
       const int f = w4 * FPW + i;
       const int t = f / KS, ks = f % KS;
-      const uint32_t ftok = (uint32_t)__shfl((int)my_tok, frow_base + 4 * t, 64);
+      const uint32_t ftok = LIN ? lin_tok(frow_base + 4 * t) : (uint32_t)__shfl((int)my_tok, frow_base + 4 * t, 64);
       const uint32_t col = (uint32_t)(4 * ks + G) * 16u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void*)(st + XF + f * 1024), 16, (int)(ftok * k_row + col),
                                                0, 0, 0);
@@ -183,7 +189,7 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bwd_dq_pp_kernel(const BoxBw
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const uint32_t tok = (uint32_t)__shfl((int)my_tok, 2 * vk + i, 64);
+      const uint32_t tok = LIN ? lin_tok(2 * vk + i) : (uint32_t)__shfl((int)my_tok, 2 * vk + i, 64);
       treg[PAR][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krsrc, (int)(tok * k_row + vc * 16), 0, 0));
     }
   };
@@ -391,7 +397,10 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bwd_dq_pp_kernel(const BoxBw
 }  // namespace
 
 hipError_t launch_attn_bwd_dq_pp(const BoxBwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(box_attn_bwd_dq_pp_kernel, dim3(p.g.total_wg), dim3(NW * 64), 0, stream, p);
+  if (p.g.dense_keys && !(p.g.rlT | p.g.rlH | p.g.rlW))
+    hipLaunchKernelGGL(box_attn_bwd_dq_pp_kernel<true>, dim3(p.g.total_wg), dim3(NW * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL(box_attn_bwd_dq_pp_kernel<false>, dim3(p.g.total_wg), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
