@@ -63,6 +63,8 @@ MERGE_CASES = [
     ("q768_bf16", 2, (4, 12, 16), (2, 4, 4), (1, 3, 3), (0, 0, 0), (2, 4), 2, 128, "bf16"),
     ("tile384_b2h3_bf16", 2, (6, 16, 16), (6, 8, 8), (1, 1, 3), (0, 0, 0), (4, 4), 3, 128, "bf16"),
     ("q576_bf16", 1, (3, 12, 16), (3, 4, 4), (1, 1, 3), (1, 2, 2), (3, 4), 1, 128, "bf16"),
+    # 2160 queries in six 384-query blocks of the global call, the last one ragged
+    ("q2160_ragged_bf16", 1, (3, 20, 36), (3, 4, 4), (1, 3, 3), (0, 0, 0), (2, 2), 2, 128, "bf16"),
     ("d64_bf16", 1, (3, 9, 10), (3, 3, 5), (1, 3, 1), (0, 1, 2), (2, 3), 2, 64, "bf16"),
     ("d64_f32", 1, (3, 9, 10), (3, 3, 5), (1, 3, 1), (0, 0, 0), (2, 3), 2, 64, "f32"),
 ]

@@ -442,6 +442,74 @@ __global__ __launch_bounds__(NW * 64) void box_attn_bf16_pp_kernel(const BoxAttn
   mphase(true, stage_of(nkb - 1), 1, false, stage_of(nkb - 1), 0);
   if (!grp_b) phase_barrier();
 
+  // ---- epilogue of the dense-key instance (the global branch, which carries
+  // the fused merges) with a merge: each row combines with the other branch's
+  // row at the positions it is written to (so out may be that tensor itself).
+  // The wave's scaled rows go through LDS in fp32, one query tile at a time
+  // (row-major, 16-byte pieces XOR-swizzled by row), so that the other
+  // branch's rows are read and the merged rows written whole, 16 bytes per
+  // lane and 16 lanes per row, with the same single rounding as below.  The
+  // areas lie in the two stages the other group's last products do not read,
+  // four waves to a stage; LDS requests of a wave complete in order, so a
+  // wave reuses its area for its three tiles without waiting.  (In the other
+  // instances the longer epilogue makes the main loop spill.)
+  if constexpr (WALK == WALK_LINEAR) {
+    if (p.merge != MERGE_NONE) {
+      char* stg = stage_of(nkb + (wave & 1)) + (wave >> 1) * (16 * 512);
+      const char* olp = (const char*)p.ol + 2 * (b * p.ol_sb + h * p.ol_sh);
+      const uint32_t ol_row = 2u * (uint32_t)p.ol_sn;
+      const int j = lane & 15;   // this lane's 16-byte piece of a bf16 row: head_dim 8j .. 8j+7
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const float l_tot = lacc[qt][0];
+        const float inv = 1.f / l_tot;
+        float wa = 0.f, sc = 0.f;
+        if (q_valid[qt]) {
+          const float lse_row = (m_run[qt] + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+          const RowMerge rm = row_merge(p, b, h, qtok[qt], lse_row);
+          wa = rm.wa;
+          sc = rm.wb * inv;
+          if (p.lse != nullptr && G == 0) {
+            const int64_t N = (int64_t)p.qT * p.qH * p.qW;
+            p.lse[((int64_t)b * p.heads + h) * N + qtok[qt]] = rm.lse;
+          }
+        }
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) {
+          f32x4 f;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) f[v] = oacc[dt][qt][v] * sc;
+          *(f32x4*)(stg + l16 * 512 + ((4 * dt + G) ^ l16) * 16) = f;
+        }
+        const uint32_t tok_own = q_valid[qt] ? qtok[qt] : ~0u;
+        asm volatile("" ::: "memory");
+#pragma unroll 1
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * i + (lane >> 4);   // row of the tile: its owner is lane r
+          const uint32_t tok = (uint32_t)__shfl((int)tok_own, r, 64);
+          const float war = __shfl(wa, r, 64);
+          const f32x4 f0 = *(const f32x4*)(stg + r * 512 + ((2 * j) ^ r) * 16);
+          const f32x4 f1 = *(const f32x4*)(stg + r * 512 + ((2 * j + 1) ^ r) * 16);
+          if (tok != ~0u) {
+            const u32x4 raw = *(const u32x4*)(olp + tok * ol_row + 16 * j);
+            float a0[4], a1[4];
+            bf16x4_to_f32(raw[0], raw[1], a0);
+            bf16x4_to_f32(raw[2], raw[3], a1);
+            bf16x8 ov;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              ov[v] = (__bf16)fmaf(war, a0[v], f0[v]);
+              ov[4 + v] = (__bf16)fmaf(war, a1[v], f1[v]);
+            }
+            *(bf16x8*)(op + tok * o_row + 16 * j) = ov;
+          }
+        }
+        asm volatile("" ::: "memory");
+      }
+      return;
+    }
+  }
+
   // ---- epilogue: O^T register v of tile (dt, qt) is head_dim 16dt + 4G + v;
   // with a merge, each row combines with the other branch's row (read at the
   // positions this lane writes, so out may be that tensor itself).
