@@ -929,6 +929,8 @@ vdsa_status compressed_global_attn_fwd(const vdsa_problem* prob, const int32_t p
   up.o_sb = o_strides->b; up.o_sh = o_strides->h; up.o_sn = o_strides->n;
   up.batch = prob->batch; up.heads = prob->heads; up.head_dim = prob->head_dim;
   up.T = prob->grid_t; up.H = prob->grid_h; up.W = prob->grid_w; up.Hp = Hp; up.Wp = Wp;
+  up.fd_hw = vdsa::make_fastdiv((uint32_t)(up.H * up.W));
+  up.fd_w = vdsa::make_fastdiv((uint32_t)up.W);
   e = vdsa::launch_upsample(up, bf16, st);
   if (e != hipSuccess) return fail(VDSA_ERR_HIP, "upsampling launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -1059,6 +1061,10 @@ vdsa_status global_pooled_attn_bwd(const vdsa_problem* prob, const int32_t pool_
     up.T = prob->grid_t; up.H = prob->grid_h; up.W = prob->grid_w;
     up.kh = pool_hw[0]; up.kw = pool_hw[1];
     up.Hp = Hp; up.Wp = Wp;
+    up.fd_hw = vdsa::make_fastdiv((uint32_t)(up.H * up.W));
+    up.fd_w = vdsa::make_fastdiv((uint32_t)up.W);
+    up.fd_kh = vdsa::make_fastdiv((uint32_t)up.kh);
+    up.fd_kw = vdsa::make_fastdiv((uint32_t)up.kw);
     e = vdsa::launch_unpool_grad(up, prob->dtype == VDSA_BF16, st);
     if (e != hipSuccess) return fail(VDSA_ERR_HIP, "pooling-gradient launch failed: %s", hipGetErrorString(e));
   }

@@ -176,46 +176,50 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const RowDotParams p) {
   if (row < rows && ch == 0) p.out[row] = acc;
 }
 
-// g[token] = gp[cell(token)] / count(cell): one thread per 16 bytes of output
+// g[token] = gp[cell(token)] / count(cell): one thread per 16 bytes of output.
+// The grid's y index walks the (batch, head) slices; within a slice, chunk i
+// is token i / cpr, piece i % cpr (a shift and a mask), and a token's frame,
+// row and cell come from division by invariants.
 template <bool BF16>
 __global__ __launch_bounds__(256) void unpool_grad_kernel(const UnpoolParams p) {
   constexpr int E = BF16 ? 8 : 4;
   const int cpr = p.head_dim / E;
+  const int cpr_log = __builtin_ctz((unsigned)cpr);
   const int64_t N = (int64_t)p.T * p.H * p.W;
-  const int64_t total = (int64_t)p.batch * p.heads * N * cpr;
-  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
-    const int ch = (int)(idx % cpr);
-    const int64_t row = idx / cpr;
-    const int64_t n = row % N;
-    const int bh = (int)(row / N);
+  const int64_t per_slice = N * cpr;
+  const int64_t g_row = p.g_sn * (BF16 ? 2 : 4);
+  for (int bh = blockIdx.y; bh < p.batch * p.heads; bh += gridDim.y) {
     const int h = bh % p.heads, b = bh / p.heads;
-    const int t = (int)(n / ((int64_t)p.H * p.W)), rem = (int)(n % ((int64_t)p.H * p.W));
-    const int hh = rem / p.W, ww = rem % p.W;
-    const int ci = hh / p.kh, cj = ww / p.kw;
-    const int cnt = (min(p.H, (ci + 1) * p.kh) - ci * p.kh) * (min(p.W, (cj + 1) * p.kw) - cj * p.kw);
-    const float inv = 1.f / (float)cnt;
-    const int64_t m = ((int64_t)t * p.Hp + ci) * p.Wp + cj;
-    const float* src = p.gp + ((int64_t)bh * p.Hp * p.Wp * p.T + m) * p.head_dim + ch * E;
-    char* dst = (char*)p.g + (b * p.g_sb + h * p.g_sh + n * p.g_sn) * (BF16 ? 2 : 4) + ch * 16;
-    if (BF16) {
-      uint32_t w[4];
+    const float* gpb = p.gp + (int64_t)bh * p.Hp * p.Wp * p.T * p.head_dim;
+    char* gb = (char*)p.g + (b * p.g_sb + h * p.g_sh) * (BF16 ? 2 : 4);
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < per_slice; i += (int64_t)gridDim.x * 256) {
+      const uint32_t n = (uint32_t)(i >> cpr_log);
+      const int ch = (int)(i & (cpr - 1));
+      const uint32_t t = fast_div(n, p.fd_hw);
+      const uint32_t rem = n - t * p.fd_hw.d;
+      const uint32_t hh = fast_div(rem, p.fd_w);
+      const uint32_t ww = rem - hh * p.fd_w.d;
+      const int ci = (int)fast_div(hh, p.fd_kh), cj = (int)fast_div(ww, p.fd_kw);
+      const int cnt = (min(p.H, (ci + 1) * p.kh) - ci * p.kh) * (min(p.W, (cj + 1) * p.kw) - cj * p.kw);
+      const float inv = 1.f / (float)cnt;
+      const int64_t m = ((int64_t)t * p.Hp + ci) * p.Wp + cj;
+      const float* src = gpb + m * p.head_dim + ch * E;
+      char* dst = gb + (int64_t)n * g_row + ch * 16;
+      if (BF16) {
+        uint32_t w[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const __bf16 lo = (__bf16)(src[2 * i] * inv), hi = (__bf16)(src[2 * i + 1] * inv);
-        w[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        for (int k = 0; k < 4; ++k) {
+          const __bf16 lo = (__bf16)(src[2 * k] * inv), hi = (__bf16)(src[2 * k + 1] * inv);
+          w[k] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        }
+        *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
+      } else {
+        *(float4*)dst = make_float4(src[0] * inv, src[1] * inv, src[2] * inv, src[3] * inv);
       }
-      *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
-    } else {
-      *(float4*)dst = make_float4(src[0] * inv, src[1] * inv, src[2] * inv, src[3] * inv);
     }
   }
 }
 
-int grid_for(int64_t work) {
-  const int64_t blocks = (work + 255) / 256;
-  const int64_t cap = 256 * 8 * 16;
-  return (int)(blocks < cap ? (blocks > 0 ? blocks : 1) : cap);
-}
 
 }  // namespace
 
@@ -259,11 +263,13 @@ hipError_t launch_rowdot(const RowDotParams& p, int bf16, hipStream_t stream) {
 }
 
 hipError_t launch_unpool_grad(const UnpoolParams& p, int bf16, hipStream_t stream) {
-  const int64_t work = (int64_t)p.batch * p.heads * p.T * p.H * p.W * (p.head_dim / (bf16 ? 8 : 4));
+  // every chunk its own thread: no cap on the grid
+  const int64_t per_slice = (int64_t)p.T * p.H * p.W * (p.head_dim / (bf16 ? 8 : 4));
+  const dim3 grid = slice_grid((int64_t)p.batch * p.heads, per_slice, (int64_t)1 << 40);
   if (bf16)
-    hipLaunchKernelGGL(unpool_grad_kernel<true>, dim3(grid_for(work)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(unpool_grad_kernel<true>, grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL(unpool_grad_kernel<false>, dim3(grid_for(work)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(unpool_grad_kernel<false>, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

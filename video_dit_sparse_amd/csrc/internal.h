@@ -208,7 +208,8 @@ struct UnpoolParams {
   int32_t T, H, W;
   int32_t kh, kw;
   int32_t Hp, Wp;
-  FastDiv fd_wp, fd_hp;   // division by Wp and Hp (pooled cell coordinates)
+  FastDiv fd_hw, fd_w;    // division by H*W and W (a token's frame and row)
+  FastDiv fd_kh, fd_kw;   // division by kh and kw (a token's cell)
 };
 
 // Frame-wise bilinear upsampling of a pooled tensor back to the grid
@@ -219,6 +220,7 @@ struct UpsampleParams {
   int64_t o_sb, o_sh, o_sn;
   int32_t batch, heads, head_dim;
   int32_t T, H, W, Hp, Wp;
+  FastDiv fd_hw, fd_w;    // division by H*W and W (a token's frame and row)
 };
 
 // The static device scratch of the entry point that allocates nothing
@@ -227,6 +229,11 @@ struct UpsampleParams {
 // with hipGetSymbolAddress on the first call for that device.
 constexpr size_t STATIC_SCRATCH_BYTES = size_t(128) << 20;
 hipError_t static_scratch(void** ptr);
+
+// Grid for per-slice work: the y index over the (batch, head) slices, at most
+// max_wg workgroups of 256 threads in all (the kernels' loops stride over the
+// rest).  pool_merge.hip.
+dim3 slice_grid(int64_t slices, int64_t per_slice_work, int64_t max_wg);
 
 // Launchers: return hipSuccess or the launch error.  They assume the
 // parameters were validated.

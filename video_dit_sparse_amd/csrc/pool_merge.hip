@@ -194,43 +194,51 @@ __global__ __launch_bounds__(NTHREADS) void merge_kernel(const MergeParams p) {
 }
 
 // One thread per 16-byte chunk of an output row: the four pooled taps of the
-// row's position, fp32 weights.
+// row's position, fp32 weights.  The grid's y index walks the (batch, head)
+// slices; within a slice, chunk i is token i / cpr, piece i % cpr (a shift and
+// a mask), and a token's frame and row come from division by invariants.
 template <bool BF16>
 __global__ __launch_bounds__(NTHREADS) void upsample_kernel(const UpsampleParams p) {
   using C = Chunk<BF16>;
   const int cpr = p.head_dim / C::E;
+  const int cpr_log = __builtin_ctz((unsigned)cpr);
   const int64_t N = (int64_t)p.T * p.H * p.W;
   const int64_t M = (int64_t)p.T * p.Hp * p.Wp;
-  const int64_t total = (int64_t)p.batch * p.heads * N * cpr;
+  const int64_t per_slice = N * cpr;
   const size_t esz = BF16 ? 2 : 4;
+  const int64_t o_row = p.o_sn * (int64_t)esz;
+  const int64_t tap_row = (int64_t)p.head_dim * esz;
   const float sy = (float)p.Hp / (float)p.H, sx = (float)p.Wp / (float)p.W;
-  for (int64_t idx = (int64_t)blockIdx.x * NTHREADS + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * NTHREADS) {
-    const int ch = (int)(idx % cpr);
-    const int64_t row = idx / cpr;
-    const int64_t n = row % N;
-    const int bh = (int)(row / N);
+  for (int bh = blockIdx.y; bh < p.batch * p.heads; bh += gridDim.y) {
     const int h = bh % p.heads, b = bh / p.heads;
-    const int t = (int)(n / ((int64_t)p.H * p.W)), rem = (int)(n % ((int64_t)p.H * p.W));
-    const int y = rem / p.W, x = rem % p.W;
-    const float fy = fmaxf(((float)y + 0.5f) * sy - 0.5f, 0.f), fx = fmaxf(((float)x + 0.5f) * sx - 0.5f, 0.f);
-    const int y0 = min((int)fy, p.Hp - 1), x0 = min((int)fx, p.Wp - 1);
-    const int y1 = min(y0 + 1, p.Hp - 1), x1 = min(x0 + 1, p.Wp - 1);
-    const float ly = fy - (float)y0, lx = fx - (float)x0;
-    const char* base = (const char*)p.xp + ((int64_t)bh * M + (int64_t)t * p.Hp * p.Wp) * p.head_dim * esz + ch * 16;
-    auto tap = [&](int yy, int xx, float (&f)[C::E]) {
-      C::unpack(*(const u32x4*)(base + ((int64_t)yy * p.Wp + xx) * p.head_dim * esz), f);
-    };
-    float a[C::E], c[C::E], acc[C::E];
-    tap(y0, x0, a);
-    tap(y0, x1, c);
+    const char* xb = (const char*)p.xp + (int64_t)bh * M * tap_row;
+    char* ob = (char*)p.out + (b * p.o_sb + h * p.o_sh) * (int64_t)esz;
+    for (int64_t i = (int64_t)blockIdx.x * NTHREADS + threadIdx.x; i < per_slice; i += (int64_t)gridDim.x * NTHREADS) {
+      const uint32_t n = (uint32_t)(i >> cpr_log);
+      const int ch = (int)(i & (cpr - 1));
+      const uint32_t t = fast_div(n, p.fd_hw);
+      const uint32_t rem = n - t * p.fd_hw.d;
+      const uint32_t y = fast_div(rem, p.fd_w);
+      const uint32_t x = rem - y * p.fd_w.d;
+      const float fy = fmaxf(((float)y + 0.5f) * sy - 0.5f, 0.f), fx = fmaxf(((float)x + 0.5f) * sx - 0.5f, 0.f);
+      const int y0 = min((int)fy, p.Hp - 1), x0 = min((int)fx, p.Wp - 1);
+      const int y1 = min(y0 + 1, p.Hp - 1), x1 = min(x0 + 1, p.Wp - 1);
+      const float ly = fy - (float)y0, lx = fx - (float)x0;
+      const char* base = xb + (int64_t)t * p.Hp * p.Wp * tap_row + ch * 16;
+      auto tap = [&](int yy, int xx, float (&f)[C::E]) {
+        C::unpack(*(const u32x4*)(base + (int64_t)(yy * p.Wp + xx) * tap_row), f);
+      };
+      float a[C::E], c[C::E], acc[C::E];
+      tap(y0, x0, a);
+      tap(y0, x1, c);
 #pragma unroll
-    for (int e = 0; e < C::E; ++e) acc[e] = (1.f - ly) * ((1.f - lx) * a[e] + lx * c[e]);
-    tap(y1, x0, a);
-    tap(y1, x1, c);
+      for (int e = 0; e < C::E; ++e) acc[e] = (1.f - ly) * ((1.f - lx) * a[e] + lx * c[e]);
+      tap(y1, x0, a);
+      tap(y1, x1, c);
 #pragma unroll
-    for (int e = 0; e < C::E; ++e) acc[e] += ly * ((1.f - lx) * a[e] + lx * c[e]);
-    __builtin_nontemporal_store(C::pack(acc), (u32x4*)((char*)p.out + (b * p.o_sb + h * p.o_sh + n * p.o_sn) * esz + ch * 16));
+      for (int e = 0; e < C::E; ++e) acc[e] += ly * ((1.f - lx) * a[e] + lx * c[e]);
+      __builtin_nontemporal_store(C::pack(acc), (u32x4*)(ob + (int64_t)n * o_row + ch * 16));
+    }
   }
 }
 
@@ -242,9 +250,7 @@ int grid_for(int64_t work) {
 
 }  // namespace
 
-// Grid for per-slice work: the y index over the (batch, head) slices, at most
-// max_wg workgroups in all (the kernels' loops stride over the rest).
-dim3 slice_grid(int64_t slices, int64_t per_slice_work, int64_t max_wg = 256 * 8 * 16) {
+dim3 slice_grid(int64_t slices, int64_t per_slice_work, int64_t max_wg) {
   const int gy = (int)(slices < 65535 ? slices : 65535);
   const int64_t gx = (per_slice_work + NTHREADS - 1) / NTHREADS;
   const int64_t cap = (max_wg + gy - 1) / gy;
@@ -253,7 +259,7 @@ dim3 slice_grid(int64_t slices, int64_t per_slice_work, int64_t max_wg = 256 * 8
 
 hipError_t launch_avgpool(const PoolParams& p, int bf16, hipStream_t stream) {
   const int cpr = p.head_dim / (bf16 ? 8 : 4);
-  const dim3 grid = slice_grid((int64_t)p.batch * p.heads, (int64_t)p.T * p.Hp * p.Wp * cpr);
+  const dim3 grid = slice_grid((int64_t)p.batch * p.heads, (int64_t)p.T * p.Hp * p.Wp * cpr, 256 * 8 * 16);
   if (bf16)
     hipLaunchKernelGGL(avgpool_kernel<true>, grid, dim3(NTHREADS), 0, stream, p);
   else
@@ -275,11 +281,12 @@ hipError_t launch_merge(const MergeParams& p, int bf16, hipStream_t stream) {
 
 hipError_t launch_upsample(const UpsampleParams& p, int bf16, hipStream_t stream) {
   const int cpr = p.head_dim / (bf16 ? 8 : 4);
-  const int64_t work = (int64_t)p.batch * p.heads * p.T * p.H * p.W * cpr;
+  // every chunk its own thread: no cap on the grid
+  const dim3 grid = slice_grid((int64_t)p.batch * p.heads, (int64_t)p.T * p.H * p.W * cpr, (int64_t)1 << 40);
   if (bf16)
-    hipLaunchKernelGGL(upsample_kernel<true>, dim3(grid_for(work)), dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL(upsample_kernel<true>, grid, dim3(NTHREADS), 0, stream, p);
   else
-    hipLaunchKernelGGL(upsample_kernel<false>, dim3(grid_for(work)), dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL(upsample_kernel<false>, grid, dim3(NTHREADS), 0, stream, p);
   return hipGetLastError();
 }
 
