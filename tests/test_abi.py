@@ -42,7 +42,7 @@ def test_kernel_choice_per_workload():
     # (and dtype / head_dim): the workloads' tiles and two edge cases
     from video_dit_sparse_amd import workloads as WL
     want = {"tiny_f32": "box_attn_f32_kernel<64>", "sta_720p": "box_attn_bf16_pp_kernel<1>",
-            "dual_1080p": "box_attn_bf16_pp_kernel<0>", "local_global_4k": "box_attn_bf16_m16_kernel<4, 1>",
+            "dual_1080p": "box_attn_bf16_pp_kernel<0>", "local_global_4k": "box_attn_bf16_m16_kernel<8, 1, true>",
             "cross_window_2k": "box_attn_bf16_kernel<128>"}
     for name, kernel in want.items():
         w = WL.WORKLOADS[name]

@@ -198,8 +198,15 @@ TILE_WALK = [
     ("whole_tiles_4x16", (6, 8, 32), (6, 4, 16), (1, 3, 3), (0, 0, 0), "clip", "box_attn_bf16_pp_kernel<1>"),
     ("whole_tiles_inward", (12, 16, 40), (6, 8, 8), (1, 1, 3), (0, 0, 0), "inward", "box_attn_bf16_pp_kernel<1>"),
     ("rolled_whole_tiles", (12, 16, 24), (6, 8, 8), (3, 3, 5), (3, 4, 4), "cyclic", "box_attn_bf16_pp_kernel<2>"),
-    ("whole_tiles_192", (9, 16, 24), (3, 8, 8), (3, 3, 3), (0, 0, 0), "clip", "box_attn_bf16_m16_kernel<4, 1>"),
+    # 192-token tiles: two tiles along w per workgroup (an odd count leaves the
+    # last workgroup one tile; windows clipped at the edges), or one tile per
+    # row of the lattice
+    ("whole_tiles_192", (9, 16, 24), (3, 8, 8), (3, 3, 3), (0, 0, 0), "clip", "box_attn_bf16_m16_kernel<8, 1, true>"),
     ("whole_tiles_192_inward", (6, 24, 32), (3, 4, 16), (1, 5, 1), (0, 0, 0), "inward",
+     "box_attn_bf16_m16_kernel<8, 1, true>"),
+    ("whole_tiles_192_pairs_w5", (6, 16, 32), (3, 8, 8), (3, 3, 5), (0, 0, 0), "clip",
+     "box_attn_bf16_m16_kernel<8, 1, true>"),
+    ("whole_tiles_192_one_per_row", (6, 16, 8), (3, 8, 8), (3, 3, 1), (0, 0, 0), "clip",
      "box_attn_bf16_m16_kernel<4, 1>"),
 ]
 

@@ -92,7 +92,7 @@ def test_sweep_reaches_every_kernel():
     # the tile walks: the 384-query kernel's, plain and on the rolled grid,
     # and the 192-query kernel's
     assert seen.get("box_attn_bf16_pp_kernel<1>", 0) + seen.get("box_attn_bf16_pp_kernel<2>", 0) >= 2, seen
-    assert seen.get("box_attn_bf16_m16_kernel<4, 1>", 0) >= 1, seen
+    assert seen.get("box_attn_bf16_m16_kernel<4, 1>", 0) + seen.get("box_attn_bf16_m16_kernel<8, 1, true>", 0) >= 1, seen
     modes = [c[7] for c in FWD]
     assert min(modes.count(m) for m in ("clip", "inward", "cyclic")) >= 5
     assert sum(1 for c in FWD if any(c[6])) >= 15   # shifted lattices

@@ -223,8 +223,12 @@ const char* attn_kernel_name(const vdsa_problem* prob, const vdsa::BoxAttnParams
                                           "box_attn_bf16_pp_kernel<2>", "box_attn_bf16_pp_kernel<3>"};
   switch (choose_bf16_shape(max_tile_volume(bp), prob->head_dim).kernel) {
     case K_PP_8W: return pp_names[tile_walk_mode(bp)];
-    case K_M16_4W:
-      return tile_walk_mode(bp) == 1 ? "box_attn_bf16_m16_kernel<4, 1>" : "box_attn_bf16_m16_kernel<4, 0>";
+    case K_M16_4W: {
+      if (tile_walk_mode(bp) != 1) return "box_attn_bf16_m16_kernel<4, 0>";
+      // one query block per tile and two or more tiles along w: tile pairs
+      const int64_t qblocks = (max_tile_volume(bp) + 191) / 192;
+      return qblocks == 1 && bp.nW >= 2 ? "box_attn_bf16_m16_kernel<8, 1, true>" : "box_attn_bf16_m16_kernel<4, 1>";
+    }
     default: return d128 ? "box_attn_bf16_kernel<128>" : "box_attn_bf16_kernel<64>";
   }
 }

@@ -60,9 +60,14 @@ constexpr int WAIT_VMCNT0 = 0x0F70;   // s_waitcnt vmcnt(0), other counters unto
 constexpr float RESCALE_MARGIN = 8.f;
 constexpr int RA = 3;   // operand fragments read ahead of their MFMAs
 
-// WALK: the key walk (box_common.h), chosen by the host.
-template <int NW, int WALK>
-__global__ __launch_bounds__(NW * 64, 2) void box_attn_bf16_m16_kernel(const BoxAttnParams p) {
+// WALK: the key walk (box_common.h), chosen by the host.  PAIR (NW = 8, the
+// tile walk): the workgroup owns two tiles adjacent along w, waves 0-3 the
+// first and 4-7 the second.  Both walk the union of their key boxes (their t
+// and h ranges are the same), so each block is loaded once for both tiles,
+// and a wave skips the products and softmax of blocks outside its own box;
+// its own blocks come in the order of its own box's walk.
+template <int NW, int WALK, bool PAIR = false>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void box_attn_bf16_m16_kernel(const BoxAttnParams p) {
   constexpr int BLOCK_M = NW * 16 * QT;
   constexpr int KDMA_W = NFRAG_K / NW;           // K fragments loaded per wave per block
   constexpr int VPT = BLOCK_N * HD / 8 / (NW * 64);   // V 16-byte chunks per thread (2 or 4)
@@ -79,20 +84,44 @@ __global__ __launch_bounds__(NW * 64, 2) void box_attn_bf16_m16_kernel(const Box
 
   // ---- which (batch, head, query tile, query block) this workgroup owns
   const int wg = xcd_remap(blockIdx.x, p.total_wg);
-  const int qblk = wg % p.qblocks;
-  const int rest = wg / p.qblocks;
-  const int ntiles = p.nT * p.nH * p.nW;
-  const int tile = rest % ntiles;
-  const int bh = rest / ntiles;
+  int qblk, tile, bh;
+  Box qb, kb, kw;   // kw: the box the walk covers (kb, or the pair's union)
+  bool own = true;  // PAIR: this wave's tile exists (uniform over the wave)
+  int wq = wave;    // the wave's index among the waves sharing its tile
+  if constexpr (PAIR) {
+    const int npw = (p.nW + 1) >> 1;   // tile pairs per row of the lattice
+    const int pairs = p.nT * p.nH * npw;
+    const int pr = wg % pairs;
+    bh = wg / pairs;
+    const int pw = pr % npw, row = pr / npw;   // row = at * nH + ah
+    const int grp = wave >> 2;
+    own = 2 * pw + grp < p.nW;
+    wq = wave & 3;
+    qblk = 0;
+    tile = row * p.nW + min(2 * pw + grp, p.nW - 1);
+    tile_boxes(p, tile, qb, kb);
+    Box qa, ka, qc, kc;
+    tile_boxes(p, row * p.nW + 2 * pw, qa, ka);
+    tile_boxes(p, row * p.nW + min(2 * pw + 1, p.nW - 1), qc, kc);
+    kw = ka;
+    kw.w0 = min(ka.w0, kc.w0);
+    kw.ew = max(ka.w0 + ka.ew, kc.w0 + kc.ew) - kw.w0;
+  } else {
+    qblk = wg % p.qblocks;
+    const int rest = wg / p.qblocks;
+    const int ntiles = p.nT * p.nH * p.nW;
+    tile = rest % ntiles;
+    bh = rest / ntiles;
+    tile_boxes(p, tile, qb, kb);
+    kw = kb;
+  }
   const int h = bh % p.heads;
   const int b = bh / p.heads;
 
-  Box qb, kb;
-  tile_boxes(p, tile, qb, kb);
   const int qvol = qb.et * qb.eh * qb.ew;
   const int q0 = qblk * BLOCK_M;
   if (q0 >= qvol) return;  // uniform over the workgroup
-  const int kvol = kb.et * kb.eh * kb.ew;
+  const int kvol = kw.et * kw.eh * kw.ew;
   const int nkb = (kvol + BLOCK_N - 1) / BLOCK_N;
 
   const char* __restrict__ qp = (const char*)p.q + 2 * (b * p.q_sb + h * p.q_sh);
@@ -113,8 +142,8 @@ __global__ __launch_bounds__(NW * 64, 2) void box_attn_bf16_m16_kernel(const Box
   bf16x8 qf[QT][KS];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    const int jq = q0 + wave * 16 * QT + 16 * qt + l16;
-    q_valid[qt] = jq < qvol;
+    const int jq = q0 + wq * 16 * QT + 16 * qt + l16;
+    q_valid[qt] = own && jq < qvol;
     const int j = min(jq, qvol - 1);
     const int plane = qb.eh * qb.ew;
     const int jt = j / plane;
@@ -156,7 +185,7 @@ __global__ __launch_bounds__(NW * 64, 2) void box_attn_bf16_m16_kernel(const Box
   // rows' byte offsets from the block's first token
   const int w_log = __builtin_ctz((unsigned)max(p.bW, 1));   // bW divides 64: a power of two
   TileCursor cur;
-  if constexpr (WALK != WALK_RASTER) cur.init(p, kb);
+  if constexpr (WALK != WALK_RASTER) cur.init(p, kw);
   uint32_t k_off[KDMA_W], v_off[VPT];
   if constexpr (WALK == WALK_TILES) {
 #pragma unroll
@@ -186,7 +215,7 @@ __global__ __launch_bounds__(NW * 64, 2) void box_attn_bf16_m16_kernel(const Box
       }
     } else {
       int t, h, w;
-      cur.next(p, kb, t, h, w);
+      cur.next(p, kw, t, h, w);
       if constexpr (WALK == WALK_TILES) {
         const uint32_t base = (uint32_t)((t * p.kH + h) * p.kW + w);
         const uint32_t kb_off = base * k_row, vb_off = base * v_row;
@@ -263,11 +292,26 @@ __global__ __launch_bounds__(NW * 64, 2) void box_attn_bf16_m16_kernel(const Box
   __builtin_amdgcn_s_waitcnt(WAIT_VMCNT0);
   __syncthreads();
 
+  // PAIR: the processed block's key tile along w (blocks are the frames of
+  // the union box's tiles, w fastest after the frame) and this wave's range
+  int wf = 0, wtw = 0;
+  const int ntw = kw.ew / max(p.bW, 1);
+  const int my_tw0 = (kb.w0 - kw.w0) / max(p.bW, 1), my_tw1 = my_tw0 + kb.ew / max(p.bW, 1);
+
   auto process = [&](int blk, auto partial_tag) {
     constexpr bool PARTIAL = decltype(partial_tag)::value;
     const int stage = blk & 1;
     const bool more = blk + 1 < nkb;
     if (more) load_block(blk + 1, stage ^ 1);
+    bool active = true;
+    if constexpr (PAIR) {
+      active = own && wtw >= my_tw0 && wtw < my_tw1;
+      if (++wf == p.bT) {
+        wf = 0;
+        if (++wtw == ntw) wtw = 0;
+      }
+    }
+    if (active) {
     const char* st = lds + stage * STAGE;
     const int nvalid = PARTIAL ? kvol - blk * BLOCK_N : BLOCK_N;
 
@@ -358,6 +402,7 @@ __global__ __launch_bounds__(NW * 64, 2) void box_attn_bf16_m16_kernel(const Box
       }
     }
 
+    }
     if (more) store_v(stage ^ 1);
     __builtin_amdgcn_s_waitcnt(WAIT_VMCNT0);   // K of the next block has landed in LDS
     __syncthreads();
@@ -418,7 +463,11 @@ __global__ __launch_bounds__(NW * 64, 2) void box_attn_bf16_m16_kernel(const Box
 // thread loads spills registers, so the host keeps the cyclic mode on the
 // raster walk for this kernel.
 hipError_t launch_box_attn_bf16_m16(const BoxAttnParams& p, hipStream_t stream) {
-  if (p.tile_walk == WALK_TILES)
+  if (p.tile_walk == WALK_TILES && p.qblocks == 1 && p.nW >= 2) {
+    BoxAttnParams pp = p;   // one workgroup per pair of tiles along w
+    pp.total_wg = p.batch * p.heads * p.nT * p.nH * ((p.nW + 1) / 2);
+    hipLaunchKernelGGL((box_attn_bf16_m16_kernel<8, WALK_TILES, true>), dim3(pp.total_wg), dim3(8 * 64), 0, stream, pp);
+  } else if (p.tile_walk == WALK_TILES)
     hipLaunchKernelGGL((box_attn_bf16_m16_kernel<4, WALK_TILES>), dim3(p.total_wg), dim3(4 * 64), 0, stream, p);
   else
     hipLaunchKernelGGL((box_attn_bf16_m16_kernel<4, WALK_RASTER>), dim3(p.total_wg), dim3(4 * 64), 0, stream, p);
