@@ -74,7 +74,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void box_attn_bf16_m16_kernel(cons
   constexpr int NKG = BLOCK_N / VPT;             // threads per V head_dim chunk
   static_assert(KDMA_W * NW == NFRAG_K && VPT * NKG == BLOCK_N && (VPT == 2 || VPT == 4), "split");
 
-  __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) char lds[(PAIR ? 3 : 2) * STAGE];   // PAIR: a three-stage ring
+  constexpr int RAW = PAIR ? 2 : RA;   // operand read-ahead (the pair form's second V set takes registers)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void box_attn_bf16_m16_kernel(cons
   // VPT*vk .. VPT*vk + VPT-1.
   const int vk = tid % NKG;
   const int vc = tid / NKG;
-  u32x4 vreg[VPT];
+  u32x4 vregs[2][VPT];   // PAIR: one set per block parity (blocks requested two ahead)
 
   // the block rows this lane loads: K row of each of its KDMA_W fragments,
   // V rows VPT*vk + i
@@ -198,7 +199,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void box_attn_bf16_m16_kernel(cons
 
   // Requests of consecutive blocks come in order (the tile cursor advances
   // once per call).
-  auto load_block = [&](int blk, int stage) {
+  auto load_block = [&](int blk, int stage, auto set_tag) {
+    u32x4 (&vreg)[VPT] = vregs[decltype(set_tag)::value];
     char* st = lds + stage * STAGE;
     if constexpr (WALK == WALK_RASTER) {
       const uint32_t my_tok = key_token(blk * BLOCK_N + lane);
@@ -240,7 +242,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void box_attn_bf16_m16_kernel(cons
     }
   };
   // Transposing store of the V registers into the V fragments of `stage`.
-  auto store_v = [&](int stage) {
+  auto store_v = [&](int stage, auto set_tag) {
+    const u32x4 (&vreg)[VPT] = vregs[decltype(set_tag)::value];
     char* vst = lds + stage * STAGE + K_STAGE;
     const int k0 = VPT * vk;
     const int c = k0 >> 5, kg = (k0 & 31) >> 3;
@@ -287,10 +290,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void box_attn_bf16_m16_kernel(cons
   const float cl2 = p.scale_log2e;
   const float inv_cl2 = 1.f / cl2;
 
-  load_block(0, 0);
-  store_v(0);
-  __builtin_amdgcn_s_waitcnt(WAIT_VMCNT0);
-  __syncthreads();
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, 1>;
+  if constexpr (!PAIR) {
+    load_block(0, 0, Set0{});
+    store_v(0, Set0{});
+    __builtin_amdgcn_s_waitcnt(WAIT_VMCNT0);
+    __syncthreads();
+  }
 
   // PAIR: the processed block's key tile along w (blocks are the frames of
   // the union box's tiles, w fastest after the frame) and this wave's range
@@ -298,11 +305,101 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void box_attn_bf16_m16_kernel(cons
   const int ntw = kw.ew / max(p.bW, 1);
   const int my_tw0 = (kb.w0 - kw.w0) / max(p.bW, 1), my_tw1 = my_tw0 + kb.ew / max(p.bW, 1);
 
+  // One 32-key chunk c of the block in stage st for this wave: S^T, the
+  // online softmax (nvalid = keys of the block; masking only in a partial
+  // last block) and O^T += V^T P^T.
+  auto chunk = [&](const char* st, int c, int nvalid, auto partial_tag) __attribute__((always_inline)) {
+    constexpr bool PARTIAL = decltype(partial_tag)::value;
+    // S^T for the chunk: s[t][qt] register v = key 32c + 8G + 4t + v, query 16qt + l16
+    f32x4 s[2][QT];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) s[t][qt] = f32x4{};
+    {
+      // K fragments in (ks, t) order, read RAW ahead of their products
+      auto kfp = [&](int i) { return st + ((c * 2 + (i & 1)) * KS + (i >> 1)) * 1024 + lane * 16; };
+      bf16x8 kb[8];
+#pragma unroll
+      for (int i = 0; i < RAW; ++i) kb[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)kfp(i));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i + RAW < 8) kb[i + RAW] = __builtin_bit_cast(bf16x8, *(const u32x4*)kfp(i + RAW));
+        __builtin_amdgcn_sched_barrier(0);
+        const int ks = i >> 1, t = i & 1;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          s[t][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[i], qf[qt][ks], s[t][qt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // online softmax over the chunk's 32 keys.  Lazy rescale: keep each
+    // query's reference max until some score of the wave exceeds it by more
+    // than RESCALE_MARGIN (log2 units); each lane tests its own eight scores
+    // of a query, and the cross-lane maximum is formed only when one fires.
+    float lmax[QT];
+    bool grow = false;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      // a running chain, so that the compiler fuses it into three v_max3 and one v_max
+      float m = fmaxf(fmaxf(s[0][qt][0], s[0][qt][1]), s[0][qt][2]);
+      m = fmaxf(fmaxf(m, s[0][qt][3]), s[1][qt][0]);
+      m = fmaxf(fmaxf(m, s[1][qt][1]), s[1][qt][2]);
+      m = fmaxf(m, s[1][qt][3]);
+      lmax[qt] = m;
+      grow = grow || (m > m_thr[qt]);
+    }
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const float m_new = fmaxf(m_run[qt], xrow4_max(lmax[qt]) * cl2);
+        const float corr = __builtin_amdgcn_exp2f(m_run[qt] - m_new);
+        lacc[qt] *= corr;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) oacc[dt][qt] *= corr;
+        m_run[qt] = m_new;
+        m_thr[qt] = (m_new + RESCALE_MARGIN) * inv_cl2;
+      }
+    }
+    bf16x8 pf[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float pv = __builtin_amdgcn_exp2f(fmaf(s[e >> 2][qt][e & 3], cl2, -m_run[qt]));
+        if constexpr (PARTIAL) {
+          if (32 * c + 8 * G + e >= nvalid) pv = 0.f;
+        }
+        pf[qt][e] = (__bf16)pv;
+      }
+    }
+    // O^T += V^T P^T for the chunk, V^T fragments read RAW ahead
+    {
+      bf16x8 vb[ND];
+#pragma unroll
+      for (int i = 0; i < RAW; ++i) vb[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + v_rd[c] + i * 1024));
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) {
+        if (dt + RAW < ND) vb[dt + RAW] = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + v_rd[c] + (dt + RAW) * 1024));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          oacc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[dt], pf[qt], oacc[dt][qt], 0, 0, 0);
+        if (dt == 3) {
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt)
+            lacc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pf[qt], lacc[qt], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
   auto process = [&](int blk, auto partial_tag) {
     constexpr bool PARTIAL = decltype(partial_tag)::value;
     const int stage = blk & 1;
     const bool more = blk + 1 < nkb;
-    if (more) load_block(blk + 1, stage ^ 1);
+    if (more) load_block(blk + 1, stage ^ 1, Set0{});
     bool active = true;
     if constexpr (PAIR) {
       active = own && wtw >= my_tw0 && wtw < my_tw1;
@@ -316,102 +413,67 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void box_attn_bf16_m16_kernel(cons
     const int nvalid = PARTIAL ? kvol - blk * BLOCK_N : BLOCK_N;
 
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      // S^T for the chunk: s[t][qt] register v = key 32c + 8G + 4t + v, query 16qt + l16
-      f32x4 s[2][QT];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) s[t][qt] = f32x4{};
-      {
-        // K fragments in (ks, t) order, read RA ahead of their products
-        auto kfp = [&](int i) { return st + ((c * 2 + (i & 1)) * KS + (i >> 1)) * 1024 + lane * 16; };
-        bf16x8 kb[8];
-#pragma unroll
-        for (int i = 0; i < RA; ++i) kb[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)kfp(i));
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          if (i + RA < 8) kb[i + RA] = __builtin_bit_cast(bf16x8, *(const u32x4*)kfp(i + RA));
-          __builtin_amdgcn_sched_barrier(0);
-          const int ks = i >> 1, t = i & 1;
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt)
-            s[t][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[i], qf[qt][ks], s[t][qt], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      // online softmax over the chunk's 32 keys.  Lazy rescale: keep each
-      // query's reference max until some score of the wave exceeds it by more
-      // than RESCALE_MARGIN (log2 units); each lane tests its own eight scores
-      // of a query, and the cross-lane maximum is formed only when one fires.
-      float lmax[QT];
-      bool grow = false;
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        // a running chain, so that the compiler fuses it into three v_max3 and one v_max
-        float m = fmaxf(fmaxf(s[0][qt][0], s[0][qt][1]), s[0][qt][2]);
-        m = fmaxf(fmaxf(m, s[0][qt][3]), s[1][qt][0]);
-        m = fmaxf(fmaxf(m, s[1][qt][1]), s[1][qt][2]);
-        m = fmaxf(m, s[1][qt][3]);
-        lmax[qt] = m;
-        grow = grow || (m > m_thr[qt]);
-      }
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-          const float m_new = fmaxf(m_run[qt], xrow4_max(lmax[qt]) * cl2);
-          const float corr = __builtin_amdgcn_exp2f(m_run[qt] - m_new);
-          lacc[qt] *= corr;
-#pragma unroll
-          for (int dt = 0; dt < ND; ++dt) oacc[dt][qt] *= corr;
-          m_run[qt] = m_new;
-          m_thr[qt] = (m_new + RESCALE_MARGIN) * inv_cl2;
-        }
-      }
-      bf16x8 pf[QT];
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float pv = __builtin_amdgcn_exp2f(fmaf(s[e >> 2][qt][e & 3], cl2, -m_run[qt]));
-          if constexpr (PARTIAL) {
-            if (32 * c + 8 * G + e >= nvalid) pv = 0.f;
-          }
-          pf[qt][e] = (__bf16)pv;
-        }
-      }
-      // O^T += V^T P^T for the chunk, V^T fragments read RA ahead
-      {
-        bf16x8 vb[ND];
-#pragma unroll
-        for (int i = 0; i < RA; ++i) vb[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + v_rd[c] + i * 1024));
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt) {
-          if (dt + RA < ND) vb[dt + RA] = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + v_rd[c] + (dt + RA) * 1024));
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt)
-            oacc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[dt], pf[qt], oacc[dt][qt], 0, 0, 0);
-          if (dt == 3) {
-#pragma unroll
-            for (int qt = 0; qt < QT; ++qt)
-              lacc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pf[qt], lacc[qt], 0, 0, 0);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    }
+    for (int c = 0; c < 2; ++c) chunk(st, c, nvalid, partial_tag);
+
 
     }
-    if (more) store_v(stage ^ 1);
+    if (more) store_v(stage ^ 1, Set0{});
     __builtin_amdgcn_s_waitcnt(WAIT_VMCNT0);   // K of the next block has landed in LDS
     __syncthreads();
   };
 
-  const bool last_partial = kvol % BLOCK_N != 0;
-  const int nfull = last_partial ? nkb - 1 : nkb;
-  for (int blk = 0; blk < nfull; ++blk) process(blk, std::false_type{});
-  if (last_partial) process(nkb - 1, std::true_type{});
+  if constexpr (PAIR) {
+    // Three stages, blocks requested two ahead: in block b the requests of
+    // block b+2 (stage (b+2) % 3, V register set b % 2) go out first, and the
+    // wait at its end keeps them in flight while block b+1's have landed.
+    // Every step requests and stores unconditionally (past the box, the last
+    // block again, into stages no later step reads), so that every path
+    // issues the same memory requests and the counted waits stay exact; the
+    // box has whole 64-key blocks only (the tile walk).
+    constexpr int NST = 3;
+    constexpr int NLOAD = KDMA_W + VPT;   // vector-memory requests per wave per block
+    auto req = [&](int blk, auto set_tag) __attribute__((always_inline)) {
+      load_block(min(blk, nkb - 1), blk % NST, set_tag);
+    };
+    req(0, Set0{});
+    req(1, Set1{});
+    __builtin_amdgcn_s_waitcnt(wait_enc(NLOAD, 15));   // block 0's requests have landed
+    store_v(0, Set0{});
+    __syncthreads();
+    auto step = [&](int blk, auto par_tag) __attribute__((always_inline)) {
+      constexpr int PAR = decltype(par_tag)::value;
+      using Own = std::integral_constant<int, PAR>;
+      using Next = std::integral_constant<int, PAR ^ 1>;
+      req(blk + 2, Own{});
+      __builtin_amdgcn_sched_barrier(0);
+      bool active = blk < nkb;
+      if (active) {
+        active = own && wtw >= my_tw0 && wtw < my_tw1;
+        if (++wf == p.bT) {
+          wf = 0;
+          if (++wtw == ntw) wtw = 0;
+        }
+      }
+      if (active) {
+        const char* st = lds + (blk % NST) * STAGE;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) chunk(st, c, BLOCK_N, std::false_type{});
+      }
+      store_v((blk + 1) % NST, Next{});
+      __builtin_amdgcn_s_waitcnt(wait_enc(NLOAD, 15));   // block blk+1 has landed, blk+2 in flight
+      __syncthreads();
+    };
+    for (int blk = 0; blk < nkb; blk += 2) {
+      step(blk, Set0{});
+      step(blk + 1, Set1{});
+    }
+    __builtin_amdgcn_s_waitcnt(WAIT_VMCNT0);   // the requests past the box have landed
+  } else {
+    const bool last_partial = kvol % BLOCK_N != 0;
+    const int nfull = last_partial ? nkb - 1 : nkb;
+    for (int blk = 0; blk < nfull; ++blk) process(blk, std::false_type{});
+    if (last_partial) process(nkb - 1, std::true_type{});
+  }
 
   // ---- epilogue: O^T register v of tile (dt, qt) is head_dim 16dt + 4G + v;
   // with a merge, each row combines with the other branch's row (read at the
