@@ -26,12 +26,31 @@ sys.path.insert(0, ROOT)
 METRIC = "effective attention TFLOP/s + ms/call (720P-shape STA, bf16); % MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0
+PEAK_F32_VECTOR_TFLOPS = 157.3   # fp32 vector ALU (the fp32 path has no matrix-core products)
 NOMINAL_CLOCK_MHZ = 2400.0   # the clock the published bf16 peak assumes
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "sta_bf16_720p_counters.md")
 # the 720P workload's 384-token (6x8x8) tiles at head_dim 128 run the 8-wave
 # kernel of attn_bf16_pp.hip; its traffic counters are tied to these sources
 KERNEL_SOURCES = [os.path.join(ROOT, "video_dit_sparse_amd", "csrc", f)
                   for f in ("attn_bf16_pp.hip", "box_common.h", "internal.h")]
+
+
+def roofline_of(dtype: str, flop: float, nbytes: float, ms: float) -> dict:
+    """Roofline of one attention launch from its effective FLOP, its compulsory
+    bytes (Q, K, V read once, O written once) and its time: the fp32 path is
+    bound by the vector ALU; a bf16 launch by the matrix cores when its FLOP
+    per compulsory byte reach the ridge of the two published peaks
+    (2500 TFLOP/s over 8 TB/s, 312.5 FLOP/B), else by HBM (a window of one
+    tile is 116-121 FLOP/B)."""
+    intensity = flop / nbytes
+    if dtype == "f32":
+        bound, achieved, peak, unit = "alu", flop / (ms * 1e-3) / 1e12, PEAK_F32_VECTOR_TFLOPS, "TFLOP/s"
+    elif intensity >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        bound, achieved, peak, unit = "mfma", flop / (ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        bound, achieved, peak, unit = "hbm", nbytes / (ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "bytes_per_launch": nbytes, "flop_per_byte": round(intensity, 1)}
 
 
 def log(*a):
@@ -272,14 +291,16 @@ def main():
     launch_flops = fl["local"] / n_local
     achieved = launch_flops / (launch_ms * 1e-3) / 1e12
     traffic = measured_traffic() if w.name == "sta_720p" else None
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": V.sta_kernel_name(w.batch, w.heads, w.head_dim, w.grid, w.tile, w.window, w.shifts[0],
-                                            dtype=w.dtype),
-                "launch_ms": round(launch_ms, 4),
-                "flop_per_launch": launch_flops,
-                "per_call_ms": {"n": len(per_call), "median": round(per_call[len(per_call) // 2], 4),
-                                "min": round(per_call[0], 4)}}
+    launch_bytes = 4.0 * q.numel() * q.element_size()   # Q, K, V read once, O written once
+    roofline = roofline_of(w.dtype, launch_flops, launch_bytes, launch_ms)
+    roofline.update({"traffic": traffic,
+                     "kernel": V.sta_kernel_name(w.batch, w.heads, w.head_dim, w.grid, w.tile, w.window, w.shifts[0],
+                                                 dtype=w.dtype),
+                     "launch_ms": round(launch_ms, 4),
+                     "flop_per_launch": launch_flops,
+                     "tflops": round(achieved, 2),
+                     "per_call_ms": {"n": len(per_call), "median": round(per_call[len(per_call) // 2], 4),
+                                     "min": round(per_call[0], 4)}})
 
     clock = None
     if args.clock_seconds > 0:

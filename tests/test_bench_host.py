@@ -54,3 +54,20 @@ def test_cpu_baseline_fields_on_a_small_workload():
     assert 1 <= r["cores"] <= min(16, r["cpus_available"]) and r["nproc"] == os.cpu_count()
     assert r["cpu_model"] and "whole query tiles" in r["sample"]
     assert r["effective_flop_done"] > 0 and r["extrapolated_full_call_s"] > 0
+
+
+def test_roofline_bound_by_flop_per_byte():
+    # 720P call: 16.583 TFLOP over 2.831 GB compulsory (5,857 FLOP/B) is
+    # matrix-core bound; a 2K window-1 call, 0.601 TFLOP over 4.955 GB
+    # (121 FLOP/B), is HBM bound; the fp32 path is vector-ALU bound
+    r = bench.roofline_of("bf16", 16.583e12, 2.831e9, 14.0)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == 2500.0
+    assert abs(r["achieved"] - 16.583e12 / 14e-3 / 1e12) < 0.01 and abs(r["frac"] - r["achieved"] / 2500.0) < 1e-4
+    r = bench.roofline_of("bf16", 0.601e12, 4.955e9, 1.3)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
+    assert abs(r["achieved"] - 4.955e9 / 1.3e-3 / 1e9) < 0.01
+    r = bench.roofline_of("f32", 33.6e6, 0.52e6, 0.01)
+    assert r["bound"] == "alu" and r["peak"] == 157.3
+    # the ridge itself (312.5 FLOP/B) counts as matrix-core bound
+    assert bench.roofline_of("bf16", 312.5e9, 1e9, 1.0)["bound"] == "mfma"
+    assert bench.roofline_of("bf16", 312.4e9, 1e9, 1.0)["bound"] == "hbm"
