@@ -75,7 +75,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void box_attn_bf16_m16_kernel(cons
   static_assert(KDMA_W * NW == NFRAG_K && VPT * NKG == BLOCK_N && (VPT == 2 || VPT == 4), "split");
 
   __shared__ __attribute__((aligned(16))) char lds[(PAIR ? 3 : 2) * STAGE];   // PAIR: a three-stage ring
-  constexpr int RAW = PAIR ? 2 : RA;   // operand read-ahead (the pair form's second V set takes registers)
+  constexpr int RAW = RA;   // operand read-ahead (4 would spill registers in the pair form's loop)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
