@@ -461,7 +461,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void box_attn_bf16_m16_kernel(cons
       }
       store_v((blk + 1) % NST, Next{});
       __builtin_amdgcn_s_waitcnt(wait_enc(NLOAD, 15));   // block blk+1 has landed, blk+2 in flight
-      __syncthreads();
+      // a barrier without the memory fence of __syncthreads(), which would
+      // also wait for block blk+2's K transfers into LDS
+      phase_barrier();
     };
     for (int blk = 0; blk < nkb; blk += 2) {
       step(blk, Set0{});
